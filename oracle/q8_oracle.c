@@ -1,0 +1,351 @@
+/*
+ * q8_oracle.c -- plain, slow, fp64 CPU oracle for the Q8_0 decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header,
+ * table or helper with the HIP library; the two meet only on the seeded
+ * inputs.  Every function is the textbook definition written out, evaluated
+ * in double precision with ascending-index loops and no blocking or fusion.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [LUMEN]  "Lumen v0.3.0 -- profile, parallelize, 4x faster than v0.2.0",
+ *            sections "Phase 7.E.0" (decode profile: qkv, wo, gate_up,
+ *            silu_mul, down, lm_head matmuls) and "Phase 7.J" (row split of
+ *            Q8 matmuls across threads); "v0.3 -> v0.4 candidate moves"
+ *            (dequant -> fp32 FMA path).
+ *   [MOE]    "Add Qwen1.5-MoE Q8_0 CPU and single-token TornadoVM GPU
+ *            inference - #144", opening description (router + top-k experts
+ *            + shared-expert FFN block) and "Key implementation notes"
+ *            (Q8_0 scales times 8-bit quants).
+ *   [AUGUR]  "augur" README, "Features" (RMSNorm, grouped-query attention,
+ *            SwiGLU MLP, decoder block order, greedy generation).
+ *   [FUSED]  "fusedtok 1.3.0" PKG-INFO, "API stability" (selection ties
+ *            resolve to the earliest index).
+ *   [COGNI]  "skuznetsov/cogni-ml" README, "Qwen 3.5 Native Metal" /
+ *            cuda_q8_gemv_probe (raw GGUF Q8_0 block layout).
+ *
+ * Q8_0 block (GGUF): 34 bytes = binary16 scale d (little-endian) followed by
+ * 32 signed 8-bit quants q; weight = d * q.  Blocks of a row are
+ * consecutive; rows are consecutive.
+ *
+ * Readings where the pages are silent are listed in the repository's design
+ * notes; the ones that change arithmetic here: activations stay fp32 (no
+ * requantisation), rmsnorm has unit weight, the shared-expert gate is
+ * sigmoid of one logit, top-k weights are renormalised over the selected
+ * experts, and the attention stand-in at position 0 copies each query head's
+ * value head.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define QK 32
+#define BLOCK_BYTES 34
+
+/* IEEE 754 binary16 -> double, by the definition of the format:
+ *   e == 0       : (-1)^s * m * 2^-24            (zero and subnormals)
+ *   0 < e < 31   : (-1)^s * (1024 + m) * 2^(e-25)
+ *   e == 31      : infinity (m == 0) or NaN       */
+double oracle_f16_to_f64(uint16_t h) {
+  int s = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int m = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24);
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + m), e - 25);
+  return s ? -v : v;
+}
+
+void oracle_f16_decode(const uint16_t* h, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f16_to_f64(h[i]);
+}
+
+/* Dequantised weight w[r][k] of an M x K Q8_0 matrix in GGUF block order
+ * [COGNI]; w = d * q [MOE "Key implementation notes"]. */
+static double q8_weight(const uint8_t* aos, int64_t K, int64_t r, int64_t k) {
+  const int64_t nb = K / QK;
+  const uint8_t* blk = aos + (r * nb + k / QK) * BLOCK_BYTES;
+  uint16_t dbits = (uint16_t)(blk[0] | (blk[1] << 8));
+  int8_t q = (int8_t)blk[2 + k % QK];
+  return oracle_f16_to_f64(dbits) * (double)q;
+}
+
+void oracle_dequant_row(const uint8_t* aos, int64_t K, int64_t r, double* out) {
+  for (int64_t k = 0; k < K; ++k) out[k] = q8_weight(aos, K, r, k);
+}
+
+/* ---------------------------------------------------------------------------
+ * Matrix-vector product  y[n][r] = sum_k w[r][k] * x[n][k]   (ascending k)
+ * and the magnitude sum  S[n][r] = sum_k |w[r][k] * x[n][k]|  used by the
+ * error tolerance.  [LUMEN "Phase 7.E.0": every projection of the decode step
+ * is this product; "Phase 7.J": output rows split across threads.]
+ * x is [N][K] double, y and S are [N][M] double.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const uint8_t* aos;
+  int64_t M, K, N;
+  const double* x;
+  double* y;
+  double* S;
+  int64_t r0, r1;
+} gemv_job;
+
+static void* gemv_rows(void* arg) {
+  gemv_job* j = (gemv_job*)arg;
+  for (int64_t n = 0; n < j->N; ++n) {
+    const double* xn = j->x + n * j->K;
+    for (int64_t r = j->r0; r < j->r1; ++r) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t k = 0; k < j->K; ++k) {
+        double p = q8_weight(j->aos, j->K, r, k) * xn[k];
+        acc += p;
+        mag += fabs(p);
+      }
+      j->y[n * j->M + r] = acc;
+      if (j->S) j->S[n * j->M + r] = mag;
+    }
+  }
+  return NULL;
+}
+
+int oracle_q8_0_gemv_f64(const uint8_t* aos, int64_t M, int64_t K, const double* x,
+                         int64_t N, double* y, double* S, int threads) {
+  if (M < 0 || K <= 0 || K % QK || N < 1) return -1;
+  if (threads < 1) threads = 1;
+  if (threads > 256) threads = 256;
+  if (threads > M) threads = M > 0 ? (int)M : 1;
+  gemv_job jobs[256];
+  pthread_t tid[256];
+  for (int t = 0; t < threads; ++t) {
+    jobs[t] = (gemv_job){aos, M, K, N, x, y, S, M * t / threads, M * (t + 1) / threads};
+  }
+  if (threads == 1) {
+    gemv_rows(&jobs[0]);
+    return 0;
+  }
+  for (int t = 0; t < threads; ++t) pthread_create(&tid[t], NULL, gemv_rows, &jobs[t]);
+  for (int t = 0; t < threads; ++t) pthread_join(tid[t], NULL);
+  return 0;
+}
+
+/* fp32 activations, widened exactly to double. */
+int oracle_q8_0_gemv(const uint8_t* aos, int64_t M, int64_t K, const float* x, int64_t N,
+                     double* y, double* S, int threads) {
+  if (K <= 0 || N < 1) return -1;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(N * K));
+  if (!xd) return -2;
+  for (int64_t i = 0; i < N * K; ++i) xd[i] = (double)x[i];
+  int rc = oracle_q8_0_gemv_f64(aos, M, K, xd, N, y, S, threads);
+  free(xd);
+  return rc;
+}
+
+/* ---------------------------------------------------------------------------
+ * Greedy pick: the lowest index among the maxima [AUGUR "Greedy generation";
+ * FUSED "API stability": ties resolve to the earliest index].
+ * ------------------------------------------------------------------------- */
+int64_t oracle_argmax_f32(const float* v, int64_t n) {
+  if (n <= 0) return -1;
+  int64_t best = 0;
+  for (int64_t i = 1; i < n; ++i)
+    if (v[i] > v[best]) best = i;
+  return best;
+}
+
+int64_t oracle_argmax_f64(const double* v, int64_t n) {
+  if (n <= 0) return -1;
+  int64_t best = 0;
+  for (int64_t i = 1; i < n; ++i)
+    if (v[i] > v[best]) best = i;
+  return best;
+}
+
+/* ---------------------------------------------------------------------------
+ * Router [MOE opening description: router + top-k experts]: the k experts
+ * with the largest logits, in descending order, ties to the lower expert
+ * index; weights are the softmax over all experts restricted to the chosen
+ * ones and renormalised, i.e. exp(l_s - l_max) / sum_{t chosen} exp(l_t -
+ * l_max) (the full-softmax denominator cancels in the renormalisation).
+ * ------------------------------------------------------------------------- */
+int oracle_route_topk(const float* logits, int32_t E, int32_t k, int32_t* ids, double* w) {
+  if (E <= 0 || k <= 0 || k > E || E > 4096) return -1;
+  char used[4096];
+  memset(used, 0, sizeof(used));
+  for (int32_t s = 0; s < k; ++s) {
+    int32_t best = -1;
+    for (int32_t e = 0; e < E; ++e) {
+      if (used[e]) continue;
+      if (best < 0 || logits[e] > logits[best]) best = e;
+    }
+    ids[s] = best;
+    used[best] = 1;
+  }
+  double lmax = (double)logits[ids[0]];
+  double den = 0.0;
+  for (int32_t s = 0; s < k; ++s) den += exp((double)logits[ids[s]] - lmax);
+  for (int32_t s = 0; s < k; ++s) w[s] = exp((double)logits[ids[s]] - lmax) / den;
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Elementwise glue [AUGUR "Features": RMSNorm, SwiGLU MLP; LUMEN "Phase
+ * 7.E.0": silu_mul].
+ * ------------------------------------------------------------------------- */
+double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
+double oracle_sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* h[i] = silu(g[i]) * u[i] */
+void oracle_swiglu(const double* g, const double* u, int64_t n, double* h) {
+  for (int64_t i = 0; i < n; ++i) h[i] = oracle_silu(g[i]) * u[i];
+}
+
+/* Root-mean-square normalisation with unit weight:
+ * out[i] = x[i] / sqrt(mean(x^2) + eps). */
+void oracle_rmsnorm(const double* x, int64_t n, double eps, double* out) {
+  double ss = 0.0;
+  for (int64_t i = 0; i < n; ++i) ss += x[i] * x[i];
+  double c = 1.0 / sqrt(ss / (double)n + eps);
+  for (int64_t i = 0; i < n; ++i) out[i] = x[i] * c;
+}
+
+/* Grouped-query attention at position 0 [AUGUR "Grouped-query attention":
+ * many query heads share fewer key/value heads].  With a single key the
+ * softmax weight is 1, so query head i outputs the value vector of kv head
+ * i / (n_heads / n_kv_heads). v is [n_kv_heads][head_dim], out is
+ * [n_heads][head_dim]. */
+int oracle_gqa_position0(const double* v, int32_t n_heads, int32_t n_kv_heads,
+                         int32_t head_dim, double* out) {
+  if (n_kv_heads <= 0 || n_heads % n_kv_heads) return -1;
+  int32_t group = n_heads / n_kv_heads;
+  for (int32_t h = 0; h < n_heads; ++h)
+    for (int32_t j = 0; j < head_dim; ++j)
+      out[(int64_t)h * head_dim + j] = v[(int64_t)(h / group) * head_dim + j];
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Mixture-of-experts FFN [MOE opening description and routed-expert fusion
+ * comments].  Experts are stacked: expert e's gate_up matrix is the
+ * (2I) x H matrix at gu_stack + e * (2I) * (H/32) * 34 bytes, rows 0..I-1
+ * gate and I..2I-1 up; its down matrix is H x I at dn_stack + e * H *
+ * (I/32) * 34.  The shared expert has the same structure with intermediate
+ * Ish.  For each output row the slots are folded in slot order, then the
+ * shared expert:  y = sum_s w[s] * down_s(h_s) + sigmoid(lambda) * down_sh(h_sh).
+ * ------------------------------------------------------------------------- */
+
+/* Combine stage on given intermediate activations h_routed [S][I] and h_sh
+ * [Ish] (double).  Sabs[r] = sum_s |w_s| S_s[r] + |gamma| S_sh[r]. */
+int oracle_moe_combine(const uint8_t* dn_stack, int32_t E, int64_t H, int64_t I,
+                       const int32_t* ids, const double* w, int32_t S,
+                       const double* h_routed, const uint8_t* sh_dn, int64_t Ish,
+                       const double* h_sh, double gamma, double* y, double* Sabs,
+                       int threads) {
+  const int64_t dn_bytes = H * (I / QK) * BLOCK_BYTES;
+  double* t = (double*)malloc(sizeof(double) * (size_t)H);
+  double* tS = (double*)malloc(sizeof(double) * (size_t)H);
+  if (!t || !tS) { free(t); free(tS); return -2; }
+  for (int64_t r = 0; r < H; ++r) { y[r] = 0.0; if (Sabs) Sabs[r] = 0.0; }
+  for (int32_t s = 0; s < S; ++s) {
+    if (ids[s] < 0 || ids[s] >= E) { free(t); free(tS); return -1; }
+    oracle_q8_0_gemv_f64(dn_stack + (int64_t)ids[s] * dn_bytes, H, I, h_routed + s * I, 1,
+                         t, tS, threads);
+    for (int64_t r = 0; r < H; ++r) {
+      y[r] += w[s] * t[r];
+      if (Sabs) Sabs[r] += fabs(w[s]) * tS[r];
+    }
+  }
+  if (sh_dn) {
+    oracle_q8_0_gemv_f64(sh_dn, H, Ish, h_sh, 1, t, tS, threads);
+    for (int64_t r = 0; r < H; ++r) {
+      y[r] += gamma * t[r];
+      if (Sabs) Sabs[r] += fabs(gamma) * tS[r];
+    }
+  }
+  free(t);
+  free(tS);
+  return 0;
+}
+
+/* Whole FFN from x: router weights and ids given (from oracle_route_topk or
+ * elsewhere), gamma = sigmoid(lambda) given. */
+int oracle_moe_ffn(const uint8_t* gu_stack, const uint8_t* dn_stack, int32_t E, int64_t H,
+                   int64_t I, const int32_t* ids, const double* w, int32_t S,
+                   const uint8_t* sh_gu, const uint8_t* sh_dn, int64_t Ish, double gamma,
+                   const float* x, double* y, int threads) {
+  const int64_t gu_bytes = 2 * I * (H / QK) * BLOCK_BYTES;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)H);
+  double* gu = (double*)malloc(sizeof(double) * (size_t)(2 * (I > Ish ? I : Ish)));
+  double* hr = (double*)malloc(sizeof(double) * (size_t)(S * I + 1));
+  double* hs = (double*)malloc(sizeof(double) * (size_t)(Ish + 1));
+  if (!xd || !gu || !hr || !hs) { free(xd); free(gu); free(hr); free(hs); return -2; }
+  for (int64_t k = 0; k < H; ++k) xd[k] = (double)x[k];
+  for (int32_t s = 0; s < S; ++s) {
+    if (ids[s] < 0 || ids[s] >= E) { free(xd); free(gu); free(hr); free(hs); return -1; }
+    oracle_q8_0_gemv_f64(gu_stack + (int64_t)ids[s] * gu_bytes, 2 * I, H, xd, 1, gu, NULL,
+                         threads);
+    oracle_swiglu(gu, gu + I, I, hr + s * I);
+  }
+  if (sh_gu) {
+    oracle_q8_0_gemv_f64(sh_gu, 2 * Ish, H, xd, 1, gu, NULL, threads);
+    oracle_swiglu(gu, gu + Ish, Ish, hs);
+  }
+  int rc = oracle_moe_combine(dn_stack, E, H, I, ids, w, S, hr, sh_gu ? sh_dn : NULL, Ish, hs,
+                              gamma, y, NULL, threads);
+  free(xd);
+  free(gu);
+  free(hr);
+  free(hs);
+  return rc;
+}
+
+/* ---------------------------------------------------------------------------
+ * One decoder layer of the Qwen2-style chain at position 0 [AUGUR "Decoder
+ * blocks": norm, attention, residual, norm, MLP, residual; LUMEN "Phase
+ * 7.E.0": the qkv, wo, gate_up, silu_mul, down steps].  Unit norm weights, no
+ * biases.  h is updated in place (double, length hidden).
+ *   a  = rmsnorm(h);  qkv = Wqkv a  (q rows first, then k, then v)
+ *   h += Wo * gqa(v);  m = rmsnorm(h);  gu = Wgu m  (gate rows, then up)
+ *   h += Wdown * (silu(gate) * up)
+ * ------------------------------------------------------------------------- */
+int oracle_qwen_layer(const uint8_t* qkv_aos, const uint8_t* wo_aos, const uint8_t* gu_aos,
+                      const uint8_t* down_aos, int64_t hidden, int32_t n_heads,
+                      int32_t n_kv_heads, int32_t head_dim, int64_t inter, double eps,
+                      double* h, int threads) {
+  const int64_t qdim = (int64_t)n_heads * head_dim, kvdim = (int64_t)n_kv_heads * head_dim;
+  const int64_t nqkv = qdim + 2 * kvdim;
+  if (qdim != hidden) return -1;
+  double* a = (double*)malloc(sizeof(double) * (size_t)hidden);
+  double* qkv = (double*)malloc(sizeof(double) * (size_t)nqkv);
+  double* att = (double*)malloc(sizeof(double) * (size_t)hidden);
+  double* t = (double*)malloc(sizeof(double) * (size_t)hidden);
+  double* gu = (double*)malloc(sizeof(double) * (size_t)(2 * inter));
+  double* s = (double*)malloc(sizeof(double) * (size_t)inter);
+  int rc = -2;
+  if (!a || !qkv || !att || !t || !gu || !s) goto done;
+  oracle_rmsnorm(h, hidden, eps, a);
+  oracle_q8_0_gemv_f64(qkv_aos, nqkv, hidden, a, 1, qkv, NULL, threads);
+  oracle_gqa_position0(qkv + qdim + kvdim, n_heads, n_kv_heads, head_dim, att);
+  oracle_q8_0_gemv_f64(wo_aos, hidden, hidden, att, 1, t, NULL, threads);
+  for (int64_t i = 0; i < hidden; ++i) h[i] += t[i];
+  oracle_rmsnorm(h, hidden, eps, a);
+  oracle_q8_0_gemv_f64(gu_aos, 2 * inter, hidden, a, 1, gu, NULL, threads);
+  oracle_swiglu(gu, gu + inter, inter, s);
+  oracle_q8_0_gemv_f64(down_aos, hidden, inter, s, 1, t, NULL, threads);
+  for (int64_t i = 0; i < hidden; ++i) h[i] += t[i];
+  rc = 0;
+done:
+  free(a);
+  free(qkv);
+  free(att);
+  free(t);
+  free(gu);
+  free(s);
+  return rc;
+}

@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs for the Q8_0 decode path.
+
+This module is shared by the CPU oracle tests, the GPU parity tests and the
+benchmark.  It draws numbers and lays them out in the GGUF Q8_0 block format;
+it performs none of the method's arithmetic (no dequantisation, no dot
+products), so neither side of a parity comparison borrows anything from the
+other through it.
+
+Block format (GGUF Q8_0, as named on the cogni-ml page, section "Qwen 3.5
+Native Metal" / cuda_q8_gemv_probe "raw GGUF Q8_0 block layout"): each block
+covers 32 consecutive weights of one row and is 34 bytes: a little-endian
+IEEE binary16 scale d followed by 32 signed 8-bit quants.  Blocks of a row are
+consecutive, rows are consecutive.
+
+Value distributions (the workloads this build measures):
+  quants  discrete uniform in [-127, 127], both ends inclusive
+  scales  |N(0,1)| * 0.01, rounded to binary16 (round-to-nearest-even)
+  x       N(0,1) in float32, shape [N][K]
+Generator: numpy PCG64 seeded by SeedSequence([cfg, layer, mat]).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+QK = 32           # weights per block
+BLOCK_BYTES = 34  # 2-byte scale + 32 quants
+
+# Matrix ids inside a configuration's seed sequence.
+MAT_QKV, MAT_WO, MAT_GATE_UP, MAT_DOWN, MAT_LM_HEAD = 0, 1, 2, 3, 4
+MAT_X = 100
+MAT_ROUTER = 101
+MAT_SHARED_GATE = 102
+MAT_SHARED_GU, MAT_SHARED_DOWN = 103, 104
+
+
+def rng(cfg: int, layer: int = 0, mat: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg, layer, mat])))
+
+
+@dataclasses.dataclass
+class Q8Matrix:
+    """A Q8_0 matrix as drawn: quants [M][K] int8, scales [M][K/32] float16."""
+    qs: np.ndarray
+    d: np.ndarray
+
+    @property
+    def M(self) -> int:
+        return self.qs.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.qs.shape[1]
+
+    def aos(self) -> np.ndarray:
+        """GGUF array-of-blocks bytes, shape [M, K/32, 34] uint8."""
+        return encode_aos(self.qs, self.d)
+
+
+def encode_aos(qs: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Lay quants and binary16 scales out as GGUF 34-byte blocks."""
+    qs = np.ascontiguousarray(qs, dtype=np.int8)
+    d = np.ascontiguousarray(d, dtype=np.float16)
+    M, K = qs.shape
+    if K % QK:
+        raise ValueError("K must be a multiple of 32")
+    B = K // QK
+    if d.shape != (M, B):
+        raise ValueError("scale shape must be [M, K/32]")
+    out = np.empty((M, B, BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = d.view(np.uint8).reshape(M, B, 2)  # little-endian host
+    out[:, :, 2:] = qs.view(np.uint8).reshape(M, B, QK)
+    return out
+
+
+def draw_matrix(g: np.random.Generator, M: int, K: int) -> Q8Matrix:
+    """Quants first, then scales, from one generator (fixed draw order)."""
+    qs = g.integers(-127, 128, size=(M, K), dtype=np.int8)
+    d = (np.abs(g.standard_normal((M, K // QK))) * 0.01).astype(np.float16)
+    return Q8Matrix(qs, d)
+
+
+def draw_x(g: np.random.Generator, N: int, K: int) -> np.ndarray:
+    return g.standard_normal((N, K)).astype(np.float32)
+
+
+def matrix(cfg: int, layer: int, mat: int, M: int, K: int) -> Q8Matrix:
+    return draw_matrix(rng(cfg, layer, mat), M, K)
+
+
+def activations(cfg: int, N: int, K: int, layer: int = 0) -> np.ndarray:
+    return draw_x(rng(cfg, layer, MAT_X), N, K)
+
+
+# --------------------------------------------------------------------------
+# Workload shapes
+# --------------------------------------------------------------------------
+
+# Single GEMV, 896 x 896, N = 1.
+C1 = dict(cfg=1, M=896, K=896, N=1)
+
+# Qwen2.5-0.5B-shaped decoder layer: hidden 896, 14 q heads / 2 kv heads of
+# 64, intermediate 4864, 24 layers, vocabulary 151936.
+QWEN05 = dict(hidden=896, n_heads=14, n_kv_heads=2, head_dim=64,
+              intermediate=4864, n_layers=24, vocab=151936, eps=1e-6)
+C2 = dict(cfg=2, **QWEN05)
+C2_SHAPES = {  # mat id -> (M, K)
+    MAT_QKV: (1152, 896),
+    MAT_WO: (896, 896),
+    MAT_GATE_UP: (9728, 896),
+    MAT_DOWN: (896, 4864),
+}
+C3 = dict(cfg=3, M=151936, K=896, N=1)
+
+# Small-batch verify chunk on 9B-class shapes.
+C4 = dict(cfg=4, hidden=4096, intermediate=12288, Ns=(2, 4, 8))
+C4_SHAPES = {MAT_GATE_UP: (24576, 4096), MAT_DOWN: (4096, 12288)}
+
+# Qwen1.5-MoE-A2.7B-shaped FFN: 60 routed experts (top-4), expert
+# intermediate 1408, shared expert intermediate 5632, hidden 2048.
+C5 = dict(cfg=5, hidden=2048, n_experts=60, top_k=4, inter=1408, shared_inter=5632)
+
+
+def layer_matrices(cfg: int, layer: int, shapes: dict) -> dict:
+    return {mat: matrix(cfg, layer, mat, M, K) for mat, (M, K) in shapes.items()}
+
+
+def expert_stack(cfg: int, mat: int, n_experts: int, M: int, K: int) -> np.ndarray:
+    """AoS bytes of n_experts matrices, shape [E, M, K/32, 34]; expert e uses
+    seed layer index e."""
+    out = np.empty((n_experts, M, K // QK, BLOCK_BYTES), dtype=np.uint8)
+    for e in range(n_experts):
+        out[e] = matrix(cfg, e, mat, M, K).aos()
+    return out
+
+
+def router_logits(cfg: int, token: int, n_experts: int) -> np.ndarray:
+    return rng(cfg, token, MAT_ROUTER).standard_normal(n_experts).astype(np.float32)
+
+
+def shared_gate_logit(cfg: int, token: int) -> np.float32:
+    return np.float32(rng(cfg, token, MAT_SHARED_GATE).standard_normal())
