@@ -1,0 +1,305 @@
+"""Python binding of the Q8_0 decode GEMV library (libq8gemv.so).
+
+Thin ctypes marshalling over the C ABI declared in include/q8gemv.h; the
+functions keep the C names.  PyTorch provides device memory and the current
+stream only: every step of the computation runs in the library's HIP kernels.
+There is no fallback path: if the shared library is missing, importing a
+function raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libq8gemv.so")
+
+Q8_OK, Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_EWORKSPACE, Q8_ELAUNCH = 0, -1, -2, -3, -4, -5, -6
+Q8_MAX_N = 8
+Q8_MAX_SLOTS = 8
+Q8_TILE_ROWS = 64
+Q8_PRO_NONE, Q8_PRO_RMSNORM, Q8_PRO_GQA = 0, 1, 2
+Q8_EPI_RESIDUAL, Q8_EPI_SWIGLU, Q8_EPI_ARGMAX = 1, 2, 4
+Q8_MOE_SCATTER, Q8_MOE_COMBINE, Q8_MOE_SWIGLU = 1, 2, 4
+Q8_OP_GEMV, Q8_OP_GEMV_FUSED, Q8_OP_ARGMAX, Q8_OP_MOE_SCATTER, Q8_OP_MOE_COMBINE = 1, 2, 3, 4, 5
+
+EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_gemv", "q8_0_gemv_fused", "q8_0_argmax",
+           "q8_0_route_topk", "q8_0_moe_gemv", "q8_0_workspace_bytes", "q8_0_gemv_plan",
+           "q8_0_strerror", "q8_0_version")
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn}: {strerror(code)} ({code})")
+
+
+class q8_0_weights(ctypes.Structure):
+    _fields_ = [("qs", ctypes.c_void_p), ("d", ctypes.c_void_p), ("M", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("n_mats", ctypes.c_int64),
+                ("qs_stride", ctypes.c_int64), ("d_stride", ctypes.c_int64)]
+
+
+class q8_0_fusion(ctypes.Structure):
+    _fields_ = [("prologue", ctypes.c_int32), ("epilogue", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("gqa_offset", ctypes.c_int64), ("residual", ctypes.c_void_p),
+                ("argmax_out", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded shared library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_quantized_gemv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        PW = ctypes.POINTER(q8_0_weights)
+        L.q8_0_packed_size.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+        L.q8_0_repack.argtypes = [P, I64, I64, P, P, P]
+        L.q8_0_gemv.argtypes = [PW, P, P, I64, I64, I64, P, SZ, P]
+        L.q8_0_gemv_fused.argtypes = [PW, P, P, I64, I64, ctypes.POINTER(q8_0_fusion), P, SZ, P]
+        L.q8_0_argmax.argtypes = [P, I64, P, P, SZ, P]
+        L.q8_0_route_topk.argtypes = [P, I32, I32, P, P, P]
+        L.q8_0_moe_gemv.argtypes = [PW, P, P, P, P, I64, I64, I32, I32, PW, P, P, P, SZ, P]
+        L.q8_0_workspace_bytes.argtypes = [I32, I64, I64, I64, I64, I64, I32]
+        L.q8_0_workspace_bytes.restype = SZ
+        L.q8_0_gemv_plan.argtypes = [I64, I64, I64, I32, ctypes.POINTER(I32)]
+        L.q8_0_strerror.argtypes = [ctypes.c_int]
+        L.q8_0_strerror.restype = ctypes.c_char_p
+        L.q8_0_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().q8_0_strerror(code).decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != Q8_OK:
+        raise Q8Error(fn, rc)
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# Workspace: zero-filled once, grown on demand (growing allocates, so size it
+# before capturing a graph).  Calls on different streams need distinct ones.
+# ---------------------------------------------------------------------------
+class Workspace:
+    def __init__(self, nbytes: int = 0, device=None):
+        self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8,
+                               device=device or torch.device("cuda"))
+
+    def get(self, nbytes: int) -> tuple[int, int]:
+        if nbytes == 0:
+            return 0, 0
+        if self.buf.numel() < nbytes:
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.buf.device)
+        return self.buf.data_ptr(), self.buf.numel()
+
+
+_default_ws: dict = {}
+
+
+def default_workspace(device=None) -> Workspace:
+    dev = torch.device(device) if device is not None else torch.device("cuda",
+                                                                       torch.cuda.current_device())
+    if dev not in _default_ws:
+        _default_ws[dev] = Workspace(1 << 20, dev)
+    return _default_ws[dev]
+
+
+def q8_0_workspace_bytes(op: int, M: int, K: int, N: int, M2: int = 0, K2: int = 0,
+                         flags: int = 0) -> int:
+    return int(lib().q8_0_workspace_bytes(op, M, K, N, M2, K2, flags))
+
+
+def q8_0_gemv_plan(M: int, K: int, N: int = 1, epilogue: int = 0) -> dict:
+    out = (ctypes.c_int32 * 4)()
+    _check("q8_0_gemv_plan", lib().q8_0_gemv_plan(M, K, N, epilogue, out))
+    return {"workgroups": out[0], "waves_per_wg": out[1], "units_per_tile": out[2],
+            "wgs_per_tile": out[3]}
+
+
+def q8_0_version() -> int:
+    return lib().q8_0_version()
+
+
+# ---------------------------------------------------------------------------
+# Packed weights
+# ---------------------------------------------------------------------------
+def q8_0_packed_size(M: int, K: int) -> tuple[int, int]:
+    qb, db = ctypes.c_size_t(), ctypes.c_size_t()
+    _check("q8_0_packed_size", lib().q8_0_packed_size(M, K, ctypes.byref(qb), ctypes.byref(db)))
+    return qb.value, db.value
+
+
+class PackedQ8:
+    """Packed device weights of one matrix or a stack of n_mats matrices."""
+
+    def __init__(self, qs: torch.Tensor, d: torch.Tensor, M: int, K: int, n_mats: int = 1):
+        qb, db = q8_0_packed_size(M, K)
+        self.qs, self.d, self.M, self.K, self.n_mats = qs, d, M, K, n_mats
+        self.qs_bytes, self.d_bytes = qb, db
+        self.desc = q8_0_weights(qs.data_ptr(), d.data_ptr(), M, K, n_mats, qb, db)
+
+    @classmethod
+    def empty(cls, M: int, K: int, n_mats: int = 1, device=None) -> "PackedQ8":
+        qb, db = q8_0_packed_size(M, K)
+        dev = device or torch.device("cuda")
+        qs = torch.empty(n_mats * qb, dtype=torch.uint8, device=dev)
+        d = torch.empty(n_mats * db, dtype=torch.uint8, device=dev)
+        return cls(qs, d, M, K, n_mats)
+
+    @classmethod
+    def from_aos(cls, aos: torch.Tensor, M: int, K: int, n_mats: int = 1,
+                 stream=None) -> "PackedQ8":
+        """Repack GGUF Q8_0 blocks (uint8 device tensor of n_mats*M*(K/32)*34
+        bytes) with q8_0_repack, one matrix at a time."""
+        _need(aos, torch.uint8, "aos")
+        per = M * (K // 32) * 34
+        if aos.numel() != n_mats * per:
+            raise ValueError(f"aos has {aos.numel()} bytes, expected {n_mats * per}")
+        p = cls.empty(M, K, n_mats, aos.device)
+        for e in range(n_mats):
+            q8_0_repack(aos[e * per:(e + 1) * per], M, K, p.qs[e * p.qs_bytes:],
+                        p.d[e * p.d_bytes:], stream)
+        return p
+
+    def expert(self, e: int) -> "PackedQ8":
+        return PackedQ8(self.qs[e * self.qs_bytes:(e + 1) * self.qs_bytes],
+                        self.d[e * self.d_bytes:(e + 1) * self.d_bytes], self.M, self.K, 1)
+
+
+def q8_0_repack(aos: torch.Tensor, M: int, K: int, qs: torch.Tensor, d: torch.Tensor,
+                stream=None) -> None:
+    _need(aos, torch.uint8, "aos")
+    _check("q8_0_repack", lib().q8_0_repack(aos.data_ptr(), M, K, qs.data_ptr(), d.data_ptr(),
+                                            _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# GEMV family
+# ---------------------------------------------------------------------------
+def _ws(ws, nbytes: int, device) -> tuple[int, int]:
+    if nbytes == 0:
+        return 0, 0
+    if ws is None:
+        ws = default_workspace(device)
+    if isinstance(ws, Workspace):
+        return ws.get(nbytes)
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def q8_0_gemv(W: PackedQ8, x: torch.Tensor, y: torch.Tensor | None = None, workspace=None,
+              stream=None) -> torch.Tensor:
+    """y[N][M] = x[N][K] @ W^T for packed Q8_0 weights W (x float32)."""
+    _need(x, torch.float32, "x")
+    N = 1 if x.dim() == 1 else x.shape[0]
+    if y is None:
+        y = torch.empty((W.M,) if x.dim() == 1 else (N, W.M), dtype=torch.float32,
+                        device=x.device)
+    _need(y, torch.float32, "y")
+    wsp, wsb = _ws(workspace, q8_0_workspace_bytes(Q8_OP_GEMV, W.M, W.K, N), x.device)
+    _check("q8_0_gemv", lib().q8_0_gemv(ctypes.byref(W.desc), x.data_ptr(), y.data_ptr(), W.M,
+                                        W.K, N, wsp, wsb, _stream(stream)))
+    return y
+
+
+def make_fusion(prologue: int = Q8_PRO_NONE, epilogue: int = 0, eps: float = 0.0,
+                n_heads: int = 0, n_kv_heads: int = 0, head_dim: int = 0, gqa_offset: int = 0,
+                residual: torch.Tensor | None = None,
+                argmax_out: torch.Tensor | None = None) -> q8_0_fusion:
+    return q8_0_fusion(prologue, epilogue, eps, n_heads, n_kv_heads, head_dim, gqa_offset,
+                       residual.data_ptr() if residual is not None else None,
+                       argmax_out.data_ptr() if argmax_out is not None else None)
+
+
+def q8_0_gemv_fused(W: PackedQ8, x: torch.Tensor, y: torch.Tensor, fusion: q8_0_fusion,
+                    workspace=None, stream=None) -> torch.Tensor:
+    _need(x, torch.float32, "x")
+    _need(y, torch.float32, "y")
+    wsp, wsb = _ws(workspace,
+                   q8_0_workspace_bytes(Q8_OP_GEMV_FUSED, W.M, W.K, fusion.epilogue), x.device)
+    _check("q8_0_gemv_fused", lib().q8_0_gemv_fused(ctypes.byref(W.desc), x.data_ptr(),
+                                                    y.data_ptr(), W.M, W.K, ctypes.byref(fusion),
+                                                    wsp, wsb, _stream(stream)))
+    return y
+
+
+def q8_0_argmax(v: torch.Tensor, out: torch.Tensor | None = None, workspace=None,
+                stream=None) -> torch.Tensor:
+    _need(v, torch.float32, "v")
+    if out is None:
+        out = torch.empty(1, dtype=torch.int32, device=v.device)
+    _need(out, torch.int32, "out")
+    wsp, wsb = _ws(workspace, q8_0_workspace_bytes(Q8_OP_ARGMAX, v.numel(), 0, 0), v.device)
+    _check("q8_0_argmax", lib().q8_0_argmax(v.data_ptr(), v.numel(), out.data_ptr(), wsp, wsb,
+                                            _stream(stream)))
+    return out
+
+
+def q8_0_route_topk(logits: torch.Tensor, k: int, expert_ids: torch.Tensor | None = None,
+                    slot_weights: torch.Tensor | None = None, stream=None):
+    _need(logits, torch.float32, "logits")
+    if expert_ids is None:
+        expert_ids = torch.empty(k, dtype=torch.int32, device=logits.device)
+    if slot_weights is None:
+        slot_weights = torch.empty(k, dtype=torch.float32, device=logits.device)
+    _need(expert_ids, torch.int32, "expert_ids")
+    _need(slot_weights, torch.float32, "slot_weights")
+    _check("q8_0_route_topk", lib().q8_0_route_topk(logits.data_ptr(), logits.numel(), k,
+                                                    expert_ids.data_ptr(),
+                                                    slot_weights.data_ptr(), _stream(stream)))
+    return expert_ids, slot_weights
+
+
+def q8_0_moe_gemv(W_experts: PackedQ8, expert_ids: torch.Tensor, slot_weights, x: torch.Tensor,
+                  y: torch.Tensor, mode: int, shared: PackedQ8 | None = None, shared_gate=None,
+                  dev_status: torch.Tensor | None = None, workspace=None,
+                  stream=None) -> torch.Tensor:
+    """All routed-expert slots (and the shared expert) in one launch; see
+    q8_0_moe_gemv in include/q8gemv.h for the modes."""
+    _need(expert_ids, torch.int32, "expert_ids")
+    _need(x, torch.float32, "x")
+    _need(y, torch.float32, "y")
+    S = expert_ids.numel()
+    base = mode & ~Q8_MOE_SWIGLU
+    if shared is not None:
+        M2, K2 = shared.M, shared.K
+    else:
+        M2, K2 = 0, 0
+    op = Q8_OP_MOE_SCATTER if base == Q8_MOE_SCATTER else Q8_OP_MOE_COMBINE
+    wsp, wsb = _ws(workspace, q8_0_workspace_bytes(op, W_experts.M, W_experts.K, S, M2, K2, mode),
+                   x.device)
+    rc = lib().q8_0_moe_gemv(
+        ctypes.byref(W_experts.desc), expert_ids.data_ptr(),
+        slot_weights.data_ptr() if slot_weights is not None else None,
+        x.data_ptr(), y.data_ptr(), W_experts.M, W_experts.K, S, mode,
+        ctypes.byref(shared.desc) if shared is not None else None,
+        shared_gate.data_ptr() if shared_gate is not None else None,
+        dev_status.data_ptr() if dev_status is not None else None, wsp, wsb, _stream(stream))
+    _check("q8_0_moe_gemv", rc)
+    return y

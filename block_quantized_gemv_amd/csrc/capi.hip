@@ -1,0 +1,377 @@
+// capi.hip -- the extern "C" boundary: argument validation, problem setup and
+// launch on the caller's stream.  Host-side checks follow the hardening notes
+// of "fusedtok 1.3.0" (1.2.1: host-side validation, a documented device-tensor
+// trust boundary, empty-input guards; 1.3: zero-copy helpers reject CPU
+// operands because a host pointer in a kernel poisons the context).  Values
+// that live in device memory (expert ids) are inside the trust boundary: the
+// kernels bound-check them instead of reading through them.
+#include <string.h>
+
+#include "q8_internal.h"
+
+using namespace q8;
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+int check_dev(const void* p) {
+  if (!p) return Q8_ENULL;
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky last-error of the failed query
+    return Q8_EHOSTPTR;
+  }
+  if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged) return Q8_EHOSTPTR;
+  return Q8_OK;
+}
+
+int check_dev_aligned(const void* p, size_t align) {
+  if (!p) return Q8_ENULL;
+  if (reinterpret_cast<uintptr_t>(p) % align) return Q8_EALIGN;
+  return check_dev(p);
+}
+
+bool shape_ok(int64_t M, int64_t K) {
+  return M >= 0 && M <= (int64_t)0x7fffffff - 64 && K > 0 && K % 32 == 0 && K <= Q8_MAX_K;
+}
+
+// Scalar checks of a weight descriptor (no pointer queries).
+int check_weights_shape(const q8_0_weights* W, int64_t M, int64_t K, bool stacked) {
+  if (!W) return Q8_ENULL;
+  if (W->M != M || W->K != K || !shape_ok(M, K)) return Q8_EINVAL;
+  if (W->n_mats < 1 || (!stacked && W->n_mats != 1)) return Q8_EINVAL;
+  if (W->n_mats > 1) {
+    size_t qb = 0, db = 0;
+    q8_0_packed_size(M, K, &qb, &db);
+    if (W->qs_stride < (int64_t)qb || W->d_stride < (int64_t)db || W->qs_stride % 16 ||
+        W->d_stride % 8)
+      return Q8_EINVAL;
+  }
+  return Q8_OK;
+}
+
+int check_weights_ptrs(const q8_0_weights* W) {
+  int rc = check_dev_aligned(W->qs, 16);
+  if (rc) return rc;
+  return check_dev_aligned(W->d, 8);
+}
+
+SegDesc seg_of(const q8_0_weights* W, const float* x, int64_t x_stride) {
+  SegDesc s;
+  memset(&s, 0, sizeof(s));
+  s.W = W;
+  s.x = x;
+  s.x_stride = x_stride;
+  s.alpha_mode = A_ONE;
+  return s;
+}
+
+// ---- problem builders (shared by sizing and launching) --------------------
+int build_gemv(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
+               const q8_0_fusion* f, ProbDesc* pd) {
+  memset(pd, 0, sizeof(*pd));
+  pd->nseg = 1;
+  pd->seg[0] = seg_of(W, x, K);
+  pd->R = 1;
+  pd->M = M;
+  pd->y = y;
+  pd->y_stride = M;
+  if (!f) return Q8_OK;
+  if (N != 1) return Q8_EINVAL;
+  const int ep = f->epilogue;
+  if (ep & ~(Q8_EPI_RESIDUAL | Q8_EPI_SWIGLU | Q8_EPI_ARGMAX)) return Q8_EINVAL;
+  if (f->prologue == Q8_PRO_RMSNORM) {
+    if (!(f->eps >= 0.f)) return Q8_EINVAL;
+    pd->flags |= F_RMSNORM;
+    pd->rms_x = x;
+    pd->rms_K = K;
+    pd->eps = f->eps;
+  } else if (f->prologue == Q8_PRO_GQA) {
+    if (f->n_heads <= 0 || f->n_kv_heads <= 0 || f->n_heads % f->n_kv_heads ||
+        f->head_dim <= 0 || f->head_dim % 32 || (int64_t)f->n_heads * f->head_dim != K ||
+        f->gqa_offset < 0)
+      return Q8_EINVAL;
+    pd->seg[0].gqa_group = f->n_heads / f->n_kv_heads;
+    pd->seg[0].gqa_hd = f->head_dim;
+    pd->seg[0].gqa_off = f->gqa_offset;
+  } else if (f->prologue != Q8_PRO_NONE) {
+    return Q8_EINVAL;
+  }
+  if (ep & Q8_EPI_SWIGLU) {
+    if (ep & (Q8_EPI_RESIDUAL | Q8_EPI_ARGMAX)) return Q8_EINVAL;
+    if (M % 2 || (M / 2) % kTile) return Q8_EINVAL;
+    pd->R = 2;
+    pd->flags |= F_SWIGLU;
+  }
+  if (ep & Q8_EPI_RESIDUAL) {
+    pd->flags |= F_RESIDUAL;
+    pd->residual = f->residual;
+  }
+  if (ep & Q8_EPI_ARGMAX) {
+    pd->flags |= F_ARGMAX;
+    pd->argmax_out = f->argmax_out;
+  }
+  return Q8_OK;
+}
+
+int build_moe(const q8_0_weights* We, const int32_t* ids, const float* sw, const float* x,
+              float* y, int64_t M, int64_t K, int32_t S, int32_t mode, const q8_0_weights* sh,
+              const float* sgate, int32_t* status, ProbDesc* pd, int* nprob) {
+  const bool swiglu = mode & Q8_MOE_SWIGLU;
+  const int base = mode & ~Q8_MOE_SWIGLU;
+  if (S < 1 || S > Q8_MAX_SLOTS) return Q8_EINVAL;
+  if (base == Q8_MOE_SCATTER) {
+    if (S + (sh ? 1 : 0) > kMaxProb) return Q8_EINVAL;
+    if (swiglu && (M % 2 || (M / 2) % kTile)) return Q8_EINVAL;
+    if (swiglu && sh && (sh->M % 2 || (sh->M / 2) % kTile)) return Q8_EINVAL;
+    if (sh && sh->K != K) return Q8_EINVAL;
+    const int64_t Mo = swiglu ? M / 2 : M;
+    int n = 0;
+    for (int s = 0; s < S; ++s, ++n) {
+      ProbDesc& p = pd[n];
+      memset(&p, 0, sizeof(p));
+      p.nseg = 1;
+      p.seg[0] = seg_of(We, x, K);
+      p.seg[0].eid = ids;
+      p.seg[0].slot = s;
+      p.R = swiglu ? 2 : 1;
+      p.M = M;
+      p.flags = swiglu ? F_SWIGLU : 0;
+      p.y = y ? y + (int64_t)s * Mo : nullptr;
+      p.y_stride = Mo;
+      p.dev_status = status;
+    }
+    if (sh) {
+      ProbDesc& p = pd[n++];
+      memset(&p, 0, sizeof(p));
+      p.nseg = 1;
+      p.seg[0] = seg_of(sh, x, K);
+      p.R = swiglu ? 2 : 1;
+      p.M = sh->M;
+      p.flags = swiglu ? F_SWIGLU : 0;
+      p.y = y ? y + (int64_t)S * Mo : nullptr;
+      p.y_stride = swiglu ? sh->M / 2 : sh->M;
+      p.dev_status = status;
+    }
+    *nprob = n;
+    return Q8_OK;
+  }
+  if (base == Q8_MOE_COMBINE) {
+    if (swiglu) return Q8_EINVAL;
+    if (S + (sh ? 1 : 0) > kMaxSeg) return Q8_EINVAL;
+    if (sh && sh->M != M) return Q8_EINVAL;
+    ProbDesc& p = pd[0];
+    memset(&p, 0, sizeof(p));
+    for (int s = 0; s < S; ++s) {
+      p.seg[s] = seg_of(We, x ? x + (int64_t)s * K : nullptr, K);
+      p.seg[s].eid = ids;
+      p.seg[s].slot = s;
+      p.seg[s].alpha_mode = A_PTR;
+      p.seg[s].alpha_ptr = sw ? sw + s : nullptr;
+    }
+    p.nseg = S;
+    if (sh) {
+      p.seg[S] = seg_of(sh, x ? x + (int64_t)S * K : nullptr, sh->K);
+      p.seg[S].alpha_mode = A_SIGMOID;
+      p.seg[S].alpha_ptr = sgate;
+      p.nseg = S + 1;
+    }
+    p.R = 1;
+    p.M = M;
+    p.y = y;
+    p.y_stride = M;
+    p.dev_status = status;
+    *nprob = 1;
+    return Q8_OK;
+  }
+  return Q8_EINVAL;
+}
+
+}  // namespace
+
+extern "C" {
+
+int q8_0_packed_size(int64_t M, int64_t K, size_t* qs_bytes, size_t* d_bytes) {
+  if (!qs_bytes || !d_bytes) return Q8_ENULL;
+  if (!shape_ok(M, K)) return Q8_EINVAL;
+  const int64_t T = cdiv(M, kTile);
+  *qs_bytes = (size_t)(T * kTile * K);
+  *d_bytes = (size_t)(T * cdiv(K / 32, 4) * kTile * 8);
+  return Q8_OK;
+}
+
+int q8_0_repack(const void* aos, int64_t M, int64_t K, void* qs, void* d, void* stream) {
+  if (!shape_ok(M, K)) return Q8_EINVAL;
+  if (!aos || !qs || !d) return Q8_ENULL;
+  if (M == 0) return Q8_OK;
+  int rc;
+  if ((rc = check_dev_aligned(aos, 2)) || (rc = check_dev_aligned(qs, 16)) ||
+      (rc = check_dev_aligned(d, 8)))
+    return rc;
+  return launch_repack(aos, M, K, qs, d, static_cast<hipStream_t>(stream));
+}
+
+static int gemv_common(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,
+                       int64_t N, const q8_0_fusion* f, void* ws, size_t wsb, void* stream) {
+  int rc = check_weights_shape(W, M, K, false);
+  if (rc) return rc;
+  if (N < 1 || N > Q8_MAX_N) return Q8_EINVAL;
+  if (!x || !y) return Q8_ENULL;
+  ProbDesc pd;
+  if ((rc = build_gemv(W, x, y, M, K, N, f, &pd))) return rc;
+  if (M == 0) return Q8_OK;
+  if ((rc = check_weights_ptrs(W)) || (rc = check_dev_aligned(x, 4)) ||
+      (rc = check_dev_aligned(y, 4)))
+    return rc;
+  if ((pd.flags & F_RESIDUAL) && (rc = check_dev_aligned(pd.residual, 4))) return rc;
+  if ((pd.flags & F_ARGMAX) && (rc = check_dev_aligned(pd.argmax_out, 4))) return rc;
+  if (ws && (rc = check_dev(ws))) return rc;
+  return launch_problems(&pd, 1, (int)N, ws, wsb, static_cast<hipStream_t>(stream));
+}
+
+int q8_0_gemv(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  return gemv_common(W, x, y, M, K, N, nullptr, workspace, workspace_bytes, stream);
+}
+
+int q8_0_gemv_fused(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,
+                    const q8_0_fusion* fusion, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (!fusion) return Q8_ENULL;
+  return gemv_common(W, x, y, M, K, 1, fusion, workspace, workspace_bytes, stream);
+}
+
+int q8_0_argmax(const float* v, int64_t n, int32_t* out_idx, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (n < 0 || n >= ((int64_t)1 << 31)) return Q8_EINVAL;
+  if (!v || !out_idx) return Q8_ENULL;
+  if (n == 0) return Q8_OK;
+  int rc;
+  if ((rc = check_dev_aligned(v, 4)) || (rc = check_dev_aligned(out_idx, 4))) return rc;
+  if (workspace && (rc = check_dev(workspace))) return rc;
+  return launch_argmax(v, n, out_idx, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream));
+}
+
+int q8_0_route_topk(const float* logits, int32_t E, int32_t k, int32_t* expert_ids,
+                    float* slot_weights, void* stream) {
+  if (E < 1 || E > 1024 || k < 1 || k > E || k > Q8_MAX_SLOTS) return Q8_EINVAL;
+  if (!logits || !expert_ids || !slot_weights) return Q8_ENULL;
+  int rc;
+  if ((rc = check_dev_aligned(logits, 4)) || (rc = check_dev_aligned(expert_ids, 4)) ||
+      (rc = check_dev_aligned(slot_weights, 4)))
+    return rc;
+  return launch_route(logits, E, k, expert_ids, slot_weights, static_cast<hipStream_t>(stream));
+}
+
+int q8_0_moe_gemv(const q8_0_weights* W_experts, const int32_t* expert_ids,
+                  const float* slot_weights, const float* x, float* y, int64_t M, int64_t K,
+                  int32_t n_slots, int32_t mode, const q8_0_weights* shared,
+                  const float* shared_gate, int32_t* dev_status, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int rc = check_weights_shape(W_experts, M, K, true);
+  if (rc) return rc;
+  const int base = mode & ~Q8_MOE_SWIGLU;
+  if (shared) {
+    const int64_t shK = base == Q8_MOE_COMBINE ? shared->K : K;
+    const int64_t shM = base == Q8_MOE_COMBINE ? M : shared->M;
+    if ((rc = check_weights_shape(shared, shM, shK, false))) return rc;
+  }
+  if (!x || !y || !expert_ids) return Q8_ENULL;
+  if (base == Q8_MOE_COMBINE && (!slot_weights || (shared && !shared_gate))) return Q8_ENULL;
+  ProbDesc pd[kMaxProb];
+  int np = 0;
+  if ((rc = build_moe(W_experts, expert_ids, slot_weights, x, y, M, K, n_slots, mode, shared,
+                      shared_gate, dev_status, pd, &np)))
+    return rc;
+  if (M == 0) return Q8_OK;
+  if ((rc = check_weights_ptrs(W_experts)) || (rc = check_dev_aligned(x, 4)) ||
+      (rc = check_dev_aligned(y, 4)) || (rc = check_dev_aligned(expert_ids, 4)))
+    return rc;
+  if (shared && (rc = check_weights_ptrs(shared))) return rc;
+  if (base == Q8_MOE_COMBINE) {
+    if ((rc = check_dev_aligned(slot_weights, 4))) return rc;
+    if (shared && (rc = check_dev_aligned(shared_gate, 4))) return rc;
+  }
+  if (dev_status && (rc = check_dev_aligned(dev_status, 4))) return rc;
+  if (workspace && (rc = check_dev(workspace))) return rc;
+  return launch_problems(pd, np, 1, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t M2, int64_t K2,
+                            int32_t flags) {
+  Plan plan;
+  if (op == Q8_OP_ARGMAX) return argmax_ws_bytes(M);
+  if (op == Q8_OP_GEMV || op == Q8_OP_GEMV_FUSED) {
+    if (!shape_ok(M, K) || M == 0) return 0;
+    q8_0_weights W = {nullptr, nullptr, M, K, 1, 0, 0};
+    q8_0_fusion f;
+    memset(&f, 0, sizeof(f));
+    const q8_0_fusion* fp = nullptr;
+    int64_t n = N;
+    if (op == Q8_OP_GEMV_FUSED) {
+      f.epilogue = (int32_t)N;
+      fp = &f;
+      n = 1;
+    } else if (N < 1 || N > Q8_MAX_N) {
+      return 0;
+    }
+    ProbDesc pd;
+    if (build_gemv(&W, nullptr, nullptr, M, K, n, fp, &pd)) return 0;
+    if (plan_problems(&pd, 1, (int)n, &plan)) return 0;
+    return plan.ws_bytes;
+  }
+  if (op == Q8_OP_MOE_SCATTER || op == Q8_OP_MOE_COMBINE) {
+    if (!shape_ok(M, K) || M == 0) return 0;
+    q8_0_weights W = {nullptr, nullptr, M, K, 1, 0, 0};
+    q8_0_weights S2 = {nullptr, nullptr, M2, K2, 1, 0, 0};
+    const bool has_sh = M2 > 0 && K2 > 0;
+    const int mode = (op == Q8_OP_MOE_SCATTER ? Q8_MOE_SCATTER : Q8_MOE_COMBINE) |
+                     (flags & Q8_MOE_SWIGLU);
+    ProbDesc pd[kMaxProb];
+    int np = 0;
+    if (build_moe(&W, nullptr, nullptr, nullptr, nullptr, M, K, (int32_t)N, mode,
+                  has_sh ? &S2 : nullptr, nullptr, nullptr, pd, &np))
+      return 0;
+    if (plan_problems(pd, np, 1, &plan)) return 0;
+    return plan.ws_bytes;
+  }
+  return 0;
+}
+
+int q8_0_gemv_plan(int64_t M, int64_t K, int64_t N, int32_t epilogue, int32_t out[4]) {
+  if (!out) return Q8_ENULL;
+  if (!shape_ok(M, K) || M == 0 || N < 1 || N > Q8_MAX_N) return Q8_EINVAL;
+  q8_0_weights W = {nullptr, nullptr, M, K, 1, 0, 0};
+  q8_0_fusion f;
+  memset(&f, 0, sizeof(f));
+  f.epilogue = epilogue;
+  ProbDesc pd;
+  if (build_gemv(&W, nullptr, nullptr, M, K, epilogue ? 1 : N, epilogue ? &f : nullptr, &pd))
+    return Q8_EINVAL;
+  Plan plan;
+  if (plan_problems(&pd, 1, (int)(epilogue ? 1 : N), &plan)) return Q8_EINVAL;
+  out[0] = plan.total_wg;
+  out[1] = kWaves;
+  out[2] = plan.U[0];
+  out[3] = plan.P[0];
+  return Q8_OK;
+}
+
+const char* q8_0_strerror(int status) {
+  switch (status) {
+    case Q8_OK: return "ok";
+    case Q8_EINVAL: return "invalid argument (shape, count or flags)";
+    case Q8_ENULL: return "required pointer is NULL";
+    case Q8_EALIGN: return "pointer is not aligned as required";
+    case Q8_EHOSTPTR: return "pointer is not device memory";
+    case Q8_EWORKSPACE: return "workspace missing or too small";
+    case Q8_ELAUNCH: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int q8_0_version(void) { return kVersion; }
+
+}  // extern "C"

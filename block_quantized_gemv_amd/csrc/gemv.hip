@@ -1,0 +1,577 @@
+// gemv.hip -- Q8_0 GEMV kernels for gfx950 (CDNA4) and their host launcher.
+//
+// One kernel body serves every GEMV-shaped step of the decode path: the dense
+// projections (qkv, wo, gate_up, down, lm_head) of the decode step profiled in
+// the "Lumen v0.3.0" release notes ("Phase 7.E.0"), the small-N verify chunk
+// ("skuznetsov/cogni-ml" README, target-verifier chunks), and the routed-expert
+// FFN of the "#144" Qwen1.5-MoE PR with all slots in one launch (routed-expert
+// fusion comments: slot index folded into the work-group id for gate/up; the
+// down projection looping over slots with one running accumulation).
+//
+// Mapping (MI355X-first, not the pages' warp-per-row designs):
+//  * A packed tile holds 64 rows; lane i of a wave owns row i of the tile, so a
+//    wave's 16-byte quant load covers 64 rows x 16 weights = 1 KiB of
+//    contiguous HBM (global_load_dwordx4, non-temporal), and its 8-byte scale
+//    load covers 4 blocks of all 64 rows (512 B contiguous).
+//  * The activation vector is the same for every lane, so it is read with
+//    scalar loads into SGPRs and used directly as the FMA's scalar operand;
+//    each weight costs one int8->fp32 convert (SDWA byte select) and one FMA.
+//    No LDS traffic on the hot loop and no cross-lane reduction per row.
+//  * A tile's K range is split into "units", one per wave; units of one tile
+//    are folded in a fixed order (bitwise reproducible).  When a tile's units
+//    span several workgroups, each writes its partials to the workspace and
+//    the last-arriving workgroup (ticket counter with release/acquire fences)
+//    folds them in unit order and resets the ticket for the next call.
+//  * No matrix cores: at N <= 8 the product is HBM-bound, not a dense
+//    contraction worth MFMA tiles.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "q8_internal.h"
+
+namespace q8 {
+
+// Signed byte k of a 32-bit word, converted exactly to fp32.
+__device__ __forceinline__ float q_at(uint32_t w, int k) {
+  return (float)(int32_t)(int8_t)(w >> (8 * k));
+}
+
+// binary16 bits -> fp32 (exact, subnormals included).
+__device__ __forceinline__ float f16_to_f32(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// Scale of block j (0..3) of a quad held as two dwords.
+__device__ __forceinline__ uint32_t quad_bits(u32x2 sc, int j) {
+  const uint32_t w = (j & 2) ? sc.y : sc.x;
+  return (j & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// Start of the 32 activations of block b (all columns offset by n * xs).
+__device__ __forceinline__ const float* x_block(const float* x, int b, int gqa_group, int gqa_hd,
+                                                int64_t gqa_off) {
+  if (gqa_group > 0) {
+    const int k = b * 32;
+    const int head = k / gqa_hd;
+    return x + gqa_off + (int64_t)(head / gqa_group) * gqa_hd + (k - head * gqa_hd);
+  }
+  return x + (int64_t)b * 32;
+}
+
+// Activations are read through the constant address space: they are not
+// written while a GEMV runs, and wave-uniform constant loads become scalar
+// loads (s_load_dwordx*) whose results feed the FMAs as SGPR operands.
+typedef const __attribute__((address_space(4))) float* cfloat_p;
+
+// acc[n] += d * sum_j q[j] * xb[n*xs + j] over the 32 weights of one block.
+template <int N>
+__device__ __forceinline__ void block_fma(u32x4 q0, u32x4 q1, const float* xg, int64_t xs,
+                                          float dsc, float (&acc)[N]) {
+  const cfloat_p xb = (cfloat_p)xg;
+  const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  float p[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) p[n] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float qf = q_at(w[j >> 2], j & 3);
+#pragma unroll
+    for (int n = 0; n < N; ++n) p[n] = fmaf(qf, xb[n * xs + j], p[n]);
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) acc[n] = fmaf(dsc, p[n], acc[n]);
+}
+
+// Partial dot products of the 64 rows of one tile over blocks [b0, b1).
+// qs_tile / d_tile point at the tile's packed quants / scales.
+template <int N>
+__device__ __forceinline__ void dot_range(const uint8_t* qs_tile, const uint8_t* d_tile, int b0,
+                                          int b1, int lane, const float* x, int64_t xs, int gg,
+                                          int ghd, int64_t goff, float (&acc)[N]) {
+  const u32x4* qp = reinterpret_cast<const u32x4*>(qs_tile) + lane;  // chunk c: qp[c * 64]
+  const u32x2* dp = reinterpret_cast<const u32x2*>(d_tile) + lane;   // quad g: dp[g * 64]
+  int b = b0;
+  // Leading blocks up to a quad boundary.
+  for (; b < b1 && (b & 3); ++b) {
+    const u32x2 sc = __builtin_nontemporal_load(dp + (b >> 2) * 64);
+    const u32x4 q0 = __builtin_nontemporal_load(qp + (2 * b) * 64);
+    const u32x4 q1 = __builtin_nontemporal_load(qp + (2 * b + 1) * 64);
+    block_fma<N>(q0, q1, x_block(x, b, gg, ghd, goff), xs, f16_to_f32(quad_bits(sc, b & 3)), acc);
+  }
+  // Whole quads, software-pipelined one quad ahead.
+  const int nq = (b1 - b) >> 2;
+  if (nq > 0) {
+    int g = b >> 2;
+    u32x4 cq[8];
+    u32x2 csc = __builtin_nontemporal_load(dp + g * 64);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cq[i] = __builtin_nontemporal_load(qp + (8 * g + i) * 64);
+    for (int it = 0; it < nq; ++it, ++g) {
+      u32x4 nq_[8];
+      u32x2 nsc;
+      if (it + 1 < nq) {
+        nsc = __builtin_nontemporal_load(dp + (g + 1) * 64);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) nq_[i] = __builtin_nontemporal_load(qp + (8 * (g + 1) + i) * 64);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int bb = 4 * g + j;
+        block_fma<N>(cq[2 * j], cq[2 * j + 1], x_block(x, bb, gg, ghd, goff), xs,
+                     f16_to_f32(quad_bits(csc, j)), acc);
+      }
+      if (it + 1 < nq) {
+        csc = nsc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cq[i] = nq_[i];
+      }
+    }
+    b += 4 * nq;
+  }
+  // Trailing blocks.
+  for (; b < b1; ++b) {
+    const u32x2 sc = __builtin_nontemporal_load(dp + (b >> 2) * 64);
+    const u32x4 q0 = __builtin_nontemporal_load(qp + (2 * b) * 64);
+    const u32x4 q1 = __builtin_nontemporal_load(qp + (2 * b + 1) * 64);
+    block_fma<N>(q0, q1, x_block(x, b, gg, ghd, goff), xs, f16_to_f32(quad_bits(sc, b & 3)), acc);
+  }
+}
+
+// Butterfly all-reduce over the wave; every lane ends with the same bits.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// (value, index) maximum with ties to the lower index; all lanes agree.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, 64);
+    const int oi = __shfl_xor(i, o, 64);
+    if (ov > v || (ov == v && oi < i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+__device__ __forceinline__ float seg_alpha(const Seg& s) {
+  if (s.alpha_mode == A_PTR) return *s.alpha_ptr;
+  if (s.alpha_mode == A_SIGMOID) return 1.0f / (1.0f + expf(-*s.alpha_ptr));
+  return 1.0f;
+}
+
+template <int N>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvParams p) {
+  __shared__ float lds_part[kWaves][N][64];
+  __shared__ int s_last;
+
+  const int g = blockIdx.x;
+  int pi = 0;
+  while (pi + 1 < p.nprob && g >= p.prob[pi + 1].wg0) ++pi;
+  const Prob& pr = p.prob[pi];
+
+  const int lg = g - pr.wg0;
+  const int ot = lg / pr.P;
+  const int pp = lg - ot * pr.P;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int u = pp * kWaves + wave;
+  const int us = pr.U / pr.R;  // units per tile of a pair
+
+  // RMS prologue: issue the loads early (wave 0 folds), reduce after the dot.
+  float rx[16];
+  const bool want_rms = (pr.flags & F_RMSNORM) && wave == 0 && pr.rms_K <= 1024;
+  if (want_rms) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = lane + 64 * i;
+      rx[i] = k < pr.rms_K ? pr.rms_x[k] : 0.f;
+    }
+  }
+
+  float acc[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) acc[n] = 0.f;
+  if (u < pr.U) {
+    const int tsel = u / us;
+    int v = u - tsel * us;
+    int si = pr.seg0;
+    while (v >= p.seg[si].units) {
+      v -= p.seg[si].units;
+      ++si;
+    }
+    const Seg& s = p.seg[si];
+    int e = 0;
+    bool ok = true;
+    if (s.eid) {
+      e = __builtin_amdgcn_readfirstlane(s.eid[s.slot]);
+      ok = e >= 0 && e < s.n_mats;
+    }
+    if (ok) {
+      const int t = ot + tsel * pr.Tout;
+      const uint8_t* qs_tile = s.qs + (int64_t)e * s.qs_stride + (int64_t)t * kTile * s.K;
+      const uint8_t* d_tile = s.d + (int64_t)e * s.d_stride + (int64_t)t * s.G * 512;
+      const int b0 = (int)((int64_t)v * s.nblk / s.units);
+      const int b1 = (int)((int64_t)(v + 1) * s.nblk / s.units);
+      dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
+                   s.gqa_off, acc);
+    } else if (lane == 0 && pr.dev_status) {
+      atomicOr(pr.dev_status, 1);
+    }
+  }
+
+  // ---- fold the units of this output tile in unit order -------------------
+  const float* part;
+  int pstride;  // floats between units
+  if (pr.P == 1) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) lds_part[wave][n][lane] = acc[n];
+    __syncthreads();
+    if (wave != 0) return;
+    part = &lds_part[0][0][0];
+    pstride = N * 64;
+  } else {
+    float* gp = pr.part + (int64_t)ot * pr.U * N * 64;
+    if (u < pr.U) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) gp[(u * N + n) * 64 + lane] = acc[n];
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(&pr.tickets[ot], 1u) == (unsigned)(pr.P - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (wave != 0) return;
+    if (lane == 0) pr.tickets[ot] = 0;  // ready for the next call
+    part = gp;
+    pstride = N * 64;
+  }
+
+  float val[2][N];
+#pragma unroll
+  for (int ts = 0; ts < 2; ++ts) {
+    if (ts >= pr.R) break;
+#pragma unroll
+    for (int n = 0; n < N; ++n) val[ts][n] = 0.f;
+    int uu = ts * us;
+    for (int si = pr.seg0; si < pr.seg0 + pr.nseg; ++si) {
+      const Seg& s = p.seg[si];
+      float ssum[N];
+#pragma unroll
+      for (int n = 0; n < N; ++n) ssum[n] = 0.f;
+      for (int i = 0; i < s.units; ++i, ++uu) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) ssum[n] += part[uu * pstride + n * 64 + lane];
+      }
+      if (s.alpha_mode == A_ONE) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) val[ts][n] += ssum[n];
+      } else {
+        const float a = seg_alpha(s);
+#pragma unroll
+        for (int n = 0; n < N; ++n) val[ts][n] = fmaf(a, ssum[n], val[ts][n]);
+      }
+    }
+  }
+
+  // ---- epilogue ---------------------------------------------------------------
+  float c = 1.0f;
+  if (pr.flags & F_RMSNORM) {
+    float ss = 0.f;
+    if (pr.rms_K <= 1024) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = fmaf(rx[i], rx[i], ss);
+    } else {
+      for (int k = lane; k < pr.rms_K; k += 64) {
+        const float t = pr.rms_x[k];
+        ss = fmaf(t, t, ss);
+      }
+    }
+    ss = wave_sum(ss);
+    c = 1.0f / sqrtf(ss / (float)pr.rms_K + pr.eps);
+  }
+  const int row = ot * kTile + lane;
+  const bool valid = row < pr.Mout;
+  if (pr.R == 2) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const float gt = val[0][n] * c;
+      const float up = val[1][n] * c;
+      const float h = gt / (1.0f + expf(-gt)) * up;
+      if (valid) pr.y[n * pr.y_stride + row] = h;
+    }
+    return;
+  }
+  float out[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    float v = val[0][n] * c;
+    if ((pr.flags & F_RESIDUAL) && valid) v += pr.residual[row];
+    out[n] = v;
+    if (valid) pr.y[n * pr.y_stride + row] = v;
+  }
+  if (pr.flags & F_ARGMAX) {
+    float mv = valid ? out[0] : -INFINITY;
+    int mi = row;
+    wave_argmax(mv, mi);
+    if (lane == 0) {
+      pr.am_val[ot] = mv;
+      pr.am_idx[ot] = mi;
+    }
+    __threadfence();
+    int last = 0;
+    if (lane == 0) last = atomicAdd(&pr.tickets[pr.Tout], 1u) == (unsigned)(pr.Tout - 1);
+    last = __builtin_amdgcn_readfirstlane(last);
+    if (!last) return;
+    __threadfence();
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int i = lane; i < pr.Tout; i += 64) {
+      const float tv = __builtin_nontemporal_load(pr.am_val + i);
+      const int ti = __builtin_nontemporal_load(pr.am_idx + i);
+      if (tv > bv || (tv == bv && ti < bi)) {
+        bv = tv;
+        bi = ti;
+      }
+    }
+    wave_argmax(bv, bi);
+    if (lane == 0) {
+      *pr.argmax_out = bi;
+      pr.tickets[pr.Tout] = 0;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: planning and launch.
+// ---------------------------------------------------------------------------
+namespace {
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  const int x = atoi(v);
+  return x > 0 ? x : dflt;
+}
+
+// Waves the planner aims for across one launch (all problems), and the
+// fewest blocks a unit should own.  Q8G_TARGET_WAVES / Q8G_MIN_BLOCKS override
+// them for tuning sweeps (they change the summation order, not the result
+// beyond the stated tolerance).
+int target_waves() {
+  static const int v = env_int("Q8G_TARGET_WAVES", 2048);
+  return v;
+}
+int min_blocks() {
+  static const int v = env_int("Q8G_MIN_BLOCKS", 4);
+  return v;
+}
+
+}  // namespace
+
+int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
+  memset(plan, 0, sizeof(*plan));
+  int64_t total_tout = 0;
+  int segc = 0;
+  for (int i = 0; i < nprob; ++i) {
+    const ProbDesc& pd = probs[i];
+    const int64_t Mout = pd.R == 2 ? pd.M / 2 : pd.M;
+    total_tout += cdiv(Mout, kTile);
+    segc += pd.nseg;
+  }
+  if (segc > kMaxSeg || nprob > kMaxProb || total_tout <= 0) return Q8_EINVAL;
+  const int64_t want_u = cdiv(target_waves(), total_tout);
+  size_t ws = 0;
+  int wg = 0;
+  int sbase = 0;
+  for (int i = 0; i < nprob; ++i) {
+    const ProbDesc& pd = probs[i];
+    const int64_t Mout = pd.R == 2 ? pd.M / 2 : pd.M;
+    const int64_t Tout = cdiv(Mout, kTile);
+    int64_t blocks = 0;
+    for (int s = 0; s < pd.nseg; ++s) blocks += pd.seg[s].W->K / 32;
+    // units per tile of a pair (per tsel)
+    int64_t us = cdiv(want_u, pd.R);
+    const int64_t us_max = blocks / min_blocks() > pd.nseg ? blocks / min_blocks() : pd.nseg;
+    if (us > us_max) us = us_max;
+    if (us < pd.nseg) us = pd.nseg;
+    if (us > blocks) us = blocks;
+    // at least one full workgroup per output tile when the K range allows it
+    if (us * pd.R < kWaves) {
+      us = cdiv(kWaves, pd.R);
+      if (us > us_max) us = us_max;
+      if (us > blocks) us = blocks;
+    }
+    int64_t U = us * pd.R;
+    if (U > kWaves) {  // fill whole workgroups
+      U = cdiv(U, kWaves) * kWaves;
+      us = U / pd.R;
+      if (us > blocks) us = blocks;
+      U = us * pd.R;
+    }
+    // distribute the us units over the segments in proportion to their blocks
+    int64_t left = us;
+    int64_t su[kMaxSeg];
+    for (int s = 0; s < pd.nseg; ++s) {
+      const int64_t nb = pd.seg[s].W->K / 32;
+      su[s] = us * nb / blocks;
+      if (su[s] < 1) su[s] = 1;
+      if (su[s] > nb) su[s] = nb;
+      left -= su[s];
+    }
+    while (left > 0) {  // give the rest to the segment with the most blocks per unit
+      int best = -1;
+      double bestr = 0;
+      for (int s = 0; s < pd.nseg; ++s) {
+        const int64_t nb = pd.seg[s].W->K / 32;
+        if (su[s] >= nb) continue;
+        const double r = (double)nb / (double)su[s];
+        if (r > bestr) {
+          bestr = r;
+          best = s;
+        }
+      }
+      if (best < 0) break;
+      ++su[best];
+      --left;
+    }
+    while (left < 0) {  // took too many (minimum one per segment)
+      int best = -1;
+      double bestr = 1e300;
+      for (int s = 0; s < pd.nseg; ++s) {
+        if (su[s] <= 1) continue;
+        const double r = (double)(pd.seg[s].W->K / 32) / (double)su[s];
+        if (r < bestr) {
+          bestr = r;
+          best = s;
+        }
+      }
+      if (best < 0) break;
+      --su[best];
+      ++left;
+    }
+    int64_t usum = 0;
+    for (int s = 0; s < pd.nseg; ++s) {
+      plan->seg_units[sbase + s] = (int32_t)su[s];
+      usum += su[s];
+    }
+    U = usum * pd.R;
+    const int64_t P = cdiv(U, kWaves);
+    plan->U[i] = (int32_t)U;
+    plan->P[i] = (int32_t)P;
+    // workspace: tickets, argmax partials, unit partials
+    const bool need = P > 1 || (pd.flags & F_ARGMAX);
+    plan->ws_off[i] = ws;
+    if (need) {
+      ws += align_up((size_t)(Tout + 1) * 4, 256);
+      ws += align_up((size_t)Tout * 4, 256) * 2;
+      if (P > 1) ws += align_up((size_t)Tout * U * N * 64 * 4, 256);
+    }
+    wg += (int)(Tout * P);
+    sbase += pd.nseg;
+  }
+  plan->ws_bytes = ws;
+  plan->total_wg = wg;
+  return Q8_OK;
+}
+
+template <int N>
+static hipError_t launch_n(const GemvParams& gp, int wgs, hipStream_t stream) {
+  hipLaunchKernelGGL(gemv_kernel<N>, dim3(wgs), dim3(kThreads), 0, stream, gp);
+  return hipGetLastError();
+}
+
+int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  Plan plan;
+  int rc = plan_problems(probs, nprob, N, &plan);
+  if (rc) return rc;
+  if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return Q8_EWORKSPACE;
+  GemvParams gp;
+  memset(&gp, 0, sizeof(gp));
+  gp.nprob = nprob;
+  int sbase = 0;
+  int wg = 0;
+  for (int i = 0; i < nprob; ++i) {
+    const ProbDesc& pd = probs[i];
+    Prob& pr = gp.prob[i];
+    const int64_t Mout = pd.R == 2 ? pd.M / 2 : pd.M;
+    const int64_t Tout = cdiv(Mout, kTile);
+    pr.seg0 = sbase;
+    pr.nseg = pd.nseg;
+    pr.R = pd.R;
+    pr.M = (int32_t)pd.M;
+    pr.Mout = (int32_t)Mout;
+    pr.Tout = (int32_t)Tout;
+    pr.U = plan.U[i];
+    pr.P = plan.P[i];
+    pr.wg0 = wg;
+    pr.flags = pd.flags;
+    pr.eps = pd.eps;
+    pr.y = pd.y;
+    pr.y_stride = pd.y_stride;
+    pr.residual = pd.residual;
+    pr.rms_x = pd.rms_x;
+    pr.rms_K = (int32_t)pd.rms_K;
+    pr.argmax_out = pd.argmax_out;
+    pr.dev_status = pd.dev_status;
+    const bool need = pr.P > 1 || (pd.flags & F_ARGMAX);
+    if (need) {
+      uint8_t* base = static_cast<uint8_t*>(ws) + plan.ws_off[i];
+      pr.tickets = reinterpret_cast<uint32_t*>(base);
+      base += align_up((size_t)(Tout + 1) * 4, 256);
+      pr.am_val = reinterpret_cast<float*>(base);
+      base += align_up((size_t)Tout * 4, 256);
+      pr.am_idx = reinterpret_cast<int32_t*>(base);
+      base += align_up((size_t)Tout * 4, 256);
+      pr.part = reinterpret_cast<float*>(base);
+    }
+    for (int s = 0; s < pd.nseg; ++s) {
+      const SegDesc& sd = pd.seg[s];
+      Seg& sg = gp.seg[sbase + s];
+      const int64_t K = sd.W->K;
+      sg.qs = static_cast<const uint8_t*>(sd.W->qs);
+      sg.d = static_cast<const uint8_t*>(sd.W->d);
+      sg.qs_stride = sd.W->qs_stride;
+      sg.d_stride = sd.W->d_stride;
+      sg.eid = sd.eid;
+      sg.slot = sd.slot;
+      sg.n_mats = (int32_t)sd.W->n_mats;
+      sg.x = sd.x;
+      sg.x_stride = sd.x_stride;
+      sg.K = (int32_t)K;
+      sg.nblk = (int32_t)(K / 32);
+      sg.G = (int32_t)cdiv(K / 32, 4);
+      sg.units = plan.seg_units[sbase + s];
+      sg.alpha_mode = sd.alpha_mode;
+      sg.alpha_ptr = sd.alpha_ptr;
+      sg.gqa_group = sd.gqa_group;
+      sg.gqa_hd = sd.gqa_hd;
+      sg.gqa_off = sd.gqa_off;
+    }
+    sbase += pd.nseg;
+    wg += (int)(Tout * pr.P);
+  }
+  gp.total_wg = wg;
+  if (wg <= 0) return Q8_OK;
+  hipError_t e;
+  switch (N) {
+    case 1: e = launch_n<1>(gp, wg, stream); break;
+    case 2: e = launch_n<2>(gp, wg, stream); break;
+    case 3: e = launch_n<3>(gp, wg, stream); break;
+    case 4: e = launch_n<4>(gp, wg, stream); break;
+    case 5: e = launch_n<5>(gp, wg, stream); break;
+    case 6: e = launch_n<6>(gp, wg, stream); break;
+    case 7: e = launch_n<7>(gp, wg, stream); break;
+    case 8: e = launch_n<8>(gp, wg, stream); break;
+    default: return Q8_EINVAL;
+  }
+  return e == hipSuccess ? Q8_OK : Q8_ELAUNCH;
+}
+
+}  // namespace q8

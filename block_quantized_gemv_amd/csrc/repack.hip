@@ -1,0 +1,76 @@
+// repack.hip -- load-time repack of GGUF Q8_0 blocks into the packed layout.
+//
+// GGUF stores a Q8_0 matrix as an array of 34-byte blocks (binary16 scale,
+// then 32 signed quants; "skuznetsov/cogni-ml" README, cuda_q8_gemv_probe:
+// "raw GGUF Q8_0 block layout").  The 34-byte stride leaves every block only
+// 2-byte aligned, so the decode kernels cannot stream it with 16-byte loads.
+// This kernel moves the bytes (no value changes) into:
+//   qs: per 64-row tile, per 16-weight chunk, the 16 bytes of each of the 64
+//       rows back to back (1 KiB per chunk per tile);
+//   d:  per 64-row tile, per quad of 4 blocks, the 4 scales of each of the 64
+//       rows back to back (512 B per quad per tile).
+// Padding rows and blocks are written as zeros.
+#include "q8_internal.h"
+
+namespace q8 {
+
+__global__ __launch_bounds__(256) void repack_qs_kernel(const uint16_t* __restrict__ aos16,
+                                                        int64_t M, int64_t K,
+                                                        u32x4* __restrict__ qs, int64_t total) {
+  const int64_t nchunk = K / 16;
+  const int64_t nb = K / 32;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lane = idx & 63;
+    const int64_t c = (idx >> 6) % nchunk;
+    const int64_t t = (idx >> 6) / nchunk;
+    const int64_t r = t * 64 + lane;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (r < M) {
+      // quants of block c/2 start 1 uint16 after the block's scale
+      const uint16_t* src = aos16 + (r * nb + c / 2) * 17 + 1 + (c & 1) * 8;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (uint32_t)src[2 * i] | ((uint32_t)src[2 * i + 1] << 16);
+      out = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    qs[idx] = out;
+  }
+}
+
+__global__ __launch_bounds__(256) void repack_d_kernel(const uint16_t* __restrict__ aos16,
+                                                       int64_t M, int64_t K,
+                                                       u32x2* __restrict__ d, int64_t total) {
+  const int64_t nb = K / 32;
+  const int64_t G = (nb + 3) / 4;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lane = idx & 63;
+    const int64_t g = (idx >> 6) % G;
+    const int64_t t = (idx >> 6) / G;
+    const int64_t r = t * 64 + lane;
+    uint32_t bits[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t b = 4 * g + j;
+      bits[j] = (r < M && b < nb) ? aos16[(r * nb + b) * 17] : 0u;
+    }
+    d[idx] = u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+  }
+}
+
+int launch_repack(const void* aos, int64_t M, int64_t K, void* qs, void* d, hipStream_t stream) {
+  const int64_t T = cdiv(M, kTile);
+  const int64_t nq = T * 64 * (K / 16);
+  const int64_t nd = T * 64 * cdiv(K / 32, 4);
+  const auto* a16 = static_cast<const uint16_t*>(aos);
+  auto grid = [](int64_t n) { return (unsigned)(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536); };
+  hipLaunchKernelGGL(repack_qs_kernel, dim3(grid(nq)), dim3(256), 0, stream, a16, M, K,
+                     static_cast<u32x4*>(qs), nq);
+  if (hipGetLastError() != hipSuccess) return Q8_ELAUNCH;
+  hipLaunchKernelGGL(repack_d_kernel, dim3(grid(nd)), dim3(256), 0, stream, a16, M, K,
+                     static_cast<u32x2*>(d), nd);
+  return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
+}
+
+}  // namespace q8

@@ -1,0 +1,149 @@
+// select.hip -- greedy argmax over logits and the MoE top-k router.
+//
+// argmax: the greedy pick of the "augur" README ("Features": greedy generation
+// chooses the highest-probability next token) with the tie rule of "fusedtok
+// 1.3.0" ("API stability": selection ties resolve to the earliest index).
+// Two phases in one launch, like the "two-phase partial-scan/reduce" resident
+// top1 of the cogni-ml README: each workgroup reduces a contiguous slice to
+// (value, index); the last workgroup to arrive (ticket counter) reduces the
+// per-workgroup results and resets the counter.  Exact float comparisons make
+// the result independent of the reduction order.
+//
+// router: top-k of the router logits with renormalised softmax weights (the
+// "#144" Qwen1.5-MoE PR: router + top-k experts), one wave.
+#include <math.h>
+
+#include "q8_internal.h"
+
+namespace q8 {
+
+namespace {
+
+__device__ __forceinline__ void better(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) better(v, i, __shfl_xor(v, o, 64), __shfl_xor(i, o, 64));
+}
+
+constexpr int kArgThreads = 256;
+constexpr int kArgPerThread = 8;
+
+int argmax_groups(int64_t n) {
+  int64_t g = cdiv(n, (int64_t)kArgThreads * kArgPerThread);
+  if (g < 1) g = 1;
+  if (g > 1024) g = 1024;
+  return (int)g;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kArgThreads) void argmax_kernel(const float* __restrict__ v, int n,
+                                                             int32_t* out, uint32_t* ticket,
+                                                             float* wv, int32_t* wi) {
+  __shared__ float sv[kArgThreads / 64];
+  __shared__ int si[kArgThreads / 64];
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // contiguous slice per workgroup, strided by the workgroup's threads
+  const int per = (int)(((int64_t)n + gridDim.x - 1) / gridDim.x);
+  const int lo = blockIdx.x * per;
+  const int hi = min(n, lo + per);
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = lo + threadIdx.x; i < hi; i += kArgThreads) better(bv, bi, v[i], i);
+  wave_best(bv, bi);
+  if (lane == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kArgThreads / 64; ++w) better(bv, bi, sv[w], si[w]);
+    wv[blockIdx.x] = bv;
+    wi[blockIdx.x] = bi;
+    __threadfence();
+    s_last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last || wave != 0) return;
+  __threadfence();
+  bv = -INFINITY;
+  bi = 0x7fffffff;
+  for (int g = lane; g < (int)gridDim.x; g += 64)
+    better(bv, bi, __builtin_nontemporal_load(wv + g), __builtin_nontemporal_load(wi + g));
+  wave_best(bv, bi);
+  if (lane == 0) {
+    *out = bi;
+    *ticket = 0;
+  }
+}
+
+size_t argmax_ws_bytes(int64_t n) {
+  if (n <= 0) return 0;
+  const size_t g = (size_t)argmax_groups(n);
+  return 256 + align_up(g * 4, 256) * 2;
+}
+
+int launch_argmax(const float* v, int64_t n, int32_t* out, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
+  if (n <= 0) return Q8_OK;
+  if (!ws || ws_bytes < argmax_ws_bytes(n)) return Q8_EWORKSPACE;
+  const int g = argmax_groups(n);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  auto* ticket = reinterpret_cast<uint32_t*>(base);
+  auto* wv = reinterpret_cast<float*>(base + 256);
+  auto* wi = reinterpret_cast<int32_t*>(base + 256 + align_up((size_t)g * 4, 256));
+  hipLaunchKernelGGL(argmax_kernel, dim3(g), dim3(kArgThreads), 0, stream, v, (int)n, out, ticket,
+                     wv, wi);
+  return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
+}
+
+// One wave; lane l holds logits l, l+64, ... (E <= 1024).
+__global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ logits, int E, int k,
+                                                   int32_t* ids, float* w) {
+  const int lane = threadIdx.x;
+  float lv[16];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    lv[i] = e < E ? logits[e] : -INFINITY;
+  }
+  float sel_v[Q8_MAX_SLOTS];
+  int sel_i[Q8_MAX_SLOTS];
+  for (int s = 0; s < k; ++s) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !(taken >> i & 1u)) better(bv, bi, lv[i], e);
+    }
+    wave_best(bv, bi);
+    sel_v[s] = bv;
+    sel_i[s] = bi;
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+  }
+  if (lane == 0) {
+    float den = 0.f;
+    for (int s = 0; s < k; ++s) den += expf(sel_v[s] - sel_v[0]);
+    for (int s = 0; s < k; ++s) {
+      ids[s] = sel_i[s];
+      w[s] = expf(sel_v[s] - sel_v[0]) / den;
+    }
+  }
+}
+
+int launch_route(const float* logits, int32_t E, int32_t k, int32_t* ids, float* w,
+                 hipStream_t stream) {
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(64), 0, stream, logits, E, k, ids, w);
+  return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
+}
+
+}  // namespace q8

@@ -1,0 +1,239 @@
+/*
+ * q8gemv.h -- C ABI of the MI355X (gfx950) Q8_0 decode GEMV library.
+ *
+ * What it computes.  Batch-1 (and small-batch) decode matrix-vector products
+ * of a Qwen-style decoder with Q8_0 block-quantised weights and fp32
+ * activations: the qkv, wo, fused gate_up, down and lm_head projections
+ * ("Lumen v0.3.0" release notes, section "Phase 7.E.0", where these matmuls
+ * take 88.6 % of decode time), greedy argmax over the logits ("augur" README,
+ * "Features": greedy generation), and the routed-expert FFN of a Qwen-MoE
+ * layer with all selected expert slots in one launch ("Add Qwen1.5-MoE Q8_0
+ * CPU and single-token TornadoVM GPU inference - #144", the routed-expert
+ * fusion comments: slot index folded into the work-group id for gate/up, the
+ * down projection looping over slots).
+ *
+ * Q8_0 block (GGUF, "raw GGUF Q8_0 block layout" on the cogni-ml README,
+ * cuda_q8_gemv_probe): 32 consecutive weights of one row share one binary16
+ * scale d; each weight is d * q with q a signed 8-bit integer.  In GGUF files
+ * a block is 34 bytes: d (little-endian) then the 32 quants.
+ *
+ * Arithmetic: quants and scales are converted exactly to fp32, products and
+ * sums are fp32 FMAs, activations stay fp32 (no requantisation).  Results
+ * agree with the exact value within 2e-5 * sum_k |w_k x_k| + 1e-6 per output.
+ * For a fixed (M, K, N) and device the summation order is fixed: repeated
+ * calls give bitwise identical results.
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are device memory of the current HIP device (hipMalloc
+ *    or torch CUDA tensors).  Host pointers passed where device memory is
+ *    required are rejected with Q8_EHOSTPTR before any launch.
+ *  - The library never allocates, frees or synchronises inside a call; all
+ *    work is enqueued on `stream` (a hipStream_t; NULL = the default stream),
+ *    so calls are stream-ordered with other work and may be captured into a
+ *    HIP graph.
+ *  - The caller owns every buffer.  Outputs are written only by the kernels,
+ *    after the call returns Q8_OK (i.e. when the stream reaches them).
+ *  - Return value: Q8_OK (0) or a negative Q8_E* code; nothing is enqueued
+ *    when a call returns an error.  q8_0_strerror() names the code.
+ *  - Empty problems (M == 0, or n == 0 for argmax) return Q8_OK and enqueue
+ *    nothing.
+ *  - Workspace: calls that take one need workspace_bytes >= the value from
+ *    q8_0_workspace_bytes() for the same op and shape (0 means none is
+ *    needed and the pointer may be NULL).  The workspace must be zero-filled
+ *    once before its first use; every call leaves its counters at zero again.
+ *    Calls that may run concurrently (different streams) need distinct
+ *    workspaces.
+ */
+#ifndef Q8GEMV_H
+#define Q8GEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define Q8_OK 0
+#define Q8_EINVAL (-1)     /* bad scalar argument: shape, count, flag combination */
+#define Q8_ENULL (-2)      /* a required pointer is NULL */
+#define Q8_EALIGN (-3)     /* a pointer lacks the alignment stated below */
+#define Q8_EHOSTPTR (-4)   /* a pointer that must be device memory is not */
+#define Q8_EWORKSPACE (-5) /* workspace missing or smaller than required */
+#define Q8_ELAUNCH (-6)    /* the HIP runtime reported an error */
+
+/* ---- limits -------------------------------------------------------------- */
+#define Q8_QK 32            /* weights per block */
+#define Q8_TILE_ROWS 64     /* rows per packed tile (one row per wave64 lane) */
+#define Q8_MAX_N 8          /* activation columns per call */
+#define Q8_MAX_SLOTS 8      /* routed-expert slots per MoE call */
+#define Q8_MAX_K (1 << 20)  /* largest K accepted */
+
+/* ---- packed weight layout (output of q8_0_repack) -------------------------
+ * For an M x K matrix (K % 32 == 0), T = ceil(M / 64) tiles of 64 rows,
+ * nb = K / 32 blocks per row, G = ceil(nb / 4) scale quads per row.
+ *  qs: T * 64 * K bytes.  The 16 quants k = 16c .. 16c+15 of row r sit at byte
+ *      ((t * (K/16) + c) * 64 + i) * 16, t = r / 64, i = r % 64: one 16-byte
+ *      chunk per row, 64 rows of one chunk contiguous (1 KiB).
+ *  d:  T * G * 64 * 8 bytes.  The scale of block b of row r sits at uint16
+ *      index ((t * G + b / 4) * 64 + i) * 4 + b % 4 (binary16 bits).
+ *  Rows M .. 64T-1 and blocks nb .. 4G-1 are zero.  Alignment: qs 16 bytes,
+ *  d 8 bytes.  A stack of E matrices (MoE experts) is E packed matrices at a
+ *  fixed byte stride. */
+typedef struct {
+  const void* qs;    /* device, packed quants of matrix 0 */
+  const void* d;     /* device, packed scales of matrix 0 */
+  int64_t M, K;      /* shape of one matrix */
+  int64_t n_mats;    /* stacked matrices (experts); 1 for a dense matrix */
+  int64_t qs_stride; /* bytes from one matrix's qs to the next (>= packed qs size) */
+  int64_t d_stride;  /* bytes from one matrix's d to the next */
+} q8_0_weights;
+
+/* Bytes of the packed quants and scales of one M x K matrix.
+ * Errors: Q8_EINVAL (M < 0, K <= 0, K % 32, K > Q8_MAX_K), Q8_ENULL. */
+int q8_0_packed_size(int64_t M, int64_t K, size_t* qs_bytes, size_t* d_bytes);
+
+/* Load-time repack of GGUF Q8_0 blocks into the packed layout above (no value
+ * changes; byte moves only).
+ *  aos: device, M * K/32 blocks of 34 bytes, row-major, 2-byte aligned.
+ *  qs, d: device outputs of q8_0_packed_size() bytes (16- and 8-byte aligned);
+ *  every byte, padding included, is written.
+ * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_ELAUNCH. */
+int q8_0_repack(const void* aos, int64_t M, int64_t K, void* qs, void* d, void* stream);
+
+/* ---- GEMV ------------------------------------------------------------------
+ * y[n][r] = sum_k w[r][k] * x[n][k],  n < N, r < M.
+ *  W: host pointer to a descriptor of packed device weights (n_mats == 1);
+ *     W->M and W->K must equal M and K.
+ *  x: device fp32 [N][K], 4-byte aligned.  y: device fp32 [N][M].
+ *  1 <= N <= Q8_MAX_N.  x and y must not overlap.
+ * The N = 1 case is the decode projection; N in {2,4,8} is a small verify
+ * chunk ("skuznetsov/cogni-ml" README, "Qwen 3.5 Native Metal":
+ * target-verifier chunks), weights read once for all N columns.
+ * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_EWORKSPACE,
+ * Q8_ELAUNCH. */
+int q8_0_gemv(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- GEMV with fused decode-chain glue (N = 1) ----------------------------
+ * The non-matmul steps between the projections of one Qwen2-style decoder
+ * layer ("augur" README, "Features": RMSNorm before attention, before the MLP
+ * and after the last layer; grouped-query attention; SwiGLU MLP; decoder
+ * block order norm, attention, residual, norm, MLP, residual), folded into
+ * the GEMV so the chain needs no extra launches:
+ *  prologue Q8_PRO_RMSNORM: the GEMV input is a = x / sqrt(mean(x^2) + eps)
+ *      (unit norm weight) over the K entries of x.
+ *  prologue Q8_PRO_GQA: the GEMV input is the position-0 attention output
+ *      a[h*hd + j] = x[gqa_offset + (h / (n_heads/n_kv_heads)) * hd + j],
+ *      K == n_heads * hd, hd % 32 == 0 (with one key the softmax weight is 1,
+ *      so each query head returns its key/value head's value vector).
+ *  epilogue Q8_EPI_SWIGLU: M even, (M/2) % 64 == 0; rows 0..M/2-1 are gate,
+ *      M/2..M-1 up; y gets M/2 values silu(g) * u, silu(z) = z/(1+e^-z).
+ *  epilogue Q8_EPI_RESIDUAL: y[r] = residual[r] + (W a)[r]; residual may be y
+ *      itself (in-place h += W a).
+ *  epilogue Q8_EPI_ARGMAX: also writes to *argmax_out the lowest index of the
+ *      largest y value (fp32 comparisons, "fusedtok 1.3.0", "API stability":
+ *      ties resolve to the earliest index).
+ *  SWIGLU excludes RESIDUAL and ARGMAX.
+ * Errors as q8_0_gemv. */
+#define Q8_PRO_NONE 0
+#define Q8_PRO_RMSNORM 1
+#define Q8_PRO_GQA 2
+#define Q8_EPI_RESIDUAL 1
+#define Q8_EPI_SWIGLU 2
+#define Q8_EPI_ARGMAX 4
+typedef struct {
+  int32_t prologue;       /* Q8_PRO_* */
+  int32_t epilogue;       /* OR of Q8_EPI_* */
+  float eps;              /* RMSNORM epsilon */
+  int32_t n_heads;        /* GQA */
+  int32_t n_kv_heads;     /* GQA */
+  int32_t head_dim;       /* GQA */
+  int64_t gqa_offset;     /* GQA: index in x of the first value-head element */
+  const float* residual;  /* RESIDUAL: device fp32 [M] */
+  int32_t* argmax_out;    /* ARGMAX: device int32 [1] */
+} q8_0_fusion;
+
+int q8_0_gemv_fused(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,
+                    const q8_0_fusion* fusion, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* ---- argmax ------------------------------------------------------------------
+ * *out_idx = min{ i : v[i] == max_j v[j] } over fp32 v[0..n) (device), as
+ * int32 (device).  Inputs are finite (NaN is outside the contract).
+ * Errors: Q8_EINVAL (n < 0 or n >= 2^31), Q8_ENULL, Q8_EHOSTPTR,
+ * Q8_EWORKSPACE, Q8_ELAUNCH. */
+int q8_0_argmax(const float* v, int64_t n, int32_t* out_idx, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* ---- MoE router --------------------------------------------------------------
+ * Top-k of E fp32 router logits (device): expert_ids[s] (device int32 [k]) are
+ * the k largest logits in descending order, ties to the lower expert index;
+ * slot_weights[s] (device fp32 [k]) = exp(l_s - l_max) / sum over the chosen
+ * t of exp(l_t - l_max), i.e. softmax over all experts renormalised over the
+ * chosen ones (#144 PR: router + top-k experts).  Selection compares the
+ * logits themselves.  1 <= k <= min(E, Q8_MAX_SLOTS), E <= 1024.
+ * Errors: Q8_EINVAL, Q8_ENULL, Q8_EHOSTPTR, Q8_ELAUNCH. */
+int q8_0_route_topk(const float* logits, int32_t E, int32_t k, int32_t* expert_ids,
+                    float* slot_weights, void* stream);
+
+/* ---- MoE expert GEMV, all slots in one launch -------------------------------
+ * W_experts: stacked packed matrices (n_mats experts, M x K each).
+ * expert_ids: device int32 [n_slots]; read on the device, so the call needs no
+ *   host round trip.  An id outside [0, n_mats) makes that slot contribute
+ *   zeros and sets bit 0 of *dev_status (if dev_status != NULL); no memory is
+ *   read through it.
+ * mode Q8_MOE_SCATTER (gate_up of every slot, one launch):
+ *   y[s][r] = (W_e[s] x)[r], x device fp32 [K], y [n_slots][M]; if `shared`
+ *   is given (M_sh x K), its product follows at y + n_slots*M.
+ *   With Q8_MOE_SWIGLU each matrix's rows are gate then up halves and y gets
+ *   silu(g)*u instead: [n_slots][M/2] then [M_sh/2] ((M/2) % 64 == 0).
+ * mode Q8_MOE_COMBINE (down of every slot plus the shared expert, one launch):
+ *   y[r] = sum_s slot_weights[s] * (W_e[s] x_s)[r]
+ *          + sigmoid(*shared_gate) * (shared x_sh)[r],
+ *   x = [n_slots][K] then [shared->K], y [M]; folded per output row in slot
+ *   order, then the shared expert (#144 PR: each slot reduced with the same
+ *   tree and folded in the same order).  shared may be NULL (no shared term).
+ *   slot_weights: device fp32 [n_slots]; shared_gate: device fp32 scalar.
+ * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_EWORKSPACE,
+ * Q8_ELAUNCH. */
+#define Q8_MOE_SCATTER 1
+#define Q8_MOE_COMBINE 2
+#define Q8_MOE_SWIGLU 4
+int q8_0_moe_gemv(const q8_0_weights* W_experts, const int32_t* expert_ids,
+                  const float* slot_weights, const float* x, float* y, int64_t M, int64_t K,
+                  int32_t n_slots, int32_t mode, const q8_0_weights* shared,
+                  const float* shared_gate, int32_t* dev_status, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* ---- workspace sizes --------------------------------------------------------
+ * op Q8_OP_GEMV: (M, K, N) of q8_0_gemv.
+ * op Q8_OP_GEMV_FUSED: (M, K, epilogue flags in N) of q8_0_gemv_fused.
+ * op Q8_OP_ARGMAX: (n, 0, 0).
+ * op Q8_OP_MOE_SCATTER / Q8_OP_MOE_COMBINE: (M, K, n_slots) with the
+ *   shared expert's shape in (M2, K2) (0, 0 for none) and mode flags in flags.
+ * Returns the byte count, or 0 when none is needed or the shape is invalid. */
+#define Q8_OP_GEMV 1
+#define Q8_OP_GEMV_FUSED 2
+#define Q8_OP_ARGMAX 3
+#define Q8_OP_MOE_SCATTER 4
+#define Q8_OP_MOE_COMBINE 5
+size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t M2, int64_t K2,
+                            int32_t flags);
+
+/* Launch plan the library picks for a GEMV of this shape (for reports):
+ * out[0] = workgroups, out[1] = waves per workgroup, out[2] = K-splits per
+ * 64-row tile, out[3] = workgroups per tile.  Returns Q8_OK or Q8_EINVAL. */
+int q8_0_gemv_plan(int64_t M, int64_t K, int64_t N, int32_t epilogue, int32_t out[4]);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* q8_0_strerror(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int q8_0_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q8GEMV_H */

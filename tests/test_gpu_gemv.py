@@ -1,0 +1,145 @@
+"""GPU parity of the repack and the Q8_0 GEMV (N = 1..8) against the fp64
+oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_gemv_amd as q
+import oracle
+import q8tol
+import workloads as W
+from gpu_util import DEV, expected_packed, host, pack, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (64, 64), (65, 96), (130, 160), (200, 896),
+                                 (333, 1408), (64, 4864)])
+def test_repack_layout_bit_exact(M, K):
+    m = W.draw_matrix(W.rng(10, M, K), M, K)
+    p = pack(m)
+    eq, ed = expected_packed(m.qs, m.d)
+    assert np.array_equal(host(p.qs), eq)
+    assert np.array_equal(host(p.d), ed)
+
+
+SHAPES = [(1, 32), (7, 64), (64, 896), (65, 96), (130, 160), (200, 224), (896, 896),
+          (1152, 896), (300, 4864), (333, 1408), (129, 2048), (64, 5632), (40, 12288)]
+
+
+@pytest.mark.parametrize("M,K", SHAPES)
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 8])
+def test_gemv_matches_oracle(M, K, N):
+    g = W.rng(20, M * 7 + N, K)
+    m = W.draw_matrix(g, M, K)
+    x = W.draw_x(g, N, K)
+    p = pack(m)
+    y = q.q8_0_gemv(p, to_dev(x))
+    yr, S = oracle.gemv(m.aos(), x)
+    q8tol.check(host(y), yr, S, f"gemv {M}x{K} N={N}")
+
+
+def test_constant_quants_exact():
+    """All quants q, scales d = 2^e, x in {-1, 0, 1}: every partial sum is an
+    exact small integer times d, so the GPU result equals d*q*sum(x) exactly."""
+    for (M, K) in [(64, 896), (130, 4864), (896, 896), (65, 12288)]:
+        g = np.random.default_rng(M + K)
+        x = g.integers(-1, 2, size=(2, K)).astype(np.float32)
+        for qv in (-128, 127, -1, 0):
+            for dbits in (0x3C00, 0x2000, 0x0001, 0x4400):
+                d = np.array([dbits], dtype=np.uint16).view(np.float16)[0]
+                m = W.Q8Matrix(np.full((M, K), qv, np.int8), np.full((M, K // 32), d))
+                y = host(q.q8_0_gemv(pack(m), to_dev(x)))
+                want = float(d) * qv * x.astype(np.float64).sum(axis=1)
+                assert np.array_equal(y.astype(np.float64), np.repeat(want[:, None], M, 1)), \
+                    (M, K, qv, dbits)
+
+
+def test_one_hot_exact():
+    """x = e_k selects d[r, k/32] * q[r, k], exact in fp32 (11 x 8 bits)."""
+    M, K = 200, 1408
+    m = W.draw_matrix(W.rng(21), M, K)
+    # include subnormal, zero, negative and extreme scales
+    d = m.d.view(np.uint16).copy()
+    d[0, :] = 0x0001
+    d[1, :] = 0x8000
+    d[2, :] = 0xFBFF
+    d[3, :] = 0x03FF
+    m = W.Q8Matrix(m.qs, d.view(np.float16))
+    m.qs[4, :] = -128
+    p = pack(m)
+    ks = [0, 1, 31, 32, 33, 127, 128, 700, K - 33, K - 1]
+    x = np.zeros((len(ks[:8]), K), dtype=np.float32)
+    for i, k in enumerate(ks[:8]):
+        x[i, k] = 1.0
+    y = host(q.q8_0_gemv(p, to_dev(x)))
+    for i, k in enumerate(ks[:8]):
+        want = (m.d[:, k // 32].astype(np.float64) * m.qs[:, k].astype(np.float64))
+        assert np.array_equal(y[i].astype(np.float64), want), k
+    x1 = np.zeros((1, K), dtype=np.float32)
+    x1[0, K - 1] = -2.0
+    y = host(q.q8_0_gemv(p, to_dev(x1)))[0]
+    assert np.array_equal(y.astype(np.float64),
+                          -2.0 * m.d[:, -1].astype(np.float64) * m.qs[:, -1].astype(np.float64))
+
+
+def test_edge_scales_and_quants_within_tolerance():
+    M, K = 256, 896
+    g = W.rng(22)
+    m = W.draw_matrix(g, M, K)
+    d = m.d.view(np.uint16).copy()
+    d[:64, ::3] = 0x0001       # smallest subnormal
+    d[64:128, ::2] = 0x8000    # negative zero
+    d[128:160, :] = 0x7BFF     # 65504
+    d[160:192, :] |= 0x8000    # negative scales
+    qs = m.qs.copy()
+    qs[192:, ::5] = -128
+    qs[200:210, :] = 0         # all-zero rows: tolerance is the 1e-6 floor
+    m = W.Q8Matrix(qs, d.view(np.float16))
+    x = W.draw_x(g, 3, K)
+    y = host(q.q8_0_gemv(pack(m), to_dev(x)))
+    yr, S = oracle.gemv(m.aos(), x)
+    q8tol.check(y, yr, S, "edge scales")
+    assert np.all(y[:, 200:210] == 0)
+
+
+@pytest.mark.parametrize("M,K,N", [(896, 4864, 1), (896, 896, 1), (4096, 12288, 2),
+                                   (9728, 896, 1), (1152, 896, 8)])
+def test_repeated_calls_bitwise_identical(M, K, N):
+    g = W.rng(23, M, K)
+    m = W.draw_matrix(g, M, K)
+    p = pack(m)
+    x = to_dev(W.draw_x(g, N, K))
+    y0 = q.q8_0_gemv(p, x).clone()
+    for _ in range(20):
+        y = q.q8_0_gemv(p, x)
+        assert torch.equal(y, y0)
+
+
+def test_rejects_host_and_misaligned_pointers():
+    m = W.draw_matrix(W.rng(24), 64, 64)
+    p = pack(m)
+    x_host = torch.zeros(64, dtype=torch.float32)
+    y = torch.empty(64, dtype=torch.float32, device=DEV)
+    L = q.lib()
+    import ctypes
+    rc = L.q8_0_gemv(ctypes.byref(p.desc), x_host.data_ptr(), y.data_ptr(), 64, 64, 1, None, 0,
+                     None)
+    assert rc == q.Q8_EHOSTPTR
+    xb = torch.zeros(65, dtype=torch.float32, device=DEV)
+    raw = xb.data_ptr() + 2  # not 4-byte aligned
+    rc = L.q8_0_gemv(ctypes.byref(p.desc), raw, y.data_ptr(), 64, 64, 1, None, 0, None)
+    assert rc == q.Q8_EALIGN
+    # workspace too small for a split-K plan
+    m2 = W.draw_matrix(W.rng(25), 896, 4864)
+    p2 = pack(m2)
+    x2 = torch.zeros(4864, dtype=torch.float32, device=DEV)
+    y2 = torch.empty(896, dtype=torch.float32, device=DEV)
+    need = q.q8_0_workspace_bytes(q.Q8_OP_GEMV, 896, 4864, 1)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    rc = L.q8_0_gemv(ctypes.byref(p2.desc), x2.data_ptr(), y2.data_ptr(), 896, 4864, 1,
+                     ws.data_ptr(), need - 1, None)
+    assert rc == q.Q8_EWORKSPACE
+    rc = L.q8_0_gemv(ctypes.byref(p2.desc), x2.data_ptr(), y2.data_ptr(), 896, 4864, 1,
+                     None, 0, None)
+    assert rc == q.Q8_EWORKSPACE
