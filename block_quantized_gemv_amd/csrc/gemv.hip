@@ -20,8 +20,14 @@
 //  * A tile's K range is split into "units", one per wave; units of one tile
 //    are folded in a fixed order (bitwise reproducible).  When a tile's units
 //    span several workgroups, each writes its partials to the workspace and
-//    the last-arriving workgroup (ticket counter with release/acquire fences)
-//    folds them in unit order and resets the ticket for the next call.
+//    the last-arriving workgroup (ticket counter) folds them in unit order and
+//    resets the ticket for the next call.  The L2 of each of the 8 XCDs is not
+//    coherent with the others, and an agent-scope fence writes back and
+//    invalidates a whole L2; issued by every workgroup that costs more than
+//    the GEMV itself.  So everything exchanged between workgroups is written
+//    and read with device-scope atomic stores/loads (coherent at the memory
+//    side), each wave waits for its stores to complete (vmcnt 0) before the
+//    workgroup barrier, and only then is the ticket incremented.
 //  * No matrix cores: at N <= 8 the product is HBM-bound, not a dense
 //    contraction worth MFMA tiles.
 #include <math.h>
@@ -164,6 +170,38 @@ __device__ __forceinline__ float seg_alpha(const Seg& s) {
   return 1.0f;
 }
 
+// val[ts][n] = sum over segments (in order) of alpha_seg * (sum of the
+// segment's unit partials, in unit order), for each tile of a pair.
+template <int N, typename Get>
+__device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, int us, Get get,
+                                           float (&val)[2][N]) {
+#pragma unroll
+  for (int ts = 0; ts < 2; ++ts) {
+    if (ts >= pr.R) break;
+#pragma unroll
+    for (int n = 0; n < N; ++n) val[ts][n] = 0.f;
+    int uu = ts * us;
+    for (int si = pr.seg0; si < pr.seg0 + pr.nseg; ++si) {
+      const Seg& s = p.seg[si];
+      float ssum[N];
+#pragma unroll
+      for (int n = 0; n < N; ++n) ssum[n] = 0.f;
+      for (int i = 0; i < s.units; ++i, ++uu) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) ssum[n] += get(uu, n);
+      }
+      if (s.alpha_mode == A_ONE) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) val[ts][n] += ssum[n];
+      } else {
+        const float a = seg_alpha(s);
+#pragma unroll
+        for (int n = 0; n < N; ++n) val[ts][n] = fmaf(a, ssum[n], val[ts][n]);
+      }
+    }
+  }
+}
+
 template <int N>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvParams p) {
   __shared__ float lds_part[kWaves][N][64];
@@ -225,58 +263,28 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvParams p) {
   }
 
   // ---- fold the units of this output tile in unit order -------------------
-  const float* part;
-  int pstride;  // floats between units
+  float val[2][N];
   if (pr.P == 1) {
 #pragma unroll
     for (int n = 0; n < N; ++n) lds_part[wave][n][lane] = acc[n];
     __syncthreads();
     if (wave != 0) return;
-    part = &lds_part[0][0][0];
-    pstride = N * 64;
+    fold_units<N>(p, pr, us, [&](int uu, int n) { return lds_part[uu][n][lane]; }, val);
   } else {
     float* gp = pr.part + (int64_t)ot * pr.U * N * 64;
     if (u < pr.U) {
 #pragma unroll
-      for (int n = 0; n < N; ++n) gp[(u * N + n) * 64 + lane] = acc[n];
+      for (int n = 0; n < N; ++n) st_dev(gp + (u * N + n) * 64 + lane, acc[n]);
     }
-    __threadfence();
+    wait_stores();
     __syncthreads();
-    if (threadIdx.x == 0) s_last = atomicAdd(&pr.tickets[ot], 1u) == (unsigned)(pr.P - 1);
+    if (threadIdx.x == 0) s_last = ticket_add(&pr.tile_tickets[ot]) == (unsigned)(pr.P - 1);
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
     if (wave != 0) return;
-    if (lane == 0) pr.tickets[ot] = 0;  // ready for the next call
-    part = gp;
-    pstride = N * 64;
-  }
-
-  float val[2][N];
-#pragma unroll
-  for (int ts = 0; ts < 2; ++ts) {
-    if (ts >= pr.R) break;
-#pragma unroll
-    for (int n = 0; n < N; ++n) val[ts][n] = 0.f;
-    int uu = ts * us;
-    for (int si = pr.seg0; si < pr.seg0 + pr.nseg; ++si) {
-      const Seg& s = p.seg[si];
-      float ssum[N];
-#pragma unroll
-      for (int n = 0; n < N; ++n) ssum[n] = 0.f;
-      for (int i = 0; i < s.units; ++i, ++uu) {
-#pragma unroll
-        for (int n = 0; n < N; ++n) ssum[n] += part[uu * pstride + n * 64 + lane];
-      }
-      if (s.alpha_mode == A_ONE) {
-#pragma unroll
-        for (int n = 0; n < N; ++n) val[ts][n] += ssum[n];
-      } else {
-        const float a = seg_alpha(s);
-#pragma unroll
-        for (int n = 0; n < N; ++n) val[ts][n] = fmaf(a, ssum[n], val[ts][n]);
-      }
-    }
+    if (lane == 0) st_dev(&pr.tile_tickets[ot], 0u);  // ready for the next call
+    fold_units<N>(p, pr, us, [&](int uu, int n) { return ld_dev(gp + (uu * N + n) * 64 + lane); },
+                  val);
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -320,20 +328,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvParams p) {
     int mi = row;
     wave_argmax(mv, mi);
     if (lane == 0) {
-      pr.am_val[ot] = mv;
-      pr.am_idx[ot] = mi;
+      st_dev(pr.am_val + ot, mv);
+      st_dev(pr.am_idx + ot, mi);
     }
-    __threadfence();
+    wait_stores();
     int last = 0;
-    if (lane == 0) last = atomicAdd(&pr.tickets[pr.Tout], 1u) == (unsigned)(pr.Tout - 1);
+    if (lane == 0) last = ticket_add(pr.am_ticket) == (unsigned)(pr.Tout - 1);
     last = __builtin_amdgcn_readfirstlane(last);
     if (!last) return;
-    __threadfence();
     float bv = -INFINITY;
     int bi = 0x7fffffff;
     for (int i = lane; i < pr.Tout; i += 64) {
-      const float tv = __builtin_nontemporal_load(pr.am_val + i);
-      const int ti = __builtin_nontemporal_load(pr.am_idx + i);
+      const float tv = ld_dev(pr.am_val + i);
+      const int ti = ld_dev(pr.am_idx + i);
       if (tv > bv || (tv == bv && ti < bi)) {
         bv = tv;
         bi = ti;
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvParams p) {
     wave_argmax(bv, bi);
     if (lane == 0) {
       *pr.argmax_out = bi;
-      pr.tickets[pr.Tout] = 0;
+      st_dev(pr.am_ticket, 0u);
     }
   }
 }
@@ -386,7 +393,8 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
   }
   if (segc > kMaxSeg || nprob > kMaxProb || total_tout <= 0) return Q8_EINVAL;
   const int64_t want_u = cdiv(target_waves(), total_tout);
-  size_t ws = 0;
+  int64_t cnt = 0;
+  size_t data = 0;
   int wg = 0;
   int sbase = 0;
   for (int i = 0; i < nprob; ++i) {
@@ -461,21 +469,45 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
       usum += su[s];
     }
     U = usum * pd.R;
-    const int64_t P = cdiv(U, kWaves);
+    // per-tile arrival counters are needed when a tile spans workgroups; keep
+    // them within the fixed counter region
+    int64_t P = cdiv(U, kWaves);
+    const int64_t cnt_need = (P > 1 ? Tout : 0) + ((pd.flags & F_ARGMAX) ? 1 : 0);
+    if (P > 1 && cnt + cnt_need > kMaxCounters) {
+      // too many tiles to split across workgroups: one workgroup per tile
+      if ((int64_t)pd.nseg * pd.R > kWaves) return Q8_EINVAL;
+      int64_t left2 = kWaves / pd.R;
+      for (int s = 0; s < pd.nseg; ++s) {
+        su[s] = 1;
+        --left2;
+      }
+      for (int s = 0, guard = 0; left2 > 0 && guard < 64 * kMaxSeg; s = (s + 1) % pd.nseg, ++guard) {
+        if (su[s] < pd.seg[s].W->K / 32) {
+          ++su[s];
+          --left2;
+        }
+      }
+      usum = 0;
+      for (int s = 0; s < pd.nseg; ++s) {
+        plan->seg_units[sbase + s] = (int32_t)su[s];
+        usum += su[s];
+      }
+      U = usum * pd.R;
+      P = 1;
+    }
+    const int64_t cnt_use = (P > 1 ? Tout : 0) + ((pd.flags & F_ARGMAX) ? 1 : 0);
+    if (cnt + cnt_use > kMaxCounters) return Q8_EINVAL;
     plan->U[i] = (int32_t)U;
     plan->P[i] = (int32_t)P;
-    // workspace: tickets, argmax partials, unit partials
-    const bool need = P > 1 || (pd.flags & F_ARGMAX);
-    plan->ws_off[i] = ws;
-    if (need) {
-      ws += align_up((size_t)(Tout + 1) * 4, 256);
-      ws += align_up((size_t)Tout * 4, 256) * 2;
-      if (P > 1) ws += align_up((size_t)Tout * U * N * 64 * 4, 256);
-    }
+    plan->cnt_off[i] = (int32_t)cnt;
+    plan->data_off[i] = data;
+    cnt += cnt_use;
+    if (pd.flags & F_ARGMAX) data += align_up((size_t)Tout * 4, 256) * 2;
+    if (P > 1) data += align_up((size_t)Tout * U * N * 64 * 4, 256);
     wg += (int)(Tout * P);
     sbase += pd.nseg;
   }
-  plan->ws_bytes = ws;
+  plan->ws_bytes = (cnt > 0 || data > 0) ? kCounterBytes + data : 0;
   plan->total_wg = wg;
   return Q8_OK;
 }
@@ -520,16 +552,21 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
     pr.rms_K = (int32_t)pd.rms_K;
     pr.argmax_out = pd.argmax_out;
     pr.dev_status = pd.dev_status;
-    const bool need = pr.P > 1 || (pd.flags & F_ARGMAX);
-    if (need) {
-      uint8_t* base = static_cast<uint8_t*>(ws) + plan.ws_off[i];
-      pr.tickets = reinterpret_cast<uint32_t*>(base);
-      base += align_up((size_t)(Tout + 1) * 4, 256);
-      pr.am_val = reinterpret_cast<float*>(base);
-      base += align_up((size_t)Tout * 4, 256);
-      pr.am_idx = reinterpret_cast<int32_t*>(base);
-      base += align_up((size_t)Tout * 4, 256);
-      pr.part = reinterpret_cast<float*>(base);
+    if (plan.ws_bytes > 0) {
+      uint32_t* cnt = static_cast<uint32_t*>(ws) + plan.cnt_off[i];
+      uint8_t* base = static_cast<uint8_t*>(ws) + kCounterBytes + plan.data_off[i];
+      if (pr.P > 1) {
+        pr.tile_tickets = cnt;
+        cnt += Tout;
+      }
+      if (pd.flags & F_ARGMAX) {
+        pr.am_ticket = cnt;
+        pr.am_val = reinterpret_cast<float*>(base);
+        base += align_up((size_t)Tout * 4, 256);
+        pr.am_idx = reinterpret_cast<int32_t*>(base);
+        base += align_up((size_t)Tout * 4, 256);
+      }
+      if (pr.P > 1) pr.part = reinterpret_cast<float*>(base);
     }
     for (int s = 0; s < pd.nseg; ++s) {
       const SegDesc& sd = pd.seg[s];

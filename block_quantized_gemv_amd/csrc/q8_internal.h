@@ -15,6 +15,12 @@ constexpr int kWaves = 4;            // waves per GEMV workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSeg = 9;           // K-segments over all problems of one launch
 constexpr int kMaxProb = 9;          // problems (independent GEMVs) per launch
+// Every workspace starts with a fixed region of 32-bit counters that each
+// call leaves at zero; data (partials) always lives after it, so calls of
+// different shapes can share one workspace without a counter ever landing on
+// another call's data.
+constexpr size_t kCounterBytes = 65536;
+constexpr int kMaxCounters = (int)(kCounterBytes / 4);
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -66,7 +72,8 @@ struct Prob {
   const float* rms_x;    // vector whose RMS scales the output
   int32_t rms_K;
   int32_t* argmax_out;
-  uint32_t* tickets;     // [Tout + 1]; the last one counts argmax partials
+  uint32_t* tile_tickets;  // [Tout] arrivals per output tile (P > 1)
+  uint32_t* am_ticket;   // arrivals of argmax partials (F_ARGMAX)
   float* am_val;         // [Tout]
   int32_t* am_idx;       // [Tout]
   float* part;           // [Tout][U][N][64] partial sums when P > 1
@@ -114,8 +121,9 @@ struct Plan {
   int32_t U[kMaxProb];
   int32_t P[kMaxProb];
   int32_t seg_units[kMaxSeg];
-  size_t ws_off[kMaxProb];   // start of each problem's workspace region
-  size_t ws_bytes;           // total
+  int32_t cnt_off[kMaxProb];   // first counter of each problem
+  size_t data_off[kMaxProb];   // byte offset of each problem's data (after the counters)
+  size_t ws_bytes;             // total (0: no workspace needed)
   int32_t total_wg;
 };
 
@@ -130,6 +138,28 @@ int launch_argmax(const float* v, int64_t n, int32_t* out, void* ws, size_t ws_b
 int launch_route(const float* logits, int32_t E, int32_t k, int32_t* ids, float* w,
                  hipStream_t stream);
 int launch_repack(const void* aos, int64_t M, int64_t K, void* qs, void* d, hipStream_t stream);
+
+// ---- data exchanged between workgroups of one launch ------------------------
+// The 8 XCDs of an MI355X each have their own L2, not coherent with the
+// others; an agent-scope fence writes back and invalidates a whole L2, which
+// is far too costly per workgroup.  Data handed from one workgroup to another
+// is therefore written and read with device-scope atomic stores/loads
+// (coherent at the memory side), the writer waits for its stores to complete
+// (vmcnt 0) before it signals, and the signal is a device-scope atomic add.
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory store this wave issued has completed (vmcnt(0);
+// expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ unsigned ticket_add(uint32_t* t) {
+  return __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

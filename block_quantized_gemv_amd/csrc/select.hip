@@ -65,29 +65,27 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const float* __rest
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int w = 1; w < kArgThreads / 64; ++w) better(bv, bi, sv[w], si[w]);
-    wv[blockIdx.x] = bv;
-    wi[blockIdx.x] = bi;
-    __threadfence();
-    s_last = atomicAdd(ticket, 1u) == gridDim.x - 1;
+    st_dev(wv + blockIdx.x, bv);
+    st_dev(wi + blockIdx.x, bi);
+    wait_stores();
+    s_last = ticket_add(ticket) == gridDim.x - 1;
   }
   __syncthreads();
   if (!s_last || wave != 0) return;
-  __threadfence();
   bv = -INFINITY;
   bi = 0x7fffffff;
-  for (int g = lane; g < (int)gridDim.x; g += 64)
-    better(bv, bi, __builtin_nontemporal_load(wv + g), __builtin_nontemporal_load(wi + g));
+  for (int g = lane; g < (int)gridDim.x; g += 64) better(bv, bi, ld_dev(wv + g), ld_dev(wi + g));
   wave_best(bv, bi);
   if (lane == 0) {
     *out = bi;
-    *ticket = 0;
+    st_dev(ticket, 0u);
   }
 }
 
 size_t argmax_ws_bytes(int64_t n) {
   if (n <= 0) return 0;
   const size_t g = (size_t)argmax_groups(n);
-  return 256 + align_up(g * 4, 256) * 2;
+  return kCounterBytes + align_up(g * 4, 256) * 2;
 }
 
 int launch_argmax(const float* v, int64_t n, int32_t* out, void* ws, size_t ws_bytes,
@@ -96,9 +94,9 @@ int launch_argmax(const float* v, int64_t n, int32_t* out, void* ws, size_t ws_b
   if (!ws || ws_bytes < argmax_ws_bytes(n)) return Q8_EWORKSPACE;
   const int g = argmax_groups(n);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  auto* ticket = reinterpret_cast<uint32_t*>(base);
-  auto* wv = reinterpret_cast<float*>(base + 256);
-  auto* wi = reinterpret_cast<int32_t*>(base + 256 + align_up((size_t)g * 4, 256));
+  auto* ticket = reinterpret_cast<uint32_t*>(base);  // counter 0
+  auto* wv = reinterpret_cast<float*>(base + kCounterBytes);
+  auto* wi = reinterpret_cast<int32_t*>(base + kCounterBytes + align_up((size_t)g * 4, 256));
   hipLaunchKernelGGL(argmax_kernel, dim3(g), dim3(kArgThreads), 0, stream, v, (int)n, out, ticket,
                      wv, wi);
   return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;

@@ -39,10 +39,13 @@
  *    nothing.
  *  - Workspace: calls that take one need workspace_bytes >= the value from
  *    q8_0_workspace_bytes() for the same op and shape (0 means none is
- *    needed and the pointer may be NULL).  The workspace must be zero-filled
- *    once before its first use; every call leaves its counters at zero again.
- *    Calls that may run concurrently (different streams) need distinct
- *    workspaces.
+ *    needed and the pointer may be NULL).  Its first 64 KiB are arrival
+ *    counters used to hand partial results between workgroups; every call
+ *    leaves them at zero, and partial results always live after them, so one
+ *    workspace, zero-filled once before its first use, serves any sequence of
+ *    stream-ordered calls of any shapes.  Calls that may run concurrently
+ *    (different streams, or the same stream inside concurrent graph
+ *    branches) need distinct workspaces.
  */
 #ifndef Q8GEMV_H
 #define Q8GEMV_H

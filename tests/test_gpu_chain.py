@@ -1,0 +1,172 @@
+"""GPU decode chain (Qwen2.5-0.5B-shaped layers, glue fused into the GEMVs):
+every GEMV is checked against the oracle applied to the GPU's own input to
+that GEMV; the fused glue (RMSNorm scale, GQA broadcast, SwiGLU, residual)
+is evaluated in fp64 by the oracle; the 24-layer token is checked end to end
+through the argmax band; graph replay must equal eager execution bitwise."""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_gemv_amd as q
+import oracle
+import q8tol
+import workloads as W
+from block_quantized_gemv_amd.decode import ChainConfig, DecodeChain
+from gpu_util import DEV, host, pack, to_dev
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+# fp32 RMS scale: sum of squares over <= 1024 terms (16 per lane + 6 butterfly
+# steps), divide, add, sqrt, reciprocal -> a few tens of ulps relative.
+C_REL = 32 * U
+
+
+def normed_bound(S, y_ref):
+    """GEMV tolerance for y = c * (W h) against W (h * c_ref)."""
+    return q8tol.bound(S) + (C_REL + 2 * U) * np.abs(y_ref)
+
+
+def silu_prime(g):
+    s = 1.0 / (1.0 + np.exp(-g))
+    return s * (1.0 + g * (1.0 - s))
+
+
+def make_layers(cfg_id, cfg: ChainConfig, n_layers):
+    shapes = {W.MAT_QKV: (cfg.qkv_rows, cfg.hidden), W.MAT_WO: (cfg.hidden, cfg.hidden),
+              W.MAT_GATE_UP: (2 * cfg.intermediate, cfg.hidden),
+              W.MAT_DOWN: (cfg.hidden, cfg.intermediate)}
+    names = {W.MAT_QKV: "qkv", W.MAT_WO: "wo", W.MAT_GATE_UP: "gate_up", W.MAT_DOWN: "down"}
+    aos, packed = [], []
+    for l in range(n_layers):
+        mats = W.layer_matrices(cfg_id, l, shapes)
+        a = {names[k]: m.aos() for k, m in mats.items()}
+        aos.append(a)
+        packed.append({k: pack(v) for k, v in a.items()})
+    return aos, packed
+
+
+def stagewise(cfg: ChainConfig, n_layers, vocab_rows=None, cfg_id=2):
+    aos, packed = make_layers(cfg_id, cfg, n_layers)
+    lm = W.matrix(cfg_id, 0, W.MAT_LM_HEAD, cfg.vocab, cfg.hidden)
+    chain = DecodeChain(cfg, packed, pack(lm))
+    h0 = W.activations(cfg_id, 1, cfg.hidden)[0]
+    chain.h0.copy_(to_dev(h0))
+    it = chain.run_layer_calls()
+    H, I = cfg.hidden, cfg.intermediate
+    voff = (cfg.n_heads + cfg.n_kv_heads) * cfg.head_dim
+    for l in range(n_layers):
+        hin = host(chain.h0 if l == 0 else chain.h).astype(np.float64)
+        next(it)  # qkv = Wqkv rmsnorm(h)
+        qkv = host(chain.qkv).astype(np.float64)
+        yr, S = oracle.gemv(aos[l]["qkv"], oracle.rmsnorm(hin, cfg.eps))
+        assert np.all(np.abs(qkv - yr) <= normed_bound(S, yr)), f"layer {l} qkv"
+        next(it)  # h = h + Wo gqa(v)
+        h1 = host(chain.h).astype(np.float64)
+        att = oracle.gqa_position0(qkv[voff:voff + cfg.n_kv_heads * cfg.head_dim], cfg.n_heads,
+                                   cfg.n_kv_heads, cfg.head_dim)
+        t, S = oracle.gemv(aos[l]["wo"], att)
+        yr = hin + t
+        assert np.all(np.abs(h1 - yr) <= q8tol.bound(S) + 2 * U * np.abs(yr)), f"layer {l} wo"
+        next(it)  # s = swiglu(Wgu rmsnorm(h))
+        s = host(chain.s).astype(np.float64)
+        gu, S = oracle.gemv(aos[l]["gate_up"], oracle.rmsnorm(h1, cfg.eps))
+        g, u = gu[:I], gu[I:]
+        tg = normed_bound(S[:I], g)
+        tu = normed_bound(S[I:], u)
+        sil = g / (1 + np.exp(-g))
+        b = (np.abs(silu_prime(g)) * np.abs(u) * tg + (np.abs(sil) + 1.2 * tg) * tu
+             + 0.5 * tg * tg * np.abs(u) + 8 * U * np.abs(sil * u))
+        assert np.all(np.abs(s - oracle.swiglu(g, u)) <= b), f"layer {l} swiglu"
+        next(it)  # h = h + Wdown s
+        h2 = host(chain.h).astype(np.float64)
+        t, S = oracle.gemv(aos[l]["down"], s)
+        yr = h1 + t
+        assert np.all(np.abs(h2 - yr) <= q8tol.bound(S) + 2 * U * np.abs(yr)), f"layer {l} down"
+    hin = host(chain.h if n_layers else chain.h0).astype(np.float64)
+    next(it)  # logits = Wlm rmsnorm(h); argmax
+    logits = host(chain.logits)
+    pick = int(host(chain.next_token)[0])
+    assert pick == int(np.argmax(logits))
+    rows = np.unique(np.concatenate([np.random.default_rng(0).integers(0, cfg.vocab, 3000),
+                                     [0, cfg.vocab - 1, pick]]))
+    yr, S = oracle.gemv(lm.aos()[rows], oracle.rmsnorm(hin, cfg.eps))
+    lg = logits[rows].astype(np.float64)
+    assert np.all(np.abs(lg - yr) <= normed_bound(S, yr)), "lm_head"
+    return chain
+
+
+def test_chain_two_layers_stagewise():
+    stagewise(ChainConfig(), 2)
+
+
+def test_chain_small_config_stagewise():
+    cfg = ChainConfig(hidden=128, n_heads=4, n_kv_heads=2, head_dim=32, intermediate=192,
+                      vocab=1000)
+    stagewise(cfg, 3, cfg_id=60)
+
+
+def test_chain_24_layers_end_to_end():
+    """The full Qwen2.5-0.5B-shaped step: 24 layers + lm_head + argmax.  The
+    pick must be the oracle's (fp64 throughout) whenever the oracle's top-2
+    logit gap exceeds the accumulated fp32 error allowance; otherwise the pick
+    must lie within that allowance of the maximum."""
+    cfg = ChainConfig()
+    aos, packed = make_layers(2, cfg, 24)
+    lm = W.matrix(2, 0, W.MAT_LM_HEAD, cfg.vocab, cfg.hidden)
+    chain = DecodeChain(cfg, packed, pack(lm))
+    h0 = W.activations(2, 1, cfg.hidden)[0]
+    chain.h0.copy_(to_dev(h0))
+    chain.enqueue()
+    pick = int(host(chain.next_token)[0])
+    logits = host(chain.logits)
+    assert pick == int(np.argmax(logits))
+    h = h0.astype(np.float64)
+    for l in range(24):
+        h = oracle.qwen_layer(aos[l]["qkv"], aos[l]["wo"], aos[l]["gate_up"], aos[l]["down"], h,
+                              cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.eps)
+    yr, S = oracle.gemv(lm.aos(), oracle.rmsnorm(h, cfg.eps))
+    order = np.argsort(-yr)
+    gap = yr[order[0]] - yr[order[1]]
+    allowance = 1e-3 * np.abs(yr[order[0]])
+    print(f"oracle top-2 gap {gap:.4g}, allowance {allowance:.4g}, pick {pick}, oracle {order[0]}")
+    if gap > allowance:
+        assert pick == order[0]
+    else:
+        assert yr[pick] >= yr[order[0]] - allowance
+    # hidden state after 24 layers agrees closely with the fp64 chain
+    hg = host(chain.h).astype(np.float64)
+    assert np.max(np.abs(hg - h)) <= 1e-3 * np.max(np.abs(h))
+
+
+def test_chain_graph_replay_bitwise_equals_eager():
+    cfg = ChainConfig(vocab=4096)
+    aos, packed = make_layers(70, cfg, 2)
+    lm = W.matrix(70, 0, W.MAT_LM_HEAD, cfg.vocab, cfg.hidden)
+    chain = DecodeChain(cfg, packed, pack(lm))
+    chain.h0.copy_(to_dev(W.activations(70, 1, cfg.hidden)[0]))
+    chain.enqueue()
+    ref = (chain.h.clone(), chain.logits.clone(), chain.next_token.clone())
+    g = chain.capture()
+    for _ in range(3):
+        chain.h.fill_(0)
+        chain.logits.fill_(0)
+        chain.next_token.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(chain.h, ref[0])
+        assert torch.equal(chain.logits, ref[1])
+        assert torch.equal(chain.next_token, ref[2])
+        chain.enqueue()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(chain.logits, ref[1])
+    # a new input flows through the captured graph
+    chain.h0.copy_(to_dev(W.activations(71, 1, cfg.hidden)[0]))
+    g.replay()
+    torch.cuda.synchronize()
+    new_logits = chain.logits.clone()
+    chain.enqueue()
+    torch.cuda.synchronize()
+    assert torch.equal(chain.logits, new_logits)
+    assert not torch.equal(new_logits, ref[1])

@@ -1,0 +1,50 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark uses: every output for the single 896 x 896 GEMV, sampled rows (the
+oracle computes them one by one) for the LM head and the 9B-class verify
+chunk shapes."""
+import numpy as np
+import pytest
+
+import block_quantized_gemv_amd as q
+import oracle
+import q8tol
+import workloads as W
+from gpu_util import host, pack, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_single_gemv_896():
+    c = W.C1
+    m = W.matrix(c["cfg"], 0, 0, c["M"], c["K"])
+    x = W.activations(c["cfg"], c["N"], c["K"])
+    y = host(q.q8_0_gemv(pack(m), to_dev(x)))
+    yr, S = oracle.gemv(m.aos(), x)
+    q8tol.check(y, yr, S, "C1 896x896")
+
+
+def test_lm_head_plain_gemv_sampled():
+    c = W.C3
+    m = W.matrix(c["cfg"], 0, W.MAT_LM_HEAD, c["M"], c["K"])
+    x = W.activations(c["cfg"], 1, c["K"])
+    y = host(q.q8_0_gemv(pack(m), to_dev(x)))[0]
+    rows = np.unique(np.concatenate([np.random.default_rng(3).integers(0, c["M"], 4000),
+                                     np.arange(64), np.arange(c["M"] - 64, c["M"])]))
+    yr, S = oracle.gemv(m.aos()[rows], x)
+    q8tol.check(y[rows], yr[0], S[0], "lm_head sampled")
+
+
+@pytest.mark.parametrize("mat", [W.MAT_GATE_UP, W.MAT_DOWN])
+def test_verify_chunk_9b_shapes_sampled(mat):
+    c = W.C4
+    M, K = W.C4_SHAPES[mat]
+    m = W.matrix(c["cfg"], 0, mat, M, K)
+    p = pack(m)
+    g = np.random.default_rng(mat)
+    rows = np.unique(np.concatenate([g.integers(0, M, 512), [0, 63, 64, M - 1]]))
+    aos_rows = m.aos()[rows]
+    for N in c["Ns"]:
+        x = W.activations(c["cfg"], N, K, layer=N)
+        y = host(q.q8_0_gemv(p, to_dev(x)))
+        yr, S = oracle.gemv(aos_rows, x)
+        q8tol.check(y[:, rows], yr, S, f"C4 {M}x{K} N={N}")

@@ -143,3 +143,33 @@ def test_rejects_host_and_misaligned_pointers():
     rc = L.q8_0_gemv(ctypes.byref(p2.desc), x2.data_ptr(), y2.data_ptr(), 896, 4864, 1,
                      None, 0, None)
     assert rc == q.Q8_EWORKSPACE
+
+
+def test_one_workspace_serves_interleaved_shapes():
+    """Split-K GEMVs, fused argmax and standalone argmax of different shapes
+    share one workspace: counters never land on another call's partials."""
+    g = W.rng(26)
+    shapes = [(896, 4864), (5000, 896), (130, 12288), (4096, 2048)]
+    mats = [W.draw_matrix(g, M, K) for (M, K) in shapes]
+    packs = [pack(m) for m in mats]
+    xs = [W.draw_x(g, 1, K)[0] for (_, K) in shapes]
+    need = max([q.q8_0_workspace_bytes(q.Q8_OP_GEMV, M, K, 1) for (M, K) in shapes] +
+               [q.q8_0_workspace_bytes(q.Q8_OP_GEMV_FUSED, M, K, q.Q8_EPI_ARGMAX)
+                for (M, K) in shapes] + [q.q8_0_workspace_bytes(q.Q8_OP_ARGMAX, 100003, 0, 0)])
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    refs = [oracle.gemv(m.aos(), x) for m, x in zip(mats, xs)]
+    v = W.draw_x(g, 1, 100003)[0]
+    am = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for rnd in range(3):
+        for i, (M, K) in enumerate(shapes):
+            y = q.q8_0_gemv(packs[i], to_dev(xs[i]), workspace=ws)
+            q8tol.check(host(y), refs[i][0], refs[i][1], f"round {rnd} gemv {M}x{K}")
+            y2 = torch.empty(M, dtype=torch.float32, device=DEV)
+            f = q.make_fusion(epilogue=q.Q8_EPI_ARGMAX, argmax_out=am)
+            q.q8_0_gemv_fused(packs[i], to_dev(xs[i]), y2, f, workspace=ws)
+            yh = host(y2)
+            assert int(host(am)[0]) == int(np.argmax(yh)), (rnd, M, K)
+            out = q.q8_0_argmax(to_dev(v), workspace=ws)
+            assert int(host(out)[0]) == int(np.argmax(v))
+    # every counter is back at zero
+    assert int(ws[:65536].view(torch.int32).abs().sum().item()) == 0

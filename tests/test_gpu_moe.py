@@ -1,0 +1,184 @@
+"""GPU mixture-of-experts FFN, stage by stage against the oracle:
+router ids bit-exact, gate_up of every slot (+ shared) in one launch, SwiGLU
+epilogue, and the fused down + weighted combine in one launch."""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_gemv_amd as q
+import oracle
+import q8tol
+import workloads as W
+from gpu_util import DEV, host, pack, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def silu_prime(g):
+    s = 1.0 / (1.0 + np.exp(-g))
+    return s * (1.0 + g * (1.0 - s))
+
+
+def swiglu_bound(g_ref, u_ref, Sg, Su):
+    """Tolerance of h = silu(g) * u computed in fp32 from g, u that are each
+    within the GEMV tolerance: first-order propagation plus the fp32
+    evaluation of silu and the product (a few ulps of |h|)."""
+    tg, tu = q8tol.bound(Sg), q8tol.bound(Su)
+    sil = g_ref / (1.0 + np.exp(-g_ref))
+    h = sil * u_ref
+    return (np.abs(silu_prime(g_ref)) * np.abs(u_ref) * tg + (np.abs(sil) + 1.2 * tg) * tu
+            + 0.5 * tg * tg * np.abs(u_ref) + 8 * 2.0 ** -24 * np.abs(h))
+
+
+class MoE:
+    def __init__(self, cfg, E, H, I, Ish, S=4):
+        self.E, self.H, self.I, self.Ish, self.S = E, H, I, Ish, S
+        self.gu = W.expert_stack(cfg, W.MAT_GATE_UP, E, 2 * I, H)
+        self.dn = W.expert_stack(cfg, W.MAT_DOWN, E, H, I)
+        self.sgu = W.matrix(cfg, 0, W.MAT_SHARED_GU, 2 * Ish, H).aos()
+        self.sdn = W.matrix(cfg, 0, W.MAT_SHARED_DOWN, H, Ish).aos()
+        self.p_gu = pack(self.gu, 2 * I, H, n_mats=E)
+        self.p_dn = pack(self.dn, H, I, n_mats=E)
+        self.p_sgu = pack(self.sgu)
+        self.p_sdn = pack(self.sdn)
+        self.cfg = cfg
+
+    def inputs(self, token):
+        x = W.activations(self.cfg, 1, self.H, layer=token)[0]
+        lg = W.router_logits(self.cfg, token, self.E)
+        lam = W.shared_gate_logit(self.cfg, token)
+        return x, lg, lam
+
+    def scatter(self, ids, x, swiglu, shared=True):
+        Mo = self.I if swiglu else 2 * self.I
+        Msh = (self.Ish if swiglu else 2 * self.Ish) if shared else 0
+        y = torch.full((self.S * Mo + Msh,), np.nan, dtype=torch.float32, device=DEV)
+        mode = q.Q8_MOE_SCATTER | (q.Q8_MOE_SWIGLU if swiglu else 0)
+        q.q8_0_moe_gemv(self.p_gu, ids, None, x, y, mode, shared=self.p_sgu if shared else None)
+        return y
+
+    def combine(self, ids, w, h, lam, shared=True):
+        y = torch.full((self.H,), np.nan, dtype=torch.float32, device=DEV)
+        q.q8_0_moe_gemv(self.p_dn, ids, w, h, y, q.Q8_MOE_COMBINE,
+                        shared=self.p_sdn if shared else None,
+                        shared_gate=lam if shared else None)
+        return y
+
+
+def run_stagewise(moe: MoE, token: int):
+    x, lg, lam = moe.inputs(token)
+    xd, lgd = to_dev(x), to_dev(lg)
+    lamd = torch.tensor([lam], dtype=torch.float32, device=DEV)
+    ids, w = q.q8_0_route_topk(lgd, moe.S)
+    ids_r, w_r = oracle.route_topk(lg, moe.S)
+    idh = host(ids)
+    assert np.array_equal(idh, ids_r)
+    assert np.all(np.abs(host(w).astype(np.float64) - w_r) <= 1e-6)
+    I, Ish = moe.I, moe.Ish
+    # gate_up of every slot + shared, one launch, raw outputs
+    gu = host(moe.scatter(ids, xd, swiglu=False)).astype(np.float64)
+    refs = []
+    for s in range(moe.S):
+        yr, S = oracle.gemv(moe.gu[idh[s]], x)
+        q8tol.check(gu[s * 2 * I:(s + 1) * 2 * I], yr, S, f"scatter slot {s}")
+        refs.append((yr, S))
+    ysh, Ssh = oracle.gemv(moe.sgu, x)
+    q8tol.check(gu[moe.S * 2 * I:], ysh, Ssh, "scatter shared")
+    # SwiGLU epilogue
+    h = moe.scatter(ids, xd, swiglu=True)
+    hh = host(h).astype(np.float64)
+    for s, (yr, S) in enumerate(refs):
+        b = swiglu_bound(yr[:I], yr[I:], S[:I], S[I:])
+        err = np.abs(hh[s * I:(s + 1) * I] - oracle.swiglu(yr[:I], yr[I:]))
+        assert np.all(err <= b), f"swiglu slot {s}"
+    b = swiglu_bound(ysh[:Ish], ysh[Ish:], Ssh[:Ish], Ssh[Ish:])
+    assert np.all(np.abs(hh[moe.S * I:] - oracle.swiglu(ysh[:Ish], ysh[Ish:])) <= b)
+    # combine on the GPU's own h, router weights and gate logit
+    y = host(moe.combine(ids, w, h, lamd)).astype(np.float64)
+    yr, Sabs = oracle.moe_combine(moe.dn, idh, host(w).astype(np.float64),
+                                  hh[:moe.S * I].reshape(moe.S, I), moe.sdn, hh[moe.S * I:],
+                                  oracle.sigmoid(float(lam)))
+    q8tol.check(y, yr, Sabs, "combine")
+    # end to end against the oracle on x (reported; rounding composes)
+    ye = oracle.moe_ffn(moe.gu, moe.dn, ids_r, w_r, moe.sgu, moe.sdn, oracle.sigmoid(float(lam)), x)
+    rel = float(np.max(np.abs(y - ye)) / np.max(np.abs(ye)))
+    assert rel < 1e-3, rel
+    return ids, w, h, y
+
+
+def test_moe_small_stagewise():
+    moe = MoE(cfg=50, E=8, H=256, I=128, Ish=192)
+    for token in range(4):
+        run_stagewise(moe, token)
+
+
+def test_moe_qwen15_shapes_stagewise():
+    c = W.C5
+    moe = MoE(cfg=c["cfg"], E=c["n_experts"], H=c["hidden"], I=c["inter"], Ish=c["shared_inter"],
+              S=c["top_k"])
+    for token in range(2):
+        run_stagewise(moe, token)
+
+
+def test_moe_fused_equals_per_slot_composition():
+    """The one-launch scatter/combine equals per-slot dense GEMV calls on each
+    selected expert (the fused-vs-per-slot check of the #144 PR), within the
+    GEMV tolerance."""
+    moe = MoE(cfg=51, E=8, H=256, I=128, Ish=192)
+    x, lg, lam = moe.inputs(0)
+    xd = to_dev(x)
+    ids, w = q.q8_0_route_topk(to_dev(lg), moe.S)
+    idh = host(ids)
+    gu = host(moe.scatter(ids, xd, swiglu=False)).astype(np.float64)
+    for s in range(moe.S):
+        ys = host(q.q8_0_gemv(moe.p_gu.expert(int(idh[s])), xd)).astype(np.float64)
+        _, S = oracle.gemv(moe.gu[idh[s]], x)
+        assert np.all(np.abs(gu[s * 256:(s + 1) * 256] - ys) <= 2 * q8tol.bound(S))
+
+
+def test_moe_one_hot_weights_no_shared_is_dense_ffn():
+    moe = MoE(cfg=52, E=8, H=256, I=128, Ish=192)
+    x, lg, _ = moe.inputs(1)
+    xd = to_dev(x)
+    ids, _ = q.q8_0_route_topk(to_dev(lg), moe.S)
+    w = torch.tensor([1.0, 0.0, 0.0, 0.0], dtype=torch.float32, device=DEV)
+    h = moe.scatter(ids, xd, swiglu=True, shared=False)
+    y = host(moe.combine(ids, w, h, None, shared=False)).astype(np.float64)
+    e0 = int(host(ids)[0])
+    hh = host(h).astype(np.float64)
+    yr, S = oracle.gemv(moe.dn[e0], hh[:128])
+    q8tol.check(y, yr, S, "one-hot combine")
+
+
+def test_moe_bad_expert_id_sets_status_and_zeroes_slot():
+    moe = MoE(cfg=53, E=8, H=256, I=128, Ish=192)
+    x, _, lam = moe.inputs(2)
+    xd = to_dev(x)
+    ids = torch.tensor([3, 8, -1, 5], dtype=torch.int32, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y = torch.full((4 * 256 + 384,), np.nan, dtype=torch.float32, device=DEV)
+    q.q8_0_moe_gemv(moe.p_gu, ids, None, xd, y, q.Q8_MOE_SCATTER, shared=moe.p_sgu, dev_status=st)
+    yh = host(y).astype(np.float64)
+    assert int(host(st)[0]) & 1
+    assert np.all(yh[256:768] == 0)
+    for s, e in ((0, 3), (3, 5)):
+        yr, S = oracle.gemv(moe.gu[e], x)
+        q8tol.check(yh[s * 256:(s + 1) * 256], yr, S, f"valid slot {s}")
+    st.zero_()
+    ids_ok = torch.tensor([3, 1, 2, 5], dtype=torch.int32, device=DEV)
+    q.q8_0_moe_gemv(moe.p_gu, ids_ok, None, xd, y, q.Q8_MOE_SCATTER, shared=moe.p_sgu,
+                    dev_status=st)
+    assert int(host(st)[0]) == 0
+
+
+def test_moe_repeatable():
+    moe = MoE(cfg=54, E=8, H=256, I=128, Ish=192)
+    x, lg, lam = moe.inputs(3)
+    xd, lamd = to_dev(x), torch.tensor([lam], dtype=torch.float32, device=DEV)
+    ids, w = q.q8_0_route_topk(to_dev(lg), moe.S)
+    h0 = moe.scatter(ids, xd, True).clone()
+    y0 = moe.combine(ids, w, h0, lamd).clone()
+    for _ in range(20):
+        h = moe.scatter(ids, xd, True)
+        assert torch.equal(h, h0)
+        assert torch.equal(moe.combine(ids, w, h, lamd), y0)
