@@ -353,7 +353,7 @@ int q8_0_gemv_plan(int64_t M, int64_t K, int64_t N, int32_t epilogue, int32_t ou
   Plan plan;
   if (plan_problems(&pd, 1, (int)(epilogue ? 1 : N), &plan)) return Q8_EINVAL;
   out[0] = plan.total_wg;
-  out[1] = kWaves;
+  out[1] = plan.W;
   out[2] = plan.U[0];
   out[3] = plan.P[0];
   return Q8_OK;

@@ -171,7 +171,9 @@ __device__ __forceinline__ float seg_alpha(const Seg& s) {
 }
 
 // val[ts][n] = sum over segments (in order) of alpha_seg * (sum of the
-// segment's unit partials, in unit order), for each tile of a pair.
+// segment's unit partials, in unit order), for each tile of a pair.  Partials
+// are fetched 8 units at a time so that global loads are in flight together;
+// the summation order does not depend on the batching.
 template <int N, typename Get>
 __device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, int us, Get get,
                                            float (&val)[2][N]) {
@@ -186,9 +188,24 @@ __device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, 
       float ssum[N];
 #pragma unroll
       for (int n = 0; n < N; ++n) ssum[n] = 0.f;
-      for (int i = 0; i < s.units; ++i, ++uu) {
+      for (int i0 = 0; i0 < s.units; i0 += 8) {
+        const int cnt = s.units - i0 < 8 ? s.units - i0 : 8;
+        float buf[8][N];
 #pragma unroll
-        for (int n = 0; n < N; ++n) ssum[n] += get(uu, n);
+        for (int j = 0; j < 8; ++j) {
+          if (j < cnt) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) buf[j][n] = get(uu + j, n);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (j < cnt) {
+#pragma unroll
+            for (int n = 0; n < N; ++n) ssum[n] += buf[j][n];
+          }
+        }
+        uu += cnt;
       }
       if (s.alpha_mode == A_ONE) {
 #pragma unroll
@@ -203,8 +220,8 @@ __device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, 
 }
 
 template <int N>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvParams p) {
-  __shared__ float lds_part[kWaves][N][64];
+__global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const GemvParams p) {
+  extern __shared__ float lds_part[];  // [W][N][64]
   __shared__ int s_last;
 
   const int g = blockIdx.x;
@@ -212,15 +229,17 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvParams p) {
   while (pi + 1 < p.nprob && g >= p.prob[pi + 1].wg0) ++pi;
   const Prob& pr = p.prob[pi];
 
+  const int W = p.W;
   const int lg = g - pr.wg0;
   const int ot = lg / pr.P;
   const int pp = lg - ot * pr.P;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int u = pp * kWaves + wave;
+  const int u = pp * W + wave;
   const int us = pr.U / pr.R;  // units per tile of a pair
 
-  // RMS prologue: issue the loads early (wave 0 folds), reduce after the dot.
+  // RMS prologue: wave 0 (the folding wave) issues its loads of the vector
+  // first and reduces them after the dot products.
   float rx[16];
   const bool want_rms = (pr.flags & F_RMSNORM) && wave == 0 && pr.rms_K <= 1024;
   if (want_rms) {
@@ -266,10 +285,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvParams p) {
   float val[2][N];
   if (pr.P == 1) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) lds_part[wave][n][lane] = acc[n];
+    for (int n = 0; n < N; ++n) lds_part[(wave * N + n) * 64 + lane] = acc[n];
     __syncthreads();
     if (wave != 0) return;
-    fold_units<N>(p, pr, us, [&](int uu, int n) { return lds_part[uu][n][lane]; }, val);
+    fold_units<N>(p, pr, us, [&](int uu, int n) { return lds_part[(uu * N + n) * 64 + lane]; },
+                  val);
   } else {
     float* gp = pr.part + (int64_t)ot * pr.U * N * 64;
     if (u < pr.U) {
@@ -324,33 +344,48 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvParams p) {
     if (valid) pr.y[n * pr.y_stride + row] = v;
   }
   if (pr.flags & F_ARGMAX) {
+    // per-tile (max, lowest index); the fold over tiles runs in the next
+    // kernel of the same call, ordered by the kernel boundary
     float mv = valid ? out[0] : -INFINITY;
     int mi = row;
     wave_argmax(mv, mi);
     if (lane == 0) {
-      st_dev(pr.am_val + ot, mv);
-      st_dev(pr.am_idx + ot, mi);
+      pr.am_val[ot] = mv;
+      pr.am_idx[ot] = mi;
     }
-    wait_stores();
-    int last = 0;
-    if (lane == 0) last = ticket_add(pr.am_ticket) == (unsigned)(pr.Tout - 1);
-    last = __builtin_amdgcn_readfirstlane(last);
-    if (!last) return;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int i = lane; i < pr.Tout; i += 64) {
-      const float tv = ld_dev(pr.am_val + i);
-      const int ti = ld_dev(pr.am_idx + i);
-      if (tv > bv || (tv == bv && ti < bi)) {
-        bv = tv;
-        bi = ti;
+  }
+}
+
+// Fold of per-tile argmax partials: lowest index among the largest values.
+__global__ __launch_bounds__(256) void argmax_fold_kernel(const float* __restrict__ v,
+                                                          const int32_t* __restrict__ idx, int n,
+                                                          int32_t* out) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const float tv = v[i];
+    const int ti = idx[i];
+    if (tv > bv || (tv == bv && ti < bi)) {
+      bv = tv;
+      bi = ti;
+    }
+  }
+  wave_argmax(bv, bi);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (sv[w] > bv || (sv[w] == bv && si[w] < bi)) {
+        bv = sv[w];
+        bi = si[w];
       }
-    }
-    wave_argmax(bv, bi);
-    if (lane == 0) {
-      *pr.argmax_out = bi;
-      st_dev(pr.am_ticket, 0u);
-    }
+    *out = bi;
   }
 }
 
@@ -366,10 +401,13 @@ int env_int(const char* name, int dflt) {
   return x > 0 ? x : dflt;
 }
 
-// Waves the planner aims for across one launch (all problems), and the
-// fewest blocks a unit should own.  Q8G_TARGET_WAVES / Q8G_MIN_BLOCKS override
-// them for tuning sweeps (they change the summation order, not the result
-// beyond the stated tolerance).
+// Planner targets, overridable for tuning sweeps (the overrides change the
+// summation order, never the result beyond the stated tolerance):
+//  Q8G_TARGET_WAVES  waves aimed for across one launch
+//  Q8G_MIN_BLOCKS    fewest 32-weight blocks a unit (one wave's K range) owns
+//  Q8G_MIN_UNITS     fewest units per 64-row tile when K allows
+//  Q8G_MAX_WAVES     most waves per workgroup (units of one tile beyond it
+//                    spill into more workgroups and a ticketed fold)
 int target_waves() {
   static const int v = env_int("Q8G_TARGET_WAVES", 2048);
   return v;
@@ -377,6 +415,58 @@ int target_waves() {
 int min_blocks() {
   static const int v = env_int("Q8G_MIN_BLOCKS", 4);
   return v;
+}
+int min_units() {
+  static const int v = env_int("Q8G_MIN_UNITS", 4);
+  return v;
+}
+int max_waves() {
+  static const int v = env_int("Q8G_MAX_WAVES", kMaxWaves);
+  return v < kMaxWaves ? v : kMaxWaves;
+}
+
+// Units of one tile of a pair, spread over the segments in proportion to
+// their blocks (each segment >= 1 unit, <= its blocks).
+void distribute(const ProbDesc& pd, int64_t us, int64_t blocks, int64_t* su) {
+  int64_t left = us;
+  for (int s = 0; s < pd.nseg; ++s) {
+    const int64_t nb = pd.seg[s].W->K / 32;
+    su[s] = us * nb / blocks;
+    if (su[s] < 1) su[s] = 1;
+    if (su[s] > nb) su[s] = nb;
+    left -= su[s];
+  }
+  while (left > 0) {  // the segment with the most blocks per unit takes one more
+    int best = -1;
+    double bestr = 0;
+    for (int s = 0; s < pd.nseg; ++s) {
+      const int64_t nb = pd.seg[s].W->K / 32;
+      if (su[s] >= nb) continue;
+      const double r = (double)nb / (double)su[s];
+      if (r > bestr) {
+        bestr = r;
+        best = s;
+      }
+    }
+    if (best < 0) break;
+    ++su[best];
+    --left;
+  }
+  while (left < 0) {  // over budget because of the one-per-segment minimum
+    int best = -1;
+    double bestr = 1e300;
+    for (int s = 0; s < pd.nseg; ++s) {
+      if (su[s] <= 1) continue;
+      const double r = (double)(pd.seg[s].W->K / 32) / (double)su[s];
+      if (r < bestr) {
+        bestr = r;
+        best = s;
+      }
+    }
+    if (best < 0) break;
+    --su[best];
+    ++left;
+  }
 }
 
 }  // namespace
@@ -393,128 +483,66 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
   }
   if (segc > kMaxSeg || nprob > kMaxProb || total_tout <= 0) return Q8_EINVAL;
   const int64_t want_u = cdiv(target_waves(), total_tout);
-  int64_t cnt = 0;
-  size_t data = 0;
-  int wg = 0;
+  const int wmax = max_waves();
+  // units per tile
   int sbase = 0;
+  int64_t U[kMaxProb];
   for (int i = 0; i < nprob; ++i) {
     const ProbDesc& pd = probs[i];
-    const int64_t Mout = pd.R == 2 ? pd.M / 2 : pd.M;
-    const int64_t Tout = cdiv(Mout, kTile);
     int64_t blocks = 0;
     for (int s = 0; s < pd.nseg; ++s) blocks += pd.seg[s].W->K / 32;
-    // units per tile of a pair (per tsel)
-    int64_t us = cdiv(want_u, pd.R);
     const int64_t us_max = blocks / min_blocks() > pd.nseg ? blocks / min_blocks() : pd.nseg;
+    int64_t us = cdiv(want_u, pd.R);
+    const int64_t us_min = cdiv(min_units(), pd.R);
+    if (us < us_min) us = us_min;
     if (us > us_max) us = us_max;
     if (us < pd.nseg) us = pd.nseg;
     if (us > blocks) us = blocks;
-    // at least one full workgroup per output tile when the K range allows it
-    if (us * pd.R < kWaves) {
-      us = cdiv(kWaves, pd.R);
-      if (us > us_max) us = us_max;
-      if (us > blocks) us = blocks;
-    }
-    int64_t U = us * pd.R;
-    if (U > kWaves) {  // fill whole workgroups
-      U = cdiv(U, kWaves) * kWaves;
-      us = U / pd.R;
-      if (us > blocks) us = blocks;
-      U = us * pd.R;
-    }
-    // distribute the us units over the segments in proportion to their blocks
-    int64_t left = us;
     int64_t su[kMaxSeg];
-    for (int s = 0; s < pd.nseg; ++s) {
-      const int64_t nb = pd.seg[s].W->K / 32;
-      su[s] = us * nb / blocks;
-      if (su[s] < 1) su[s] = 1;
-      if (su[s] > nb) su[s] = nb;
-      left -= su[s];
-    }
-    while (left > 0) {  // give the rest to the segment with the most blocks per unit
-      int best = -1;
-      double bestr = 0;
-      for (int s = 0; s < pd.nseg; ++s) {
-        const int64_t nb = pd.seg[s].W->K / 32;
-        if (su[s] >= nb) continue;
-        const double r = (double)nb / (double)su[s];
-        if (r > bestr) {
-          bestr = r;
-          best = s;
-        }
-      }
-      if (best < 0) break;
-      ++su[best];
-      --left;
-    }
-    while (left < 0) {  // took too many (minimum one per segment)
-      int best = -1;
-      double bestr = 1e300;
-      for (int s = 0; s < pd.nseg; ++s) {
-        if (su[s] <= 1) continue;
-        const double r = (double)(pd.seg[s].W->K / 32) / (double)su[s];
-        if (r < bestr) {
-          bestr = r;
-          best = s;
-        }
-      }
-      if (best < 0) break;
-      --su[best];
-      ++left;
-    }
+    distribute(pd, us, blocks, su);
     int64_t usum = 0;
     for (int s = 0; s < pd.nseg; ++s) {
       plan->seg_units[sbase + s] = (int32_t)su[s];
       usum += su[s];
     }
-    U = usum * pd.R;
-    // per-tile arrival counters are needed when a tile spans workgroups; keep
-    // them within the fixed counter region
-    int64_t P = cdiv(U, kWaves);
-    const int64_t cnt_need = (P > 1 ? Tout : 0) + ((pd.flags & F_ARGMAX) ? 1 : 0);
-    if (P > 1 && cnt + cnt_need > kMaxCounters) {
-      // too many tiles to split across workgroups: one workgroup per tile
-      if ((int64_t)pd.nseg * pd.R > kWaves) return Q8_EINVAL;
-      int64_t left2 = kWaves / pd.R;
-      for (int s = 0; s < pd.nseg; ++s) {
-        su[s] = 1;
-        --left2;
-      }
-      for (int s = 0, guard = 0; left2 > 0 && guard < 64 * kMaxSeg; s = (s + 1) % pd.nseg, ++guard) {
-        if (su[s] < pd.seg[s].W->K / 32) {
-          ++su[s];
-          --left2;
-        }
-      }
-      usum = 0;
-      for (int s = 0; s < pd.nseg; ++s) {
-        plan->seg_units[sbase + s] = (int32_t)su[s];
-        usum += su[s];
-      }
-      U = usum * pd.R;
-      P = 1;
-    }
-    const int64_t cnt_use = (P > 1 ? Tout : 0) + ((pd.flags & F_ARGMAX) ? 1 : 0);
-    if (cnt + cnt_use > kMaxCounters) return Q8_EINVAL;
-    plan->U[i] = (int32_t)U;
+    U[i] = usum * pd.R;
+    sbase += pd.nseg;
+  }
+  // waves per workgroup (common to the launch) and workgroups per tile
+  int64_t W = 1;
+  for (int i = 0; i < nprob; ++i) {
+    const int64_t P = cdiv(U[i], wmax);
+    const int64_t w = cdiv(U[i], P);
+    if (w > W) W = w;
+  }
+  int64_t cnt = 0;
+  size_t data = 0;
+  int64_t wg = 0;
+  for (int i = 0; i < nprob; ++i) {
+    const ProbDesc& pd = probs[i];
+    const int64_t Mout = pd.R == 2 ? pd.M / 2 : pd.M;
+    const int64_t Tout = cdiv(Mout, kTile);
+    const int64_t P = cdiv(U[i], W);
+    plan->U[i] = (int32_t)U[i];
     plan->P[i] = (int32_t)P;
     plan->cnt_off[i] = (int32_t)cnt;
     plan->data_off[i] = data;
-    cnt += cnt_use;
+    if (P > 1) cnt += Tout;
     if (pd.flags & F_ARGMAX) data += align_up((size_t)Tout * 4, 256) * 2;
-    if (P > 1) data += align_up((size_t)Tout * U * N * 64 * 4, 256);
-    wg += (int)(Tout * P);
-    sbase += pd.nseg;
+    if (P > 1) data += align_up((size_t)Tout * U[i] * N * 64 * 4, 256);
+    wg += Tout * P;
   }
+  if (cnt > kMaxCounters || wg > 0x7fffffff) return Q8_EINVAL;
+  plan->W = (int32_t)W;
   plan->ws_bytes = (cnt > 0 || data > 0) ? kCounterBytes + data : 0;
-  plan->total_wg = wg;
+  plan->total_wg = (int32_t)wg;
   return Q8_OK;
 }
 
 template <int N>
 static hipError_t launch_n(const GemvParams& gp, int wgs, hipStream_t stream) {
-  hipLaunchKernelGGL(gemv_kernel<N>, dim3(wgs), dim3(kThreads), 0, stream, gp);
+  const size_t lds = (size_t)gp.W * N * 64 * sizeof(float);
+  hipLaunchKernelGGL(gemv_kernel<N>, dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
   return hipGetLastError();
 }
 
@@ -553,14 +581,9 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
     pr.argmax_out = pd.argmax_out;
     pr.dev_status = pd.dev_status;
     if (plan.ws_bytes > 0) {
-      uint32_t* cnt = static_cast<uint32_t*>(ws) + plan.cnt_off[i];
       uint8_t* base = static_cast<uint8_t*>(ws) + kCounterBytes + plan.data_off[i];
-      if (pr.P > 1) {
-        pr.tile_tickets = cnt;
-        cnt += Tout;
-      }
+      if (pr.P > 1) pr.tile_tickets = static_cast<uint32_t*>(ws) + plan.cnt_off[i];
       if (pd.flags & F_ARGMAX) {
-        pr.am_ticket = cnt;
         pr.am_val = reinterpret_cast<float*>(base);
         base += align_up((size_t)Tout * 4, 256);
         pr.am_idx = reinterpret_cast<int32_t*>(base);
@@ -595,6 +618,7 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
     wg += (int)(Tout * pr.P);
   }
   gp.total_wg = wg;
+  gp.W = plan.W;
   if (wg <= 0) return Q8_OK;
   hipError_t e;
   switch (N) {
@@ -608,7 +632,15 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
     case 8: e = launch_n<8>(gp, wg, stream); break;
     default: return Q8_EINVAL;
   }
-  return e == hipSuccess ? Q8_OK : Q8_ELAUNCH;
+  if (e != hipSuccess) return Q8_ELAUNCH;
+  for (int i = 0; i < nprob; ++i) {
+    const Prob& pr = gp.prob[i];
+    if (!(pr.flags & F_ARGMAX)) continue;
+    hipLaunchKernelGGL(argmax_fold_kernel, dim3(1), dim3(256), 0, stream, pr.am_val, pr.am_idx,
+                       pr.Tout, pr.argmax_out);
+    if (hipGetLastError() != hipSuccess) return Q8_ELAUNCH;
+  }
+  return Q8_OK;
 }
 
 }  // namespace q8

@@ -11,8 +11,8 @@
 namespace q8 {
 
 constexpr int kTile = Q8_TILE_ROWS;  // rows per packed tile, one per lane
-constexpr int kWaves = 4;            // waves per GEMV workgroup
-constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxWaves = 16;        // most waves per GEMV workgroup
+constexpr int kMaxThreads = 64 * kMaxWaves;
 constexpr int kMaxSeg = 9;           // K-segments over all problems of one launch
 constexpr int kMaxProb = 9;          // problems (independent GEMVs) per launch
 // Every workspace starts with a fixed region of 32-bit counters that each
@@ -73,8 +73,7 @@ struct Prob {
   int32_t rms_K;
   int32_t* argmax_out;
   uint32_t* tile_tickets;  // [Tout] arrivals per output tile (P > 1)
-  uint32_t* am_ticket;   // arrivals of argmax partials (F_ARGMAX)
-  float* am_val;         // [Tout]
+  float* am_val;         // [Tout] per-tile argmax partials (F_ARGMAX)
   int32_t* am_idx;       // [Tout]
   float* part;           // [Tout][U][N][64] partial sums when P > 1
   int32_t* dev_status;
@@ -85,6 +84,7 @@ struct GemvParams {
   Prob prob[kMaxProb];
   int32_t nprob;
   int32_t total_wg;
+  int32_t W;             // waves per workgroup
 };
 
 // Host-side launcher shared by the C entry points (gemv.hip).
@@ -125,6 +125,7 @@ struct Plan {
   size_t data_off[kMaxProb];   // byte offset of each problem's data (after the counters)
   size_t ws_bytes;             // total (0: no workspace needed)
   int32_t total_wg;
+  int32_t W;                   // waves per workgroup
 };
 
 int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan);
