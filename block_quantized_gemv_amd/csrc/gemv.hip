@@ -219,14 +219,18 @@ __device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, 
   }
 }
 
-template <int N>
+// ONE: a single problem with a single segment (dense GEMVs and the decode
+// chain): every kernel argument sits at a fixed offset, so no search loops.
+template <int N, bool ONE>
 __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const GemvParams p) {
   extern __shared__ float lds_part[];  // [W][N][64]
   __shared__ int s_last;
 
   const int g = blockIdx.x;
   int pi = 0;
-  while (pi + 1 < p.nprob && g >= p.prob[pi + 1].wg0) ++pi;
+  if (!ONE) {
+    while (pi + 1 < p.nprob && g >= p.prob[pi + 1].wg0) ++pi;
+  }
   const Prob& pr = p.prob[pi];
 
   const int W = p.W;
@@ -256,10 +260,12 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const GemvParams p) {
   if (u < pr.U) {
     const int tsel = u / us;
     int v = u - tsel * us;
-    int si = pr.seg0;
-    while (v >= p.seg[si].units) {
-      v -= p.seg[si].units;
-      ++si;
+    int si = ONE ? 0 : pr.seg0;
+    if (!ONE) {
+      while (v >= p.seg[si].units) {
+        v -= p.seg[si].units;
+        ++si;
+      }
     }
     const Seg& s = p.seg[si];
     int e = 0;
@@ -272,8 +278,10 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const GemvParams p) {
       const int t = ot + tsel * pr.Tout;
       const uint8_t* qs_tile = s.qs + (int64_t)e * s.qs_stride + (int64_t)t * kTile * s.K;
       const uint8_t* d_tile = s.d + (int64_t)e * s.d_stride + (int64_t)t * s.G * 512;
-      const int b0 = (int)((int64_t)v * s.nblk / s.units);
-      const int b1 = (int)((int64_t)(v + 1) * s.nblk / s.units);
+      // units own whole scale quads (4 blocks); only a row's last may be short
+      const int b0 = 4 * (int)((int64_t)v * s.G / s.units);
+      const int b1e = 4 * (int)((int64_t)(v + 1) * s.G / s.units);
+      const int b1 = b1e < s.nblk ? b1e : s.nblk;
       dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
                    s.gqa_off, acc);
     } else if (lane == 0 && pr.dev_status) {
@@ -404,7 +412,7 @@ int env_int(const char* name, int dflt) {
 // Planner targets, overridable for tuning sweeps (the overrides change the
 // summation order, never the result beyond the stated tolerance):
 //  Q8G_TARGET_WAVES  waves aimed for across one launch
-//  Q8G_MIN_BLOCKS    fewest 32-weight blocks a unit (one wave's K range) owns
+//  Q8G_MIN_QUADS     fewest 4-block scale quads a unit (one wave's K range) owns
 //  Q8G_MIN_UNITS     fewest units per 64-row tile when K allows
 //  Q8G_MAX_WAVES     most waves per workgroup (units of one tile beyond it
 //                    spill into more workgroups and a ticketed fold)
@@ -412,8 +420,8 @@ int target_waves() {
   static const int v = env_int("Q8G_TARGET_WAVES", 2048);
   return v;
 }
-int min_blocks() {
-  static const int v = env_int("Q8G_MIN_BLOCKS", 4);
+int min_quads() {
+  static const int v = env_int("Q8G_MIN_QUADS", 1);
   return v;
 }
 int min_units() {
@@ -426,11 +434,11 @@ int max_waves() {
 }
 
 // Units of one tile of a pair, spread over the segments in proportion to
-// their blocks (each segment >= 1 unit, <= its blocks).
+// their scale quads (each segment >= 1 unit, <= its quads).
 void distribute(const ProbDesc& pd, int64_t us, int64_t blocks, int64_t* su) {
   int64_t left = us;
   for (int s = 0; s < pd.nseg; ++s) {
-    const int64_t nb = pd.seg[s].W->K / 32;
+    const int64_t nb = cdiv(pd.seg[s].W->K / 32, 4);
     su[s] = us * nb / blocks;
     if (su[s] < 1) su[s] = 1;
     if (su[s] > nb) su[s] = nb;
@@ -440,7 +448,7 @@ void distribute(const ProbDesc& pd, int64_t us, int64_t blocks, int64_t* su) {
     int best = -1;
     double bestr = 0;
     for (int s = 0; s < pd.nseg; ++s) {
-      const int64_t nb = pd.seg[s].W->K / 32;
+      const int64_t nb = cdiv(pd.seg[s].W->K / 32, 4);
       if (su[s] >= nb) continue;
       const double r = (double)nb / (double)su[s];
       if (r > bestr) {
@@ -457,7 +465,7 @@ void distribute(const ProbDesc& pd, int64_t us, int64_t blocks, int64_t* su) {
     double bestr = 1e300;
     for (int s = 0; s < pd.nseg; ++s) {
       if (su[s] <= 1) continue;
-      const double r = (double)(pd.seg[s].W->K / 32) / (double)su[s];
+      const double r = (double)(cdiv(pd.seg[s].W->K / 32, 4)) / (double)su[s];
       if (r < bestr) {
         bestr = r;
         best = s;
@@ -489,9 +497,10 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
   int64_t U[kMaxProb];
   for (int i = 0; i < nprob; ++i) {
     const ProbDesc& pd = probs[i];
+    // a unit owns whole scale quads of one segment; `blocks` below counts quads
     int64_t blocks = 0;
-    for (int s = 0; s < pd.nseg; ++s) blocks += pd.seg[s].W->K / 32;
-    const int64_t us_max = blocks / min_blocks() > pd.nseg ? blocks / min_blocks() : pd.nseg;
+    for (int s = 0; s < pd.nseg; ++s) blocks += cdiv(pd.seg[s].W->K / 32, 4);
+    const int64_t us_max = blocks / min_quads() > pd.nseg ? blocks / min_quads() : pd.nseg;
     int64_t us = cdiv(want_u, pd.R);
     const int64_t us_min = cdiv(min_units(), pd.R);
     if (us < us_min) us = us_min;
@@ -542,7 +551,10 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
 template <int N>
 static hipError_t launch_n(const GemvParams& gp, int wgs, hipStream_t stream) {
   const size_t lds = (size_t)gp.W * N * 64 * sizeof(float);
-  hipLaunchKernelGGL(gemv_kernel<N>, dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
+  if (gp.nprob == 1 && gp.prob[0].nseg == 1)
+    hipLaunchKernelGGL((gemv_kernel<N, true>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
+  else
+    hipLaunchKernelGGL((gemv_kernel<N, false>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
   return hipGetLastError();
 }
 
