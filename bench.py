@@ -74,7 +74,9 @@ def build_chain(n_layers, log):
             aos = W.matrix(W.C2["cfg"], l, mat, M, K).aos()
             if l == 0:
                 sample_aos[name] = aos
-            L[name] = q.PackedQ8.from_aos(torch.from_numpy(aos.reshape(-1)).to(dev), M, K)
+            layout = q.Q8_LAYOUT_GATE_UP_PAIRS if name == "gate_up" else q.Q8_LAYOUT_ROWS
+            L[name] = q.PackedQ8.from_aos(torch.from_numpy(aos.reshape(-1)).to(dev), M, K,
+                                          layout=layout)
         layers.append(L)
     lm = W.matrix(W.C2["cfg"], 0, W.MAT_LM_HEAD, cfg.vocab, cfg.hidden).aos()
     sample_aos["lm_head_rows"] = lm[:16384].copy()

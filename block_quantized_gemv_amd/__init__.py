@@ -25,7 +25,9 @@ Q8_EPI_RESIDUAL, Q8_EPI_SWIGLU, Q8_EPI_ARGMAX = 1, 2, 4
 Q8_MOE_SCATTER, Q8_MOE_COMBINE, Q8_MOE_SWIGLU = 1, 2, 4
 Q8_OP_GEMV, Q8_OP_GEMV_FUSED, Q8_OP_ARGMAX, Q8_OP_MOE_SCATTER, Q8_OP_MOE_COMBINE = 1, 2, 3, 4, 5
 
-EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_gemv", "q8_0_gemv_fused", "q8_0_argmax",
+Q8_LAYOUT_ROWS, Q8_LAYOUT_GATE_UP_PAIRS = 0, 1
+
+EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv", "q8_0_gemv_fused", "q8_0_argmax",
            "q8_0_route_topk", "q8_0_moe_gemv", "q8_0_workspace_bytes", "q8_0_gemv_plan",
            "q8_0_strerror", "q8_0_version")
 
@@ -39,7 +41,8 @@ class Q8Error(RuntimeError):
 class q8_0_weights(ctypes.Structure):
     _fields_ = [("qs", ctypes.c_void_p), ("d", ctypes.c_void_p), ("M", ctypes.c_int64),
                 ("K", ctypes.c_int64), ("n_mats", ctypes.c_int64),
-                ("qs_stride", ctypes.c_int64), ("d_stride", ctypes.c_int64)]
+                ("qs_stride", ctypes.c_int64), ("d_stride", ctypes.c_int64),
+                ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class q8_0_fusion(ctypes.Structure):
@@ -65,6 +68,7 @@ def lib() -> ctypes.CDLL:
         PW = ctypes.POINTER(q8_0_weights)
         L.q8_0_packed_size.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
         L.q8_0_repack.argtypes = [P, I64, I64, P, P, P]
+        L.q8_0_repack_layout.argtypes = [P, I64, I64, I32, P, P, P]
         L.q8_0_gemv.argtypes = [PW, P, P, I64, I64, I64, P, SZ, P]
         L.q8_0_gemv_fused.argtypes = [PW, P, P, I64, I64, ctypes.POINTER(q8_0_fusion), P, SZ, P]
         L.q8_0_argmax.argtypes = [P, I64, P, P, SZ, P]
@@ -159,45 +163,53 @@ def q8_0_packed_size(M: int, K: int) -> tuple[int, int]:
 class PackedQ8:
     """Packed device weights of one matrix or a stack of n_mats matrices."""
 
-    def __init__(self, qs: torch.Tensor, d: torch.Tensor, M: int, K: int, n_mats: int = 1):
+    def __init__(self, qs: torch.Tensor, d: torch.Tensor, M: int, K: int, n_mats: int = 1,
+                 layout: int = Q8_LAYOUT_ROWS):
         qb, db = q8_0_packed_size(M, K)
         self.qs, self.d, self.M, self.K, self.n_mats = qs, d, M, K, n_mats
-        self.qs_bytes, self.d_bytes = qb, db
-        self.desc = q8_0_weights(qs.data_ptr(), d.data_ptr(), M, K, n_mats, qb, db)
+        self.qs_bytes, self.d_bytes, self.layout = qb, db, layout
+        self.desc = q8_0_weights(qs.data_ptr(), d.data_ptr(), M, K, n_mats, qb, db, layout, 0)
 
     @classmethod
-    def empty(cls, M: int, K: int, n_mats: int = 1, device=None) -> "PackedQ8":
+    def empty(cls, M: int, K: int, n_mats: int = 1, device=None,
+              layout: int = Q8_LAYOUT_ROWS) -> "PackedQ8":
         qb, db = q8_0_packed_size(M, K)
         dev = device or torch.device("cuda")
         qs = torch.empty(n_mats * qb, dtype=torch.uint8, device=dev)
         d = torch.empty(n_mats * db, dtype=torch.uint8, device=dev)
-        return cls(qs, d, M, K, n_mats)
+        return cls(qs, d, M, K, n_mats, layout)
 
     @classmethod
-    def from_aos(cls, aos: torch.Tensor, M: int, K: int, n_mats: int = 1,
-                 stream=None) -> "PackedQ8":
+    def from_aos(cls, aos: torch.Tensor, M: int, K: int, n_mats: int = 1, stream=None,
+                 layout: int = Q8_LAYOUT_ROWS) -> "PackedQ8":
         """Repack GGUF Q8_0 blocks (uint8 device tensor of n_mats*M*(K/32)*34
-        bytes) with q8_0_repack, one matrix at a time."""
+        bytes), one matrix at a time, in the given row layout."""
         _need(aos, torch.uint8, "aos")
         per = M * (K // 32) * 34
         if aos.numel() != n_mats * per:
             raise ValueError(f"aos has {aos.numel()} bytes, expected {n_mats * per}")
-        p = cls.empty(M, K, n_mats, aos.device)
+        p = cls.empty(M, K, n_mats, aos.device, layout)
         for e in range(n_mats):
             q8_0_repack(aos[e * per:(e + 1) * per], M, K, p.qs[e * p.qs_bytes:],
-                        p.d[e * p.d_bytes:], stream)
+                        p.d[e * p.d_bytes:], stream, layout)
         return p
 
     def expert(self, e: int) -> "PackedQ8":
         return PackedQ8(self.qs[e * self.qs_bytes:(e + 1) * self.qs_bytes],
-                        self.d[e * self.d_bytes:(e + 1) * self.d_bytes], self.M, self.K, 1)
+                        self.d[e * self.d_bytes:(e + 1) * self.d_bytes], self.M, self.K, 1,
+                        self.layout)
 
 
 def q8_0_repack(aos: torch.Tensor, M: int, K: int, qs: torch.Tensor, d: torch.Tensor,
-                stream=None) -> None:
+                stream=None, layout: int = Q8_LAYOUT_ROWS) -> None:
     _need(aos, torch.uint8, "aos")
-    _check("q8_0_repack", lib().q8_0_repack(aos.data_ptr(), M, K, qs.data_ptr(), d.data_ptr(),
-                                            _stream(stream)))
+    if layout == Q8_LAYOUT_ROWS:
+        rc = lib().q8_0_repack(aos.data_ptr(), M, K, qs.data_ptr(), d.data_ptr(), _stream(stream))
+        _check("q8_0_repack", rc)
+    else:
+        rc = lib().q8_0_repack_layout(aos.data_ptr(), M, K, layout, qs.data_ptr(), d.data_ptr(),
+                                      _stream(stream))
+        _check("q8_0_repack_layout", rc)
 
 
 # ---------------------------------------------------------------------------

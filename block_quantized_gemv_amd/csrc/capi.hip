@@ -41,6 +41,8 @@ int check_weights_shape(const q8_0_weights* W, int64_t M, int64_t K, bool stacke
   if (!W) return Q8_ENULL;
   if (W->M != M || W->K != K || !shape_ok(M, K)) return Q8_EINVAL;
   if (W->n_mats < 1 || (!stacked && W->n_mats != 1)) return Q8_EINVAL;
+  if (W->layout != Q8_LAYOUT_ROWS && W->layout != Q8_LAYOUT_GATE_UP_PAIRS) return Q8_EINVAL;
+  if (W->layout == Q8_LAYOUT_GATE_UP_PAIRS && M % kTile) return Q8_EINVAL;
   if (W->n_mats > 1) {
     size_t qb = 0, db = 0;
     q8_0_packed_size(M, K, &qb, &db);
@@ -77,6 +79,7 @@ int build_gemv(const q8_0_weights* W, const float* x, float* y, int64_t M, int64
   pd->M = M;
   pd->y = y;
   pd->y_stride = M;
+  if (W->layout == Q8_LAYOUT_GATE_UP_PAIRS) pd->flags |= F_PAIRED;
   if (!f) return Q8_OK;
   if (N != 1) return Q8_EINVAL;
   const int ep = f->epilogue;
@@ -100,8 +103,12 @@ int build_gemv(const q8_0_weights* W, const float* x, float* y, int64_t M, int64
   }
   if (ep & Q8_EPI_SWIGLU) {
     if (ep & (Q8_EPI_RESIDUAL | Q8_EPI_ARGMAX)) return Q8_EINVAL;
-    if (M % 2 || (M / 2) % kTile) return Q8_EINVAL;
-    pd->R = 2;
+    if (W->layout == Q8_LAYOUT_GATE_UP_PAIRS) {
+      if (M % kTile) return Q8_EINVAL;
+    } else {
+      if (M % 2 || (M / 2) % kTile) return Q8_EINVAL;
+      pd->R = 2;
+    }
     pd->flags |= F_SWIGLU;
   }
   if (ep & Q8_EPI_RESIDUAL) {
@@ -123,10 +130,24 @@ int build_moe(const q8_0_weights* We, const int32_t* ids, const float* sw, const
   if (S < 1 || S > Q8_MAX_SLOTS) return Q8_EINVAL;
   if (base == Q8_MOE_SCATTER) {
     if (S + (sh ? 1 : 0) > kMaxProb) return Q8_EINVAL;
-    if (swiglu && (M % 2 || (M / 2) % kTile)) return Q8_EINVAL;
-    if (swiglu && sh && (sh->M % 2 || (sh->M / 2) % kTile)) return Q8_EINVAL;
+    // SwiGLU pairs gate and up rows: within a wave with the pairs layout,
+    // else gate tile t with up tile t + M/128
+    auto swiglu_ok = [](const q8_0_weights* w, int64_t m) {
+      return w->layout == Q8_LAYOUT_GATE_UP_PAIRS ? m % kTile == 0
+                                                  : (m % 2 == 0 && (m / 2) % kTile == 0);
+    };
+    if (swiglu && !swiglu_ok(We, M)) return Q8_EINVAL;
+    if (swiglu && sh && !swiglu_ok(sh, sh->M)) return Q8_EINVAL;
     if (sh && sh->K != K) return Q8_EINVAL;
     const int64_t Mo = swiglu ? M / 2 : M;
+    auto setup = [&](ProbDesc& p, const q8_0_weights* w, int64_t m) {
+      const bool pairs = w->layout == Q8_LAYOUT_GATE_UP_PAIRS;
+      p.R = (swiglu && !pairs) ? 2 : 1;
+      p.M = m;
+      p.flags = (swiglu ? F_SWIGLU : 0) | (pairs ? F_PAIRED : 0);
+      p.y_stride = swiglu ? m / 2 : m;
+      p.dev_status = status;
+    };
     int n = 0;
     for (int s = 0; s < S; ++s, ++n) {
       ProbDesc& p = pd[n];
@@ -135,24 +156,16 @@ int build_moe(const q8_0_weights* We, const int32_t* ids, const float* sw, const
       p.seg[0] = seg_of(We, x, K);
       p.seg[0].eid = ids;
       p.seg[0].slot = s;
-      p.R = swiglu ? 2 : 1;
-      p.M = M;
-      p.flags = swiglu ? F_SWIGLU : 0;
+      setup(p, We, M);
       p.y = y ? y + (int64_t)s * Mo : nullptr;
-      p.y_stride = Mo;
-      p.dev_status = status;
     }
     if (sh) {
       ProbDesc& p = pd[n++];
       memset(&p, 0, sizeof(p));
       p.nseg = 1;
       p.seg[0] = seg_of(sh, x, K);
-      p.R = swiglu ? 2 : 1;
-      p.M = sh->M;
-      p.flags = swiglu ? F_SWIGLU : 0;
+      setup(p, sh, sh->M);
       p.y = y ? y + (int64_t)S * Mo : nullptr;
-      p.y_stride = swiglu ? sh->M / 2 : sh->M;
-      p.dev_status = status;
     }
     *nprob = n;
     return Q8_OK;
@@ -161,6 +174,7 @@ int build_moe(const q8_0_weights* We, const int32_t* ids, const float* sw, const
     if (swiglu) return Q8_EINVAL;
     if (S + (sh ? 1 : 0) > kMaxSeg) return Q8_EINVAL;
     if (sh && sh->M != M) return Q8_EINVAL;
+    if (sh && sh->layout != We->layout) return Q8_EINVAL;  // segments share tile rows
     ProbDesc& p = pd[0];
     memset(&p, 0, sizeof(p));
     for (int s = 0; s < S; ++s) {
@@ -179,6 +193,7 @@ int build_moe(const q8_0_weights* We, const int32_t* ids, const float* sw, const
     }
     p.R = 1;
     p.M = M;
+    p.flags = We->layout == Q8_LAYOUT_GATE_UP_PAIRS ? F_PAIRED : 0;
     p.y = y;
     p.y_stride = M;
     p.dev_status = status;
@@ -209,7 +224,21 @@ int q8_0_repack(const void* aos, int64_t M, int64_t K, void* qs, void* d, void* 
   if ((rc = check_dev_aligned(aos, 2)) || (rc = check_dev_aligned(qs, 16)) ||
       (rc = check_dev_aligned(d, 8)))
     return rc;
-  return launch_repack(aos, M, K, qs, d, static_cast<hipStream_t>(stream));
+  return launch_repack(aos, M, K, Q8_LAYOUT_ROWS, qs, d, static_cast<hipStream_t>(stream));
+}
+
+int q8_0_repack_layout(const void* aos, int64_t M, int64_t K, int32_t layout, void* qs, void* d,
+                       void* stream) {
+  if (!shape_ok(M, K)) return Q8_EINVAL;
+  if (layout != Q8_LAYOUT_ROWS && layout != Q8_LAYOUT_GATE_UP_PAIRS) return Q8_EINVAL;
+  if (layout == Q8_LAYOUT_GATE_UP_PAIRS && M % kTile) return Q8_EINVAL;
+  if (!aos || !qs || !d) return Q8_ENULL;
+  if (M == 0) return Q8_OK;
+  int rc;
+  if ((rc = check_dev_aligned(aos, 2)) || (rc = check_dev_aligned(qs, 16)) ||
+      (rc = check_dev_aligned(d, 8)))
+    return rc;
+  return launch_repack(aos, M, K, layout, qs, d, static_cast<hipStream_t>(stream));
 }
 
 static int gemv_common(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,

@@ -331,8 +331,21 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const GemvParams p) {
     ss = wave_sum(ss);
     c = 1.0f / sqrtf(ss / (float)pr.rms_K + pr.eps);
   }
-  const int row = ot * kTile + lane;
-  const bool valid = row < pr.Mout;
+  // matrix row of this lane's output
+  int row = ot * kTile + lane;
+  if (pr.flags & F_PAIRED) row = lane < 32 ? 32 * ot + lane : pr.M / 2 + 32 * ot + (lane - 32);
+  bool valid = row < pr.Mout;
+  if ((pr.flags & (F_PAIRED | F_SWIGLU)) == (F_PAIRED | F_SWIGLU)) {
+    // lanes 0..31 hold gate rows, lanes 32..63 the matching up rows
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const float v = val[0][n] * c;
+      const float up = __shfl(v, (lane + 32) & 63, 64);
+      const float h = v / (1.0f + expf(-v)) * up;
+      if (lane < 32 && valid) pr.y[n * pr.y_stride + row] = h;
+    }
+    return;
+  }
   if (pr.R == 2) {
 #pragma unroll
     for (int n = 0; n < N; ++n) {
@@ -479,14 +492,21 @@ void distribute(const ProbDesc& pd, int64_t us, int64_t blocks, int64_t* su) {
 
 }  // namespace
 
+// Output rows and output tiles of a problem.
+static int64_t prob_mout(const ProbDesc& pd) {
+  return (pd.R == 2 || (pd.flags & F_SWIGLU)) ? pd.M / 2 : pd.M;
+}
+static int64_t prob_tout(const ProbDesc& pd) {
+  return (pd.flags & F_PAIRED) ? cdiv(pd.M, kTile) : cdiv(prob_mout(pd), kTile);
+}
+
 int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
   memset(plan, 0, sizeof(*plan));
   int64_t total_tout = 0;
   int segc = 0;
   for (int i = 0; i < nprob; ++i) {
     const ProbDesc& pd = probs[i];
-    const int64_t Mout = pd.R == 2 ? pd.M / 2 : pd.M;
-    total_tout += cdiv(Mout, kTile);
+    total_tout += prob_tout(pd);
     segc += pd.nseg;
   }
   if (segc > kMaxSeg || nprob > kMaxProb || total_tout <= 0) return Q8_EINVAL;
@@ -529,8 +549,7 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
   int64_t wg = 0;
   for (int i = 0; i < nprob; ++i) {
     const ProbDesc& pd = probs[i];
-    const int64_t Mout = pd.R == 2 ? pd.M / 2 : pd.M;
-    const int64_t Tout = cdiv(Mout, kTile);
+    const int64_t Tout = prob_tout(pd);
     const int64_t P = cdiv(U[i], W);
     plan->U[i] = (int32_t)U[i];
     plan->P[i] = (int32_t)P;
@@ -572,8 +591,8 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
   for (int i = 0; i < nprob; ++i) {
     const ProbDesc& pd = probs[i];
     Prob& pr = gp.prob[i];
-    const int64_t Mout = pd.R == 2 ? pd.M / 2 : pd.M;
-    const int64_t Tout = cdiv(Mout, kTile);
+    const int64_t Mout = prob_mout(pd);
+    const int64_t Tout = prob_tout(pd);
     pr.seg0 = sbase;
     pr.nseg = pd.nseg;
     pr.R = pd.R;

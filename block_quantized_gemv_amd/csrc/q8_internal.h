@@ -26,7 +26,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Problem flags (the epilogue/prologue work of one problem).
-enum : int32_t { F_RMSNORM = 1, F_RESIDUAL = 2, F_SWIGLU = 4, F_ARGMAX = 8 };
+enum : int32_t { F_RMSNORM = 1, F_RESIDUAL = 2, F_SWIGLU = 4, F_ARGMAX = 8, F_PAIRED = 16 };
 // How a segment's partial sum is weighted in the fold.
 enum : int32_t { A_ONE = 0, A_PTR = 1, A_SIGMOID = 2 };
 
@@ -54,7 +54,9 @@ struct Seg {
 };
 
 // One problem: an output of Mout rows computed from R row-tiles per output
-// tile (R = 2 pairs the gate tile t with the up tile t + Tout).
+// tile (R = 2 pairs the gate tile t with the up tile t + Tout).  F_PAIRED:
+// the matrix uses the gate/up pairs layout (R = 1; lanes 0..31 gate rows,
+// 32..63 the matching up rows).
 struct Prob {
   int32_t seg0, nseg;
   int32_t R;
@@ -138,7 +140,8 @@ int launch_argmax(const float* v, int64_t n, int32_t* out, void* ws, size_t ws_b
                   hipStream_t stream);
 int launch_route(const float* logits, int32_t E, int32_t k, int32_t* ids, float* w,
                  hipStream_t stream);
-int launch_repack(const void* aos, int64_t M, int64_t K, void* qs, void* d, hipStream_t stream);
+int launch_repack(const void* aos, int64_t M, int64_t K, int32_t layout, void* qs, void* d,
+                  hipStream_t stream);
 
 // ---- data exchanged between workgroups of one launch ------------------------
 // The 8 XCDs of an MI355X each have their own L2, not coherent with the

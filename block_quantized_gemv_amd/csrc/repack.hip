@@ -9,13 +9,21 @@
 //       rows back to back (1 KiB per chunk per tile);
 //   d:  per 64-row tile, per quad of 4 blocks, the 4 scales of each of the 64
 //       rows back to back (512 B per quad per tile).
-// Padding rows and blocks are written as zeros.
+// Padding rows and blocks are written as zeros.  With the gate/up pairs layout
+// packed row 64t + i holds matrix row 32t + i (i < 32) or M/2 + 32t + i - 32.
 #include "q8_internal.h"
 
 namespace q8 {
 
+// Matrix row held by packed row p.
+__device__ __forceinline__ int64_t src_row(int64_t p, int64_t M, int32_t layout) {
+  if (layout != Q8_LAYOUT_GATE_UP_PAIRS) return p;
+  const int64_t t = p >> 6, i = p & 63;
+  return i < 32 ? 32 * t + i : M / 2 + 32 * t + (i - 32);
+}
+
 __global__ __launch_bounds__(256) void repack_qs_kernel(const uint16_t* __restrict__ aos16,
-                                                        int64_t M, int64_t K,
+                                                        int64_t M, int64_t K, int32_t layout,
                                                         u32x4* __restrict__ qs, int64_t total) {
   const int64_t nchunk = K / 16;
   const int64_t nb = K / 32;
@@ -24,9 +32,10 @@ __global__ __launch_bounds__(256) void repack_qs_kernel(const uint16_t* __restri
     const int64_t lane = idx & 63;
     const int64_t c = (idx >> 6) % nchunk;
     const int64_t t = (idx >> 6) / nchunk;
-    const int64_t r = t * 64 + lane;
+    const int64_t pr = t * 64 + lane;
+    const int64_t r = src_row(pr, M, layout);
     u32x4 out = {0u, 0u, 0u, 0u};
-    if (r < M) {
+    if (pr < M) {
       // quants of block c/2 start 1 uint16 after the block's scale
       const uint16_t* src = aos16 + (r * nb + c / 2) * 17 + 1 + (c & 1) * 8;
       uint32_t w[4];
@@ -39,7 +48,7 @@ __global__ __launch_bounds__(256) void repack_qs_kernel(const uint16_t* __restri
 }
 
 __global__ __launch_bounds__(256) void repack_d_kernel(const uint16_t* __restrict__ aos16,
-                                                       int64_t M, int64_t K,
+                                                       int64_t M, int64_t K, int32_t layout,
                                                        u32x2* __restrict__ d, int64_t total) {
   const int64_t nb = K / 32;
   const int64_t G = (nb + 3) / 4;
@@ -48,27 +57,29 @@ __global__ __launch_bounds__(256) void repack_d_kernel(const uint16_t* __restric
     const int64_t lane = idx & 63;
     const int64_t g = (idx >> 6) % G;
     const int64_t t = (idx >> 6) / G;
-    const int64_t r = t * 64 + lane;
+    const int64_t pr = t * 64 + lane;
+    const int64_t r = src_row(pr, M, layout);
     uint32_t bits[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t b = 4 * g + j;
-      bits[j] = (r < M && b < nb) ? aos16[(r * nb + b) * 17] : 0u;
+      bits[j] = (pr < M && b < nb) ? aos16[(r * nb + b) * 17] : 0u;
     }
     d[idx] = u32x2{bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
   }
 }
 
-int launch_repack(const void* aos, int64_t M, int64_t K, void* qs, void* d, hipStream_t stream) {
+int launch_repack(const void* aos, int64_t M, int64_t K, int32_t layout, void* qs, void* d,
+                  hipStream_t stream) {
   const int64_t T = cdiv(M, kTile);
   const int64_t nq = T * 64 * (K / 16);
   const int64_t nd = T * 64 * cdiv(K / 32, 4);
   const auto* a16 = static_cast<const uint16_t*>(aos);
   auto grid = [](int64_t n) { return (unsigned)(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536); };
-  hipLaunchKernelGGL(repack_qs_kernel, dim3(grid(nq)), dim3(256), 0, stream, a16, M, K,
+  hipLaunchKernelGGL(repack_qs_kernel, dim3(grid(nq)), dim3(256), 0, stream, a16, M, K, layout,
                      static_cast<u32x4*>(qs), nq);
   if (hipGetLastError() != hipSuccess) return Q8_ELAUNCH;
-  hipLaunchKernelGGL(repack_d_kernel, dim3(grid(nd)), dim3(256), 0, stream, a16, M, K,
+  hipLaunchKernelGGL(repack_d_kernel, dim3(grid(nd)), dim3(256), 0, stream, a16, M, K, layout,
                      static_cast<u32x2*>(d), nd);
   return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
 }

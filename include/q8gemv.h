@@ -91,7 +91,19 @@ typedef struct {
   int64_t n_mats;    /* stacked matrices (experts); 1 for a dense matrix */
   int64_t qs_stride; /* bytes from one matrix's qs to the next (>= packed qs size) */
   int64_t d_stride;  /* bytes from one matrix's d to the next */
+  int32_t layout;    /* Q8_LAYOUT_ROWS or Q8_LAYOUT_GATE_UP_PAIRS (how it was repacked) */
+  int32_t reserved;  /* 0 */
 } q8_0_weights;
+
+/* Row order inside the packed tiles.
+ *  Q8_LAYOUT_ROWS: packed row r is matrix row r.
+ *  Q8_LAYOUT_GATE_UP_PAIRS: for a fused gate/up matrix (rows 0..M/2-1 gate,
+ *    M/2..M-1 up; M % 64 == 0), lanes 0..31 of tile t hold gate rows
+ *    32t..32t+31 and lanes 32..63 the matching up rows M/2+32t..M/2+32t+31,
+ *    so a SwiGLU epilogue pairs rows within one wave and every tile yields 32
+ *    outputs.  GEMV outputs are still written in matrix row order. */
+#define Q8_LAYOUT_ROWS 0
+#define Q8_LAYOUT_GATE_UP_PAIRS 1
 
 /* Bytes of the packed quants and scales of one M x K matrix.
  * Errors: Q8_EINVAL (M < 0, K <= 0, K % 32, K > Q8_MAX_K), Q8_ENULL. */
@@ -104,6 +116,12 @@ int q8_0_packed_size(int64_t M, int64_t K, size_t* qs_bytes, size_t* d_bytes);
  *  every byte, padding included, is written.
  * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_ELAUNCH. */
 int q8_0_repack(const void* aos, int64_t M, int64_t K, void* qs, void* d, void* stream);
+
+/* The same with a row order: layout Q8_LAYOUT_ROWS (as q8_0_repack) or
+ * Q8_LAYOUT_GATE_UP_PAIRS (M % 64 == 0).  Set the descriptor's `layout` to
+ * the same value.  Errors as q8_0_repack. */
+int q8_0_repack_layout(const void* aos, int64_t M, int64_t K, int32_t layout, void* qs, void* d,
+                       void* stream);
 
 /* ---- GEMV ------------------------------------------------------------------
  * y[n][r] = sum_k w[r][k] * x[n][k],  n < N, r < M.
@@ -131,8 +149,9 @@ int q8_0_gemv(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_
  *      a[h*hd + j] = x[gqa_offset + (h / (n_heads/n_kv_heads)) * hd + j],
  *      K == n_heads * hd, hd % 32 == 0 (with one key the softmax weight is 1,
  *      so each query head returns its key/value head's value vector).
- *  epilogue Q8_EPI_SWIGLU: M even, (M/2) % 64 == 0; rows 0..M/2-1 are gate,
- *      M/2..M-1 up; y gets M/2 values silu(g) * u, silu(z) = z/(1+e^-z).
+ *  epilogue Q8_EPI_SWIGLU: rows 0..M/2-1 are gate, M/2..M-1 up; y gets M/2
+ *      values silu(g) * u, silu(z) = z/(1+e^-z).  Needs M % 64 == 0 with the
+ *      Q8_LAYOUT_GATE_UP_PAIRS layout, else (M/2) % 64 == 0.
  *  epilogue Q8_EPI_RESIDUAL: y[r] = residual[r] + (W a)[r]; residual may be y
  *      itself (in-place h += W a).
  *  epilogue Q8_EPI_ARGMAX: also writes to *argmax_out the lowest index of the

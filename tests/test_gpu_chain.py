@@ -32,7 +32,7 @@ def silu_prime(g):
     return s * (1.0 + g * (1.0 - s))
 
 
-def make_layers(cfg_id, cfg: ChainConfig, n_layers):
+def make_layers(cfg_id, cfg: ChainConfig, n_layers, layout=q.Q8_LAYOUT_GATE_UP_PAIRS):
     shapes = {W.MAT_QKV: (cfg.qkv_rows, cfg.hidden), W.MAT_WO: (cfg.hidden, cfg.hidden),
               W.MAT_GATE_UP: (2 * cfg.intermediate, cfg.hidden),
               W.MAT_DOWN: (cfg.hidden, cfg.intermediate)}
@@ -42,12 +42,14 @@ def make_layers(cfg_id, cfg: ChainConfig, n_layers):
         mats = W.layer_matrices(cfg_id, l, shapes)
         a = {names[k]: m.aos() for k, m in mats.items()}
         aos.append(a)
-        packed.append({k: pack(v) for k, v in a.items()})
+        packed.append({k: pack(v, layout=layout if k == "gate_up" else q.Q8_LAYOUT_ROWS)
+                       for k, v in a.items()})
     return aos, packed
 
 
-def stagewise(cfg: ChainConfig, n_layers, vocab_rows=None, cfg_id=2):
-    aos, packed = make_layers(cfg_id, cfg, n_layers)
+def stagewise(cfg: ChainConfig, n_layers, vocab_rows=None, cfg_id=2,
+              layout=q.Q8_LAYOUT_GATE_UP_PAIRS):
+    aos, packed = make_layers(cfg_id, cfg, n_layers, layout)
     lm = W.matrix(cfg_id, 0, W.MAT_LM_HEAD, cfg.vocab, cfg.hidden)
     chain = DecodeChain(cfg, packed, pack(lm))
     h0 = W.activations(cfg_id, 1, cfg.hidden)[0]
@@ -96,8 +98,9 @@ def stagewise(cfg: ChainConfig, n_layers, vocab_rows=None, cfg_id=2):
     return chain
 
 
-def test_chain_two_layers_stagewise():
-    stagewise(ChainConfig(), 2)
+@pytest.mark.parametrize("layout", [q.Q8_LAYOUT_ROWS, q.Q8_LAYOUT_GATE_UP_PAIRS])
+def test_chain_two_layers_stagewise(layout):
+    stagewise(ChainConfig(), 2, layout=layout)
 
 
 def test_chain_small_config_stagewise():

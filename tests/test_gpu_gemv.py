@@ -173,3 +173,47 @@ def test_one_workspace_serves_interleaved_shapes():
             assert int(host(out)[0]) == int(np.argmax(v))
     # every counter is back at zero
     assert int(ws[:65536].view(torch.int32).abs().sum().item()) == 0
+
+
+@pytest.mark.parametrize("M,K", [(64, 96), (128, 896), (9728, 896), (2816, 2048)])
+def test_repack_gate_up_pairs_layout_bit_exact(M, K):
+    m = W.draw_matrix(W.rng(11, M, K), M, K)
+    p = pack(m, layout=q.Q8_LAYOUT_GATE_UP_PAIRS)
+    eq, ed = expected_packed(m.qs, m.d, q.Q8_LAYOUT_GATE_UP_PAIRS)
+    assert np.array_equal(host(p.qs), eq)
+    assert np.array_equal(host(p.d), ed)
+
+
+@pytest.mark.parametrize("M,K,N", [(128, 96, 1), (9728, 896, 1), (640, 2048, 3)])
+def test_gemv_on_pairs_layout_writes_row_order(M, K, N):
+    g = W.rng(27, M, K)
+    m = W.draw_matrix(g, M, K)
+    x = W.draw_x(g, N, K)
+    y = host(q.q8_0_gemv(pack(m, layout=q.Q8_LAYOUT_GATE_UP_PAIRS), to_dev(x)))
+    yr, S = oracle.gemv(m.aos(), x)
+    q8tol.check(y, yr, S, f"pairs layout {M}x{K} N={N}")
+
+
+@pytest.mark.parametrize("M,K", [(128, 96), (9728, 896), (2816, 2048), (192, 64)])
+def test_fused_rmsnorm_swiglu_pairs_layout(M, K):
+    """SwiGLU epilogue on the gate/up pairs layout against the oracle: gate and
+    up rows each within the GEMV tolerance plus the fp32 RMS scale's rounding,
+    propagated to first order through silu(g)*u."""
+    U = 2.0 ** -24
+    g = W.rng(28, M, K)
+    m = W.draw_matrix(g, M, K)
+    x = W.draw_x(g, 1, K)[0]
+    I = M // 2
+    y = torch.empty(I, dtype=torch.float32, device=DEV)
+    f = q.make_fusion(prologue=q.Q8_PRO_RMSNORM, epilogue=q.Q8_EPI_SWIGLU, eps=1e-6)
+    q.q8_0_gemv_fused(pack(m, layout=q.Q8_LAYOUT_GATE_UP_PAIRS), to_dev(x), y, f)
+    gu, S = oracle.gemv(m.aos(), oracle.rmsnorm(x.astype(np.float64), 1e-6))
+    gr, ur = gu[:I], gu[I:]
+    tg = q8tol.bound(S[:I]) + 34 * U * np.abs(gr)
+    tu = q8tol.bound(S[I:]) + 34 * U * np.abs(ur)
+    sg = 1.0 / (1.0 + np.exp(-gr))
+    sil = gr * sg
+    b = (np.abs(sg * (1.0 + gr * (1.0 - sg))) * np.abs(ur) * tg + (np.abs(sil) + 1.2 * tg) * tu
+         + 0.5 * tg * tg * np.abs(ur) + 8 * U * np.abs(sil * ur))
+    err = np.abs(host(y).astype(np.float64) - oracle.swiglu(gr, ur))
+    assert np.all(err <= b), float((err / b).max())

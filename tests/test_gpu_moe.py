@@ -31,15 +31,15 @@ def swiglu_bound(g_ref, u_ref, Sg, Su):
 
 
 class MoE:
-    def __init__(self, cfg, E, H, I, Ish, S=4):
+    def __init__(self, cfg, E, H, I, Ish, S=4, layout=q.Q8_LAYOUT_ROWS):
         self.E, self.H, self.I, self.Ish, self.S = E, H, I, Ish, S
         self.gu = W.expert_stack(cfg, W.MAT_GATE_UP, E, 2 * I, H)
         self.dn = W.expert_stack(cfg, W.MAT_DOWN, E, H, I)
         self.sgu = W.matrix(cfg, 0, W.MAT_SHARED_GU, 2 * Ish, H).aos()
         self.sdn = W.matrix(cfg, 0, W.MAT_SHARED_DOWN, H, Ish).aos()
-        self.p_gu = pack(self.gu, 2 * I, H, n_mats=E)
+        self.p_gu = pack(self.gu, 2 * I, H, n_mats=E, layout=layout)
         self.p_dn = pack(self.dn, H, I, n_mats=E)
-        self.p_sgu = pack(self.sgu)
+        self.p_sgu = pack(self.sgu, layout=layout)
         self.p_sdn = pack(self.sdn)
         self.cfg = cfg
 
@@ -106,16 +106,21 @@ def run_stagewise(moe: MoE, token: int):
     return ids, w, h, y
 
 
-def test_moe_small_stagewise():
-    moe = MoE(cfg=50, E=8, H=256, I=128, Ish=192)
+LAYOUTS = [q.Q8_LAYOUT_ROWS, q.Q8_LAYOUT_GATE_UP_PAIRS]
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_moe_small_stagewise(layout):
+    moe = MoE(cfg=50, E=8, H=256, I=128, Ish=192, layout=layout)
     for token in range(4):
         run_stagewise(moe, token)
 
 
-def test_moe_qwen15_shapes_stagewise():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_moe_qwen15_shapes_stagewise(layout):
     c = W.C5
     moe = MoE(cfg=c["cfg"], E=c["n_experts"], H=c["hidden"], I=c["inter"], Ish=c["shared_inter"],
-              S=c["top_k"])
+              S=c["top_k"], layout=layout)
     for token in range(2):
         run_stagewise(moe, token)
 
