@@ -26,10 +26,12 @@ Q8_MOE_SCATTER, Q8_MOE_COMBINE, Q8_MOE_SWIGLU = 1, 2, 4
 Q8_OP_GEMV, Q8_OP_GEMV_FUSED, Q8_OP_ARGMAX, Q8_OP_MOE_SCATTER, Q8_OP_MOE_COMBINE = 1, 2, 3, 4, 5
 
 Q8_LAYOUT_ROWS, Q8_LAYOUT_GATE_UP_PAIRS = 0, 1
+Q8_CHAIN_QKV, Q8_CHAIN_H_ATTN, Q8_CHAIN_SWIGLU, Q8_CHAIN_H_OUT = 0, 1, 2, 3
 
 EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv", "q8_0_gemv_fused", "q8_0_argmax",
            "q8_0_route_topk", "q8_0_moe_gemv", "q8_0_workspace_bytes", "q8_0_gemv_plan",
-           "q8_0_strerror", "q8_0_version")
+           "q8_0_strerror", "q8_0_version", "q8_0_chain_workspace_bytes", "q8_0_chain_prepare",
+           "q8_0_chain_run", "q8_0_chain_read", "q8_0_chain_status")
 
 
 class Q8Error(RuntimeError):
@@ -51,6 +53,29 @@ class q8_0_fusion(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("gqa_offset", ctypes.c_int64), ("residual", ctypes.c_void_p),
                 ("argmax_out", ctypes.c_void_p)]
+
+
+class q8_0_chain_desc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("intermediate", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("eps", ctypes.c_float),
+                ("qkv", ctypes.POINTER(q8_0_weights)), ("wo", ctypes.POINTER(q8_0_weights)),
+                ("gate_up", ctypes.POINTER(q8_0_weights)), ("down", ctypes.POINTER(q8_0_weights)),
+                ("lm_head", ctypes.POINTER(q8_0_weights))]
+
+
+class q8_0_chain_plan(ctypes.Structure):
+    _fields_ = [("grid", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("intermediate", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("ws_bytes", ctypes.c_int64), ("off", ctypes.c_int64 * 4),
+                ("layer_stride", ctypes.c_int64), ("am_off", ctypes.c_int64),
+                ("lm_qs", ctypes.c_void_p), ("lm_d", ctypes.c_void_p),
+                ("len", ctypes.c_int32 * 4)]
 
 
 _lib = None
@@ -80,6 +105,13 @@ def lib() -> ctypes.CDLL:
         L.q8_0_strerror.argtypes = [ctypes.c_int]
         L.q8_0_strerror.restype = ctypes.c_char_p
         L.q8_0_version.argtypes = []
+        PD, PP = ctypes.POINTER(q8_0_chain_desc), ctypes.POINTER(q8_0_chain_plan)
+        L.q8_0_chain_workspace_bytes.argtypes = [PD]
+        L.q8_0_chain_workspace_bytes.restype = SZ
+        L.q8_0_chain_prepare.argtypes = [PD, P, SZ, PP, P]
+        L.q8_0_chain_run.argtypes = [PP, P, P, P, P, P, P]
+        L.q8_0_chain_read.argtypes = [PP, P, I32, I32, P, P]
+        L.q8_0_chain_status.argtypes = [P, P, P]
         _lib = L
     return _lib
 
@@ -315,3 +347,63 @@ def q8_0_moe_gemv(W_experts: PackedQ8, expert_ids: torch.Tensor, slot_weights, x
         dev_status.data_ptr() if dev_status is not None else None, wsp, wsb, _stream(stream))
     _check("q8_0_moe_gemv", rc)
     return y
+
+
+# ---------------------------------------------------------------------------
+# Persistent decode chain: one launch per decode step
+# ---------------------------------------------------------------------------
+class PersistentChain:
+    """A whole decode step (n_layers Qwen2-style layers + LM head + argmax) in
+    one kernel launch; see q8_0_chain_prepare in include/q8gemv.h.  `layers`
+    is a list of dicts of PackedQ8 with keys qkv, wo, gate_up (gate/up pairs
+    layout) and down; `lm_head` a PackedQ8 or None."""
+
+    def __init__(self, layers: list, lm_head, hidden: int, n_heads: int, n_kv_heads: int,
+                 head_dim: int, intermediate: int, eps: float, stream=None):
+        n = len(layers)
+        self.layers, self.lm_head = layers, lm_head
+        arr = lambda k: (q8_0_weights * max(n, 1))(*[L[k].desc for L in layers])
+        self._arrays = {k: arr(k) for k in ("qkv", "wo", "gate_up", "down")}
+        self._lm = lm_head.desc if lm_head is not None else None
+        self.desc = q8_0_chain_desc(
+            n, hidden, n_heads, n_kv_heads, head_dim, intermediate,
+            lm_head.M if lm_head is not None else 0, eps,
+            self._arrays["qkv"], self._arrays["wo"], self._arrays["gate_up"],
+            self._arrays["down"], ctypes.pointer(self._lm) if self._lm is not None else None)
+        nbytes = int(lib().q8_0_chain_workspace_bytes(ctypes.byref(self.desc)))
+        if nbytes == 0:
+            raise Q8Error("q8_0_chain_workspace_bytes", Q8_EINVAL)
+        dev = layers[0]["qkv"].qs.device if n else lm_head.qs.device
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.plan = q8_0_chain_plan()
+        _check("q8_0_chain_prepare",
+               lib().q8_0_chain_prepare(ctypes.byref(self.desc), self.ws.data_ptr(), nbytes,
+                                        ctypes.byref(self.plan), _stream(stream)))
+        self.hidden, self.vocab = hidden, self.desc.vocab
+
+    def run(self, h_in: torch.Tensor, logits: torch.Tensor | None = None,
+            next_token: torch.Tensor | None = None, h_out: torch.Tensor | None = None,
+            stream=None) -> None:
+        _need(h_in, torch.float32, "h_in")
+        for t, name, dt in ((logits, "logits", torch.float32),
+                            (next_token, "next_token", torch.int32),
+                            (h_out, "h_out", torch.float32)):
+            if t is not None:
+                _need(t, dt, name)
+        ptr = lambda t: t.data_ptr() if t is not None else None
+        _check("q8_0_chain_run",
+               lib().q8_0_chain_run(ctypes.byref(self.plan), self.ws.data_ptr(), h_in.data_ptr(),
+                                    ptr(h_out), ptr(logits), ptr(next_token), _stream(stream)))
+
+    def read(self, layer: int, which: int, stream=None) -> torch.Tensor:
+        out = torch.empty(self.plan.len[which], dtype=torch.float32, device=self.ws.device)
+        _check("q8_0_chain_read",
+               lib().q8_0_chain_read(ctypes.byref(self.plan), self.ws.data_ptr(), layer, which,
+                                     out.data_ptr(), _stream(stream)))
+        return out
+
+    def status(self, stream=None) -> int:
+        out = torch.zeros(1, dtype=torch.int32, device=self.ws.device)
+        _check("q8_0_chain_status",
+               lib().q8_0_chain_status(self.ws.data_ptr(), out.data_ptr(), _stream(stream)))
+        return int(out.cpu()[0])

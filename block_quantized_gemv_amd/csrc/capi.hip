@@ -388,6 +388,91 @@ int q8_0_gemv_plan(int64_t M, int64_t K, int64_t N, int32_t epilogue, int32_t ou
   return Q8_OK;
 }
 
+// ---- persistent decode chain ------------------------------------------------
+namespace {
+int check_chain_desc(const q8_0_chain_desc* c, bool ptrs) {
+  if (!c) return Q8_ENULL;
+  if (q8::chain_ws_bytes(c) == 0) return Q8_EINVAL;
+  const int64_t H = c->hidden, I = c->intermediate, NHD = (int64_t)c->n_heads * c->head_dim;
+  const int64_t Mq = ((int64_t)c->n_heads + 2 * (int64_t)c->n_kv_heads) * c->head_dim;
+  if (c->n_layers > 0 && (!c->qkv || !c->wo || !c->gate_up || !c->down)) return Q8_ENULL;
+  for (int l = 0; l < c->n_layers; ++l) {
+    const q8_0_weights* m[4] = {&c->qkv[l], &c->wo[l], &c->gate_up[l], &c->down[l]};
+    const int64_t shp[4][2] = {{Mq, H}, {H, NHD}, {2 * I, H}, {H, I}};
+    for (int k = 0; k < 4; ++k) {
+      int rc = check_weights_shape(m[k], shp[k][0], shp[k][1], false);
+      if (rc) return rc;
+      if (m[k]->layout != (k == 2 ? Q8_LAYOUT_GATE_UP_PAIRS : Q8_LAYOUT_ROWS)) return Q8_EINVAL;
+      if (ptrs && (rc = check_weights_ptrs(m[k]))) return rc;
+    }
+  }
+  if (c->vocab > 0) {
+    if (!c->lm_head) return Q8_ENULL;
+    int rc = check_weights_shape(c->lm_head, c->vocab, H, false);
+    if (rc) return rc;
+    if (c->lm_head->layout != Q8_LAYOUT_ROWS) return Q8_EINVAL;
+    if (ptrs && (rc = check_weights_ptrs(c->lm_head))) return rc;
+  } else if (c->lm_head) {
+    return Q8_EINVAL;
+  }
+  return Q8_OK;
+}
+
+bool plan_ok(const q8_0_chain_plan* p) {
+  return p->grid > 0 && p->threads > 0 && p->n_layers >= 0 && p->hidden > 0 && p->vocab >= 0 &&
+         p->ws_bytes > 0;
+}
+}  // namespace
+
+size_t q8_0_chain_workspace_bytes(const q8_0_chain_desc* desc) {
+  if (check_chain_desc(desc, false)) return 0;
+  return q8::chain_ws_bytes(desc);
+}
+
+int q8_0_chain_prepare(const q8_0_chain_desc* desc, void* workspace, size_t workspace_bytes,
+                       q8_0_chain_plan* plan, void* stream) {
+  if (!plan) return Q8_ENULL;
+  int rc = check_chain_desc(desc, false);
+  if (rc) return rc;
+  if ((rc = check_dev_aligned(workspace, 256))) return rc;
+  if (workspace_bytes < q8::chain_ws_bytes(desc)) return Q8_EWORKSPACE;
+  if ((rc = check_chain_desc(desc, true))) return rc;
+  return q8::chain_prepare(desc, workspace, workspace_bytes, plan, (hipStream_t)stream);
+}
+
+int q8_0_chain_run(const q8_0_chain_plan* plan, void* workspace, const float* h_in, float* h_out,
+                   float* logits, int32_t* next_token, void* stream) {
+  if (!plan) return Q8_ENULL;
+  if (!plan_ok(plan)) return Q8_EINVAL;
+  int rc = check_dev_aligned(workspace, 256);
+  if (rc) return rc;
+  if ((rc = check_dev_aligned(h_in, 4))) return rc;
+  if (h_out && (rc = check_dev_aligned(h_out, 4))) return rc;
+  if (plan->vocab > 0) {
+    if ((rc = check_dev_aligned(logits, 4))) return rc;
+    if ((rc = check_dev_aligned(next_token, 4))) return rc;
+  }
+  return q8::chain_run(plan, workspace, h_in, h_out, logits, next_token, (hipStream_t)stream);
+}
+
+int q8_0_chain_read(const q8_0_chain_plan* plan, const void* workspace, int32_t layer,
+                    int32_t which, float* dst, void* stream) {
+  if (!plan) return Q8_ENULL;
+  if (!plan_ok(plan) || which < 0 || which > 3 || layer < 0 || layer >= plan->n_layers)
+    return Q8_EINVAL;
+  int rc = check_dev_aligned(workspace, 256);
+  if (rc) return rc;
+  if ((rc = check_dev_aligned(dst, 4))) return rc;
+  return q8::chain_read(plan, workspace, layer, which, dst, (hipStream_t)stream);
+}
+
+int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream) {
+  int rc = check_dev_aligned(workspace, 256);
+  if (rc) return rc;
+  if ((rc = check_dev_aligned(dev_status, 4))) return rc;
+  return q8::chain_status(workspace, dev_status, (hipStream_t)stream);
+}
+
 const char* q8_0_strerror(int status) {
   switch (status) {
     case Q8_OK: return "ok";

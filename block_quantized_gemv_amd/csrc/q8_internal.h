@@ -143,6 +143,16 @@ int launch_route(const float* logits, int32_t E, int32_t k, int32_t* ids, float*
 int launch_repack(const void* aos, int64_t M, int64_t K, int32_t layout, void* qs, void* d,
                   hipStream_t stream);
 
+// persistent decode chain (chain.hip); arguments validated by the C entry points
+size_t chain_ws_bytes(const q8_0_chain_desc* c);
+int chain_prepare(const q8_0_chain_desc* c, void* ws, size_t ws_bytes, q8_0_chain_plan* plan,
+                  hipStream_t stream);
+int chain_run(const q8_0_chain_plan* plan, void* ws, const float* h_in, float* h_out,
+              float* logits, int32_t* next_token, hipStream_t stream);
+int chain_read(const q8_0_chain_plan* plan, const void* ws, int32_t layer, int32_t which,
+               float* dst, hipStream_t stream);
+int chain_status(const void* ws, int32_t* out, hipStream_t stream);
+
 // ---- data exchanged between workgroups of one launch ------------------------
 // The 8 XCDs of an MI355X each have their own L2, not coherent with the
 // others; an agent-scope fence writes back and invalidates a whole L2, which

@@ -229,6 +229,113 @@ int q8_0_moe_gemv(const q8_0_weights* W_experts, const int32_t* expert_ids,
                   const float* shared_gate, int32_t* dev_status, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* ---- persistent decode chain --------------------------------------------------
+ * One launch runs a whole decode step of a Qwen2-style decoder at position 0,
+ * the per-layer steps of the fused GEMVs above in the decoder block order of
+ * the "augur" README ("Features": RMSNorm, grouped-query attention, SwiGLU
+ * MLP, residuals), unit norm weights and no biases.  For each layer l:
+ *     a = rmsnorm(h);  qkv = Wqkv_l a;            (q, k, v rows in that order)
+ *     h = h + Wo_l gqa(v);                        (position 0: head i reads
+ *                                                  value head i / (n_heads/n_kv_heads))
+ *     a = rmsnorm(h);  s = silu(g) * u, [g; u] = Wgu_l a;
+ *     h = h + Wdown_l s;
+ * then logits = Wlm rmsnorm(h) and *next_token = the lowest index of the
+ * largest logit.  Each projection's output agrees with the exact product of
+ * its own fp32 input within 2e-5 * sum_k |w_k a_k| + 1e-6 (plus a few ulps
+ * of the RMS scale); repeated runs are bitwise identical.
+ *
+ * The launch keeps one workgroup resident on every compute unit for the whole
+ * step and hands activations between projections through the workspace, so
+ * the caller must not run other work that occupies the whole device
+ * concurrently with it (it would only be slower; every wait in the kernel is
+ * bounded and an expired wait sets bit 1 of the status word).
+ *
+ * Limits: hidden, n_heads*head_dim and intermediate are multiples of 32 and
+ * at most 5376; n_heads % n_kv_heads == 0; head_dim % 16 == 0.  Weights: qkv_l
+ * ((n_heads + 2 n_kv_heads) head_dim x hidden), wo_l (hidden x
+ * n_heads*head_dim) and down_l (hidden x intermediate) in Q8_LAYOUT_ROWS;
+ * gate_up_l (2 intermediate x hidden, gate rows first) in
+ * Q8_LAYOUT_GATE_UP_PAIRS; lm_head (vocab x hidden) in Q8_LAYOUT_ROWS, or
+ * NULL with vocab == 0 (no LM head: the step ends with the last layer). */
+typedef struct {
+  int32_t n_layers;
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t intermediate;
+  int32_t vocab;
+  float eps;                    /* RMSNorm epsilon */
+  const q8_0_weights* qkv;      /* host arrays of n_layers descriptors each */
+  const q8_0_weights* wo;
+  const q8_0_weights* gate_up;
+  const q8_0_weights* down;
+  const q8_0_weights* lm_head;  /* one descriptor, or NULL */
+} q8_0_chain_desc;
+
+/* Filled by q8_0_chain_prepare; passed unchanged to the other chain calls
+ * (it holds the launch configuration, so a run needs no device reads). */
+typedef struct {
+  int32_t grid;          /* workgroups of the launch (one per compute unit) */
+  int32_t threads;       /* threads per workgroup */
+  int32_t lds_bytes;     /* dynamic LDS per workgroup */
+  int32_t n_layers;
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t intermediate;
+  int32_t vocab;
+  float eps;
+  int32_t reserved;
+  int64_t ws_bytes;      /* workspace bytes in use */
+  int64_t off[4];        /* workspace offsets of layer 0's four activation records */
+  int64_t layer_stride;  /* bytes between layers' records */
+  int64_t am_off;        /* workspace offset of the per-workgroup argmax partials */
+  const void* lm_qs;     /* LM head weights (NULL without LM head) */
+  const void* lm_d;
+  int32_t len[4];        /* entries of the four records */
+} q8_0_chain_plan;
+
+/* Workspace bytes for a chain (0 if the description is invalid). */
+size_t q8_0_chain_workspace_bytes(const q8_0_chain_desc* desc);
+
+/* Validates the description and weight pointers, writes the chain's tables
+ * into the workspace (device memory, 256-byte aligned, at least
+ * q8_0_chain_workspace_bytes), clears its records and fills *plan.  Set-up
+ * call: it synchronises `stream` before returning.  The weights must stay
+ * allocated, and the workspace dedicated to this chain, while it is used.
+ * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_EWORKSPACE,
+ * Q8_ELAUNCH. */
+int q8_0_chain_prepare(const q8_0_chain_desc* desc, void* workspace, size_t workspace_bytes,
+                       q8_0_chain_plan* plan, void* stream);
+
+/* One decode step: one kernel launch on `stream` (capturable).
+ *  h_in: device fp32 [hidden], the residual stream entering layer 0.
+ *  h_out: device fp32 [hidden] or NULL, the residual stream after the last layer.
+ *  logits: device fp32 [vocab]; next_token: device int32 [1] (both ignored
+ *  when vocab == 0).  Runs on one workspace must be stream-ordered.
+ * Errors: Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_EINVAL, Q8_ELAUNCH. */
+int q8_0_chain_run(const q8_0_chain_plan* plan, void* workspace, const float* h_in, float* h_out,
+                   float* logits, int32_t* next_token, void* stream);
+
+/* Copies one activation vector of layer `layer` from the last run to dst
+ * (device fp32): Q8_CHAIN_QKV ([q; k; v], (n_heads + 2 n_kv_heads) head_dim),
+ * Q8_CHAIN_H_ATTN (h after the attention residual, hidden), Q8_CHAIN_SWIGLU
+ * (s, intermediate), Q8_CHAIN_H_OUT (h after the MLP residual, hidden).
+ * Errors: Q8_EINVAL, Q8_ENULL, Q8_EHOSTPTR, Q8_ELAUNCH. */
+#define Q8_CHAIN_QKV 0
+#define Q8_CHAIN_H_ATTN 1
+#define Q8_CHAIN_SWIGLU 2
+#define Q8_CHAIN_H_OUT 3
+int q8_0_chain_read(const q8_0_chain_plan* plan, const void* workspace, int32_t layer,
+                    int32_t which, float* dst, void* stream);
+
+/* Copies the chain's status word to *dev_status (device int32): 0, or bit 1
+ * if a wait for another workgroup's data expired in some run since prepare.
+ * Errors: Q8_ENULL, Q8_EHOSTPTR, Q8_ELAUNCH. */
+int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
+
 /* ---- workspace sizes --------------------------------------------------------
  * op Q8_OP_GEMV: (M, K, N) of q8_0_gemv.
  * op Q8_OP_GEMV_FUSED: (M, K, epilogue flags in N) of q8_0_gemv_fused.

@@ -127,3 +127,63 @@ def test_plans_and_workspace_sizes():
     assert q.q8_0_workspace_bytes(q.Q8_OP_GEMV, 64, 33, 1) == 0  # invalid shape
     for N in range(1, 9):
         assert q.q8_0_gemv_plan(4096, 12288, N)["workgroups"] > 0
+
+
+def _chain(n_layers=2, hidden=896, n_heads=14, n_kv=2, hd=64, inter=4864, vocab=2048, eps=1e-6,
+           gu_layout=q.Q8_LAYOUT_GATE_UP_PAIRS, lm=True):
+    """A chain description with fake (host) weight pointers; only the scalar
+    checks that precede any pointer query can pass with it."""
+    mq = (n_heads + 2 * n_kv) * hd
+    mk = lambda M, K, lay=q.Q8_LAYOUT_ROWS: q.q8_0_weights(16, 16, M, K, 1, 0, 0, lay, 0)
+    arrs = {
+        "qkv": (q.q8_0_weights * max(n_layers, 1))(*[mk(mq, hidden)] * max(n_layers, 1)),
+        "wo": (q.q8_0_weights * max(n_layers, 1))(*[mk(hidden, n_heads * hd)] * max(n_layers, 1)),
+        "gate_up": (q.q8_0_weights * max(n_layers, 1))(
+            *[mk(2 * inter, hidden, gu_layout)] * max(n_layers, 1)),
+        "down": (q.q8_0_weights * max(n_layers, 1))(*[mk(hidden, inter)] * max(n_layers, 1)),
+    }
+    lmw = mk(vocab, hidden) if lm else None
+    d = q.q8_0_chain_desc(n_layers, hidden, n_heads, n_kv, hd, inter, vocab if lm else 0, eps,
+                          arrs["qkv"], arrs["wo"], arrs["gate_up"], arrs["down"],
+                          ctypes.pointer(lmw) if lm else None)
+    return d, (arrs, lmw)
+
+
+def test_chain_workspace_bytes_and_host_validation():
+    L = q.lib()
+    d, keep = _chain()
+    nbytes = L.q8_0_chain_workspace_bytes(ctypes.byref(d))
+    # header + table + 2 layers of tagged records (8 bytes per entry) + argmax partials
+    assert nbytes >= 256 + 2 * 8 * (1152 + 896 + 4864 + 896)
+    bad = [dict(gu_layout=q.Q8_LAYOUT_ROWS),   # gate_up must use the pairs layout
+           dict(hidden=900), dict(inter=4870), dict(n_kv=3), dict(hd=40),
+           dict(inter=6144),                   # polled vectors longer than the kernel's limit
+           dict(eps=-1.0), dict(n_layers=-1)]
+    for kw in bad:
+        d, keep = _chain(**kw)
+        assert L.q8_0_chain_workspace_bytes(ctypes.byref(d)) == 0, kw
+        plan = q.q8_0_chain_plan()
+        rc = L.q8_0_chain_prepare(ctypes.byref(d), ctypes.c_void_p(256), 1 << 30,
+                                  ctypes.byref(plan), None)
+        assert rc == q.Q8_EINVAL, (kw, rc)
+    # vocab > 0 without an LM head descriptor
+    d, keep = _chain()
+    d.lm_head = None
+    assert L.q8_0_chain_prepare(ctypes.byref(d), ctypes.c_void_p(256), 1 << 30,
+                                ctypes.byref(q.q8_0_chain_plan()), None) == q.Q8_ENULL
+    # NULL plan / description
+    d, keep = _chain()
+    assert L.q8_0_chain_prepare(ctypes.byref(d), ctypes.c_void_p(256), 1 << 30, None,
+                                None) == q.Q8_ENULL
+    assert L.q8_0_chain_prepare(None, ctypes.c_void_p(256), 1 << 30,
+                                ctypes.byref(q.q8_0_chain_plan()), None) == q.Q8_ENULL
+    # a host pointer where the workspace must be device memory
+    buf = ctypes.create_string_buffer(1 << 12)
+    aligned = (ctypes.addressof(buf) + 255) // 256 * 256
+    rc = L.q8_0_chain_prepare(ctypes.byref(d), ctypes.c_void_p(aligned), 1 << 30,
+                              ctypes.byref(q.q8_0_chain_plan()), None)
+    assert rc in (q.Q8_EHOSTPTR, q.Q8_ELAUNCH), rc
+    # run / read reject an empty plan before touching anything
+    plan = q.q8_0_chain_plan()
+    assert L.q8_0_chain_run(ctypes.byref(plan), None, None, None, None, None, None) == q.Q8_EINVAL
+    assert L.q8_0_chain_read(ctypes.byref(plan), None, 0, 0, None, None) == q.Q8_EINVAL
