@@ -140,32 +140,58 @@ __device__ __forceinline__ T ld_w(const void* p) {
       reinterpret_cast<uintptr_t>(p)));
 }
 
+// Per-kind constants of one workgroup's share of a projection, computed once
+// per launch (integer divisions kept off the per-stage path).
+struct KindInfo {
+  int K, C, tpi, ntask;
+  int tpi_mul;  // ceil(2^16 / tpi): tau / tpi == (tau * tpi_mul) >> 16 for tau < 256
+};
+
+__device__ __forceinline__ KindInfo kind_info(const ChainArgs& P, int kind, int vwg) {
+  int M, K;
+  switch (kind) {
+    case ST_QKV: M = P.Mq; K = P.H; break;
+    case ST_WO: M = P.H; K = P.NH * P.HD; break;
+    case ST_GU: M = 2 * P.I; K = P.H; break;
+    default: M = P.H; K = P.I; break;
+  }
+  KindInfo ki;
+  ki.K = K;
+  ki.C = K >> 4;
+  ki.tpi = (ki.C + kTaskChunks - 1) / kTaskChunks;
+  const int n_items = M >> 2;
+  const int n_it = n_items > vwg ? (n_items - 1 - vwg) / P.G + 1 : 0;
+  ki.ntask = n_it * ki.tpi;
+  ki.tpi_mul = (65536 + ki.tpi - 1) / ki.tpi;
+  return ki;
+}
+
 // One projection of the step as seen by one workgroup.
 struct Stage {
   ChainMat W;
   int kind, layer;
-  int M, K, C, tpi, n_items, n_it, ntask;
+  int K, C, tpi, ntask, tpi_mul;
   bool pairs;
 };
 
-__device__ __forceinline__ Stage stage_of(const ChainArgs& P, const ChainMat* wt, int s, int vwg) {
+__device__ __forceinline__ Stage stage_of(const KindInfo* ki, const ChainMat* wt, int s) {
   Stage st;
   st.layer = s >> 2;
   st.kind = s & 3;
   st.W = wt[s];
   st.pairs = st.kind == ST_GU;
-  switch (st.kind) {
-    case ST_QKV: st.M = P.Mq; st.K = P.H; break;
-    case ST_WO: st.M = P.H; st.K = P.NH * P.HD; break;
-    case ST_GU: st.M = 2 * P.I; st.K = P.H; break;
-    default: st.M = P.H; st.K = P.I; break;
-  }
-  st.C = st.K >> 4;
-  st.tpi = (st.C + kTaskChunks - 1) / kTaskChunks;
-  st.n_items = st.M >> 2;
-  st.n_it = st.n_items > vwg ? (st.n_items - 1 - vwg) / P.G + 1 : 0;
-  st.ntask = st.n_it * st.tpi;
+  const KindInfo k = ki[st.kind];
+  st.K = k.K;
+  st.C = k.C;
+  st.tpi = k.tpi;
+  st.ntask = k.ntask;
+  st.tpi_mul = k.tpi_mul;
   return st;
+}
+
+// item (within this workgroup) and chunk block of wave task tau
+__device__ __forceinline__ int task_item(const Stage& st, int tau) {
+  return (tau * st.tpi_mul) >> 16;
 }
 
 // Packed-tile position of row r (0..3) of item j (0..15) of a tile.
@@ -175,7 +201,7 @@ __device__ __forceinline__ int item_pos(bool pairs, int j, int r) {
 
 // Chunk of this lane in round k of wave task tau (may be >= C: no work).
 __device__ __forceinline__ int task_chunk(const Stage& st, int tau, int k, int lane) {
-  return (tau % st.tpi) * kTaskChunks + 16 * k + (lane >> 2);
+  return (tau - task_item(st, tau) * st.tpi) * kTaskChunks + 16 * k + (lane >> 2);
 }
 
 // The weights of one lane for one wave task: 4 rounds of 16 quants + scale.
@@ -345,6 +371,8 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ float s_ss[2][kPW];     // poll waves' sums of squares, by stage parity
   __shared__ int s_cnt[kMaxTasks];   // per-item arrivals of wave tasks
+  __shared__ KindInfo s_ki[4];
+  __shared__ int s_xoff[kMaxIn / 16]; // input offset of each wo chunk
   __shared__ float s_cv[kCW];
   __shared__ int s_ci[kCW];
   __shared__ int s_last;
@@ -377,6 +405,14 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
     const ChainMat* wg = reinterpret_cast<const ChainMat*>(ws + kHdrBytes);
     for (int i = threadIdx.x; i < 4 * L; i += kCT) wt[i] = wg[i];
     for (int i = threadIdx.x; i < kMaxTasks; i += kCT) s_cnt[i] = 0;
+    if (threadIdx.x < 4) s_ki[threadIdx.x] = kind_info(P, threadIdx.x, vwg);
+    // the position-0 attention output of head h is its key/value head's
+    // value vector: wo reads v at head h / (n_heads / n_kv_heads)
+    const int grp = P.NH / P.NKV;
+    for (int c = threadIdx.x; c < (P.NH * P.HD) >> 4; c += kCT) {
+      const int k = 16 * c, h = k / P.HD;
+      s_xoff[c] = (h / grp) * P.HD + (k - h * P.HD);
+    }
   }
   __syncthreads();
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -433,7 +469,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   // loaded that early.
   int nt[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) nt[k] = NS > 0 ? stage_of(P, wt, k, vwg).ntask : 0;
+  for (int k = 0; k < 4; ++k) nt[k] = NS > 0 ? s_ki[k].ntask : 0;
   const int cap_dn = nt[ST_DN] < kXW ? nt[ST_DN] : kXW;
   const int cap_qkv = nt[ST_QKV] < kXW ? nt[ST_QKV] : kXW;
   auto base_of = [&](int kind) {
@@ -453,12 +489,13 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   auto prefetch = [&](int s) {
     pf_s = s;
     if (s < 0) return;
-    const Stage nx = stage_of(P, wt, s, vwg);
+    const Stage nx = stage_of(s_ki, wt, s);
     const int tau = first_task(nx.kind);
+    const int item = vwg + task_item(nx, tau) * G;
 #pragma unroll
     for (int k = 0; k < kRounds; ++k) {
       const int c = task_chunk(nx, tau, k, lane);
-      if (c < nx.C) load_lane(nx, vwg + (tau / nx.tpi) * G, c, lane, pf.q[k], pf.d[k]);
+      if (c < nx.C) load_lane(nx, item, c, lane, pf.q[k], pf.d[k]);
     }
   };
 
@@ -478,17 +515,10 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
       if (s + 1 < NS || P.V > 0) poll_stage(s + 1);
       continue;
     }
-    const Stage st = stage_of(P, wt, s, vwg);
+    const Stage st = stage_of(s_ki, wt, s);
     const int l = st.layer;
     const float* xs = xsb + (s & 1) * XSa;
-    const int grp = P.NH / P.NKV;
-    // input offset of chunk c: the position-0 attention output of head h is
-    // its key/value head's value vector, so wo reads v at head h / group
-    auto x_off = [&](int c) {
-      if (st.kind != ST_WO) return 16 * c;
-      const int k = 16 * c, h = k / P.HD;
-      return (h / grp) * P.HD + (k - h * P.HD);
-    };
+    auto x_off = [&](int c) { return st.kind == ST_WO ? s_xoff[c] : 16 * c; };
     const int tau0 = first_task(st.kind);
     for (int tau = tau0; tau < st.ntask; tau += kXW) {
       TaskRegs w;
@@ -500,7 +530,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
 #pragma unroll
         for (int k = 0; k < kRounds; ++k) {
           const int c = task_chunk(st, tau, k, lane);
-          if (c < st.C) load_lane(st, vwg + (tau / st.tpi) * G, c, lane, w.q[k], w.d[k]);
+          if (c < st.C) load_lane(st, vwg + task_item(st, tau) * G, c, lane, w.q[k], w.d[k]);
         }
       }
       float v = 0.f;
@@ -510,7 +540,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
         if (c < st.C) v += lane_dot(w.q[k], w.d[k], xs, x_off(c));
       }
       v = row_sum(v);
-      const int it = tau / st.tpi;
+      const int it = task_item(st, tau);
       float y = v;
       if (st.tpi > 1) {
         if (lane < 4) red[tau * 4 + lane] = v;
