@@ -1,23 +1,27 @@
 """Benchmark: the Q8_0 decode matmul chain of a Qwen2.5-0.5B-shaped decoder on
 one MI355X.
 
-A step is one decode token through the whole hot path: 24 layers of fused
-Q8_0 GEMVs (qkv 1152x896 with the RMSNorm prologue, wo 896x896 with the GQA
-prologue and residual epilogue, gate_up 9728x896 with RMSNorm and SwiGLU,
-down 896x4864 with the residual epilogue), then the LM head 151936x896 with
-the RMSNorm prologue and the argmax epilogue: 97 launches, captured once in a
-HIP graph and replayed.  Weights are synthetic and seeded (quants uniform in
-[-127, 127], scales |N(0,1)|*0.01 in binary16, h0 ~ N(0,1)); 527 MB of
-weights per step exceed the 256 MB Infinity Cache, so replays stream from HBM.
+A step is one decode token through the whole hot path: 24 layers of Q8_0
+GEMVs (qkv 1152x896 behind the RMSNorm, wo 896x896 behind the GQA broadcast
+with the residual add, gate_up 9728x896 behind the RMSNorm with the SwiGLU,
+down 896x4864 with the residual add), then the LM head 151936x896 behind the
+final RMSNorm and the argmax.  By default the step is ONE launch of the
+persistent decode-chain kernel (q8_0_chain_run); `--path graph` times the
+97-launch chain of q8_0_gemv_fused calls replayed from a HIP graph instead.
+Weights are synthetic and seeded (quants uniform in [-127, 127], scales
+|N(0,1)|*0.01 in binary16, h0 ~ N(0,1)); 527 MB of weights per step exceed
+the 256 MB Infinity Cache, so every step streams them from HBM.
 
 Prints one JSON line:
   value        algorithmic HBM GB/s of the step (1.0625 B/weight + x + y per
                GEMV) over the timed region; tok/s alongside
-  roofline     the GEMV kernel (the only kernel of the step): algorithmic bytes
-               per launch / average launch duration over the timed region
+  roofline     the step's kernel: algorithmic bytes per launch / average
+               launch duration, from HIP events on the launch stream
+  rows         every kernel of the path on its own workload (C1..C5 shapes),
+               graph-timed over rotating cold weight copies (>1 GB)
   cpu_baseline the fp64 oracle timed on this host on a bounded sample
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--path persistent|graph]
 """
 from __future__ import annotations
 
@@ -46,31 +50,41 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=24)
+    ap.add_argument("--path", choices=("persistent", "graph"), default="persistent",
+                    help="persistent: one q8_0_chain_run launch per step; graph: 97 "
+                         "q8_0_gemv_fused launches replayed from a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the per-kernel measurements of every workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     return ap.parse_args()
 
 
-def build_chain(n_layers, log):
+SHAPES = {"qkv": (1152, 896), "wo": (896, 896), "gate_up": (9728, 896), "down": (896, 4864)}
+
+
+def build_weights(n_layers, log):
+    """Seeded synthetic weights of every layer and the LM head, repacked on
+    the device.  gate_up uses the gate/up pairs layout the chain kernels
+    expect; the others the plain row layout."""
     import torch
     import block_quantized_gemv_amd as q
     import workloads as W
-    from block_quantized_gemv_amd.decode import ChainConfig, DecodeChain
+    from block_quantized_gemv_amd.decode import ChainConfig
 
     cfg = ChainConfig()
     dev = torch.device("cuda", 0)
-    shapes = {W.MAT_QKV: ("qkv", cfg.qkv_rows, cfg.hidden), W.MAT_WO: ("wo", cfg.hidden, cfg.hidden),
-              W.MAT_GATE_UP: ("gate_up", 2 * cfg.intermediate, cfg.hidden),
-              W.MAT_DOWN: ("down", cfg.hidden, cfg.intermediate)}
+    mats = {"qkv": W.MAT_QKV, "wo": W.MAT_WO, "gate_up": W.MAT_GATE_UP, "down": W.MAT_DOWN}
     layers, sample_aos = [], {}
     t0 = time.time()
     for l in range(n_layers):
         L = {}
-        for mat, (name, M, K) in shapes.items():
+        for name, mat in mats.items():
+            M, K = SHAPES[name]
             aos = W.matrix(W.C2["cfg"], l, mat, M, K).aos()
             if l == 0:
                 sample_aos[name] = aos
@@ -82,14 +96,203 @@ def build_chain(n_layers, log):
     sample_aos["lm_head_rows"] = lm[:16384].copy()
     lm_p = q.PackedQ8.from_aos(torch.from_numpy(lm.reshape(-1)).to(dev), cfg.vocab, cfg.hidden)
     del lm
+    h0 = torch.from_numpy(W.activations(W.C2["cfg"], 1, cfg.hidden)[0]).to(dev)
     torch.cuda.synchronize()
     log(f"weights generated and repacked in {time.time() - t0:.1f} s")
-    chain = DecodeChain(cfg, layers, lm_p)
-    chain.h0.copy_(torch.from_numpy(W.activations(W.C2["cfg"], 1, cfg.hidden)[0]).to(dev))
-    step_bytes = n_layers * sum(gemv_bytes(M, K) for (_, M, K) in shapes.values())
+    step_bytes = n_layers * sum(gemv_bytes(M, K) for (M, K) in SHAPES.values())
     step_bytes += gemv_bytes(cfg.vocab, cfg.hidden)
-    launches = 4 * n_layers + 1
-    return chain, cfg, step_bytes, launches, sample_aos
+    return cfg, layers, lm_p, h0, step_bytes, sample_aos
+
+
+def time_launches(launch, steps, warmup, stream):
+    """Average time of one `launch()` over `steps` back-to-back launches,
+    from HIP events recorded on the stream the kernels run on."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def time_persistent(cfg, layers, lm_p, h0, steps, warmup, stream, log):
+    import torch
+    import block_quantized_gemv_amd as q
+    pc = q.PersistentChain(layers, lm_p, cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
+                           cfg.intermediate, cfg.eps)
+    dev = h0.device
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
+    tok = torch.empty(1, dtype=torch.int32, device=dev)
+    h_out = torch.empty(cfg.hidden, dtype=torch.float32, device=dev)
+    log(f"persistent chain: grid {pc.plan.grid} x {pc.plan.threads} threads, "
+        f"LDS {pc.plan.lds_bytes} B, workspace {pc.plan.ws_bytes} B")
+    s = time_launches(lambda: pc.run(h0, logits, tok, h_out, stream=stream), steps, warmup,
+                      stream)
+    status = pc.status()
+    if status != 0:
+        raise RuntimeError(f"persistent chain reported status {status}")
+    return s, 1, "q8::chain_kernel", int(tok.cpu()[0])
+
+
+def time_graph(cfg, layers, lm_p, h0, steps, warmup, stream, log):
+    from block_quantized_gemv_amd.decode import DecodeChain
+    chain = DecodeChain(cfg, layers, lm_p)
+    chain.h0.copy_(h0)
+    g = chain.capture()
+    s = time_launches(g.replay, steps, warmup, stream)
+    return s, 4 * len(layers) + 1, "q8::gemv_kernel<1>", int(chain.next_token.cpu()[0])
+
+
+def graph_time(enqueue, n_calls, replays=5):
+    """Seconds per call of `enqueue(i)` (i < n_calls), captured once into a
+    HIP graph and replayed; HIP events on the replay stream bracket the
+    replays, so host launch overhead is excluded and each call's dispatch
+    latency (about 1.6 us per graph node) is included."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(min(n_calls, 2)):
+            enqueue(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(n_calls):
+            enqueue(i)
+    g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(replays):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / replays / n_calls
+
+
+def rand_packed(M, K, n_mats, gen):
+    """Seeded packed Q8_0 weights drawn on the device with the workload's
+    distributions (quants uniform in [-127, 127], scales |N(0,1)|*0.01 in
+    binary16); only for shapes with no padding (M % 64 == 0, K % 128 == 0)."""
+    import torch
+    import block_quantized_gemv_amd as q
+    assert M % 64 == 0 and K % 128 == 0
+    qb, db = q.q8_0_packed_size(M, K)
+    dev = torch.device("cuda", 0)
+    qs = torch.randint(-127, 128, (n_mats * qb,), dtype=torch.int8, device=dev, generator=gen)
+    d = (torch.randn(n_mats * db // 2, device=dev, generator=gen).abs() * 0.01).half()
+    return q.PackedQ8(qs.view(torch.uint8), d.view(torch.uint8), M, K, n_mats)
+
+
+def measure_rows(log, cold_bytes=1.2e9):
+    """Every kernel of the path on its own workload, graph-timed over rotating
+    cold weight copies (more than `cold_bytes` in rotation, beyond the 256 MB
+    Infinity Cache): C1 896x896; the 0.5B layer shapes; lm_head with the fused
+    RMSNorm/argmax and the standalone argmax; the 9B-class shapes at N = 1, 2,
+    4, 8; the Qwen1.5-MoE-shaped FFN (router, scatter + SwiGLU, combine)."""
+    import torch
+    import block_quantized_gemv_amd as q
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    rows = []
+
+    def rec(row, what, sec, nbytes):
+        r = {"row": row, "what": what, "us": round(sec * 1e6, 2)}
+        if nbytes:
+            gbs = nbytes / sec / 1e9
+            r.update(GBs=round(gbs, 1), frac=round(gbs / PEAK_HBM_GBS, 4))
+        rows.append(r)
+        log(f"{row} {what}: {sec * 1e6:.2f} us" + (f", {r['GBs']} GB/s" if nbytes else ""))
+
+    def gemv_row(row, M, K, N, what, epi=None):
+        n = max(2, min(64, int(cold_bytes // (1.0625 * M * K)) + 1))
+        Wm = rand_packed(M, K, n, gen)
+        qb, db = q.q8_0_packed_size(M, K)
+        views = [q.PackedQ8(Wm.qs[i * qb:(i + 1) * qb], Wm.d[i * db:(i + 1) * db], M, K)
+                 for i in range(n)]
+        x = torch.randn(N, K, device=dev, generator=gen)
+        y = torch.empty(N, M, device=dev)
+        if epi is None:
+            ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_GEMV, M, K, N))
+            sec = graph_time(lambda i: q.q8_0_gemv(views[i % n], x, y, ws), n)
+        else:
+            tok = torch.empty(1, dtype=torch.int32, device=dev)
+            fus = q.make_fusion(q.Q8_PRO_RMSNORM, q.Q8_EPI_ARGMAX, 1e-6, argmax_out=tok)
+            ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_GEMV_FUSED, M, K, q.Q8_EPI_ARGMAX))
+            sec = graph_time(lambda i: q.q8_0_gemv_fused(views[i % n], x[0], y[0], fus, ws), n)
+        rec(row, what, sec, gemv_bytes(M, K, N))
+        del views, Wm
+        torch.cuda.empty_cache()
+
+    # context: what plain torch kernels reach on this device (read-reduce, copy)
+    big = torch.empty(1 << 29, dtype=torch.float32, device=dev).uniform_(generator=gen)
+    dst = torch.empty_like(big)
+    sink = torch.empty((), device=dev)
+    st = torch.cuda.current_stream()
+    rec("hbm", "torch sum over 2 GiB fp32 (read)",
+        time_launches(lambda: torch.sum(big, dim=0, out=sink), 5, 2, st), big.numel() * 4)
+    rec("hbm", "torch copy of 2 GiB (read + write)",
+        time_launches(lambda: dst.copy_(big), 5, 2, st), big.numel() * 8)
+    del big, dst
+    torch.cuda.empty_cache()
+    gemv_row("a2", 896, 896, 1, "C1 gemv 896x896")
+    for name, (M, K) in SHAPES.items():
+        gemv_row("a2", M, K, 1, f"C2 {name} {M}x{K}")
+    gemv_row("a2", 151936, 896, 1, "C3 lm_head 151936x896")
+    gemv_row("a4", 151936, 896, 1, "C3 lm_head 151936x896 + RMSNorm + argmax", epi="argmax")
+    v = torch.randn(151936, device=dev, generator=gen)
+    out = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_ARGMAX, v.numel(), 0, 0))
+    rec("a4", "argmax over 151936 fp32 logits", graph_time(lambda i: q.q8_0_argmax(v, out, ws), 32),
+        4 * v.numel())
+    for N in (1, 2, 4, 8):
+        gemv_row("a3" if N > 1 else "a2", 24576, 4096, N, f"C4 gate_up 24576x4096 N={N}")
+        gemv_row("a3" if N > 1 else "a2", 4096, 12288, N, f"C4 down 4096x12288 N={N}")
+
+    # Qwen1.5-MoE-shaped FFN, one token per call, routing from seeded N(0,1) logits
+    E, H, I, Ish, S, T, NSH = 60, 2048, 1408, 5632, 4, 32, 8
+    gu, dn = rand_packed(2 * I, H, E, gen), rand_packed(H, I, E, gen)
+    sgu = [rand_packed(2 * Ish, H, 1, gen) for _ in range(NSH)]
+    sdn = [rand_packed(H, Ish, 1, gen) for _ in range(NSH)]
+    logits = torch.from_numpy(np.stack([W.router_logits(5, t, E) for t in range(T)])).to(dev)
+    lam = torch.randn(T, device=dev, generator=gen)
+    x = torch.randn(T, H, device=dev, generator=gen)
+    ids = torch.empty(T, S, dtype=torch.int32, device=dev)
+    w = torch.empty(T, S, device=dev)
+    h = torch.empty(T, S * I + Ish, device=dev)
+    y = torch.empty(T, H, device=dev)
+    mode_s = q.Q8_MOE_SCATTER | q.Q8_MOE_SWIGLU
+    ws1 = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_MOE_SCATTER, 2 * I, H, S, 2 * Ish, H, mode_s))
+    ws2 = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_MOE_COMBINE, H, I, S, H, Ish, q.Q8_MOE_COMBINE))
+    route = lambda t: q.q8_0_route_topk(logits[t], S, ids[t], w[t])
+    scatter = lambda t: q.q8_0_moe_gemv(gu, ids[t], None, x[t], h[t], mode_s, shared=sgu[t % NSH],
+                                        workspace=ws1)
+    combine = lambda t: q.q8_0_moe_gemv(dn, ids[t], w[t], h[t], y[t], q.Q8_MOE_COMBINE,
+                                        shared=sdn[t % NSH], shared_gate=lam[t:t + 1],
+                                        workspace=ws2)
+    for t in range(T):
+        route(t)
+    torch.cuda.synchronize()
+    bs = S * gemv_bytes(2 * I, H) + gemv_bytes(2 * Ish, H)
+    bc = S * gemv_bytes(H, I) + gemv_bytes(H, Ish)
+    rec("a5", "C5 router top-4 of 60", graph_time(route, T), 0)
+    rec("a6", "C5 scatter: 4 slots gate_up 2816x2048 + shared 11264x2048 + SwiGLU",
+        graph_time(scatter, T), bs)
+    rec("a8", "C5 combine: 4 slots down 2048x1408 + shared 2048x5632, weighted",
+        graph_time(combine, T), bc)
+    rec("a5-a8", "C5 MoE FFN token: router + scatter + combine",
+        graph_time(lambda t: (route(t), scatter(t), combine(t)), T), bs + bc)
+    del gu, dn, sgu, sdn
+    torch.cuda.empty_cache()
+    return rows
 
 
 def cpu_baseline(sample_aos, cfg, seconds, log):
@@ -126,16 +329,17 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def committed_traffic(launches):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, when
-    it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "chain_counters.json")
+def committed_traffic(kernel, launches):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, when it was taken on the current kernel sources; else None."""
+    name = "chain_kernel_counters.json" if "chain" in kernel else "gemv_kernel_counters.json"
+    path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_hash") != kernel_source_hash():
+    if c.get("kernel_source_hash") != kernel_source_hash() or c.get("kernel") != kernel:
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -159,26 +363,24 @@ def main():
         torch.cuda.synchronize()
         log(f"copied {args.calibrate_copy} bytes 5 times")
         return
-    chain, cfg, step_bytes, launches, sample_aos = build_chain(args.layers, log)
+    cfg, layers, lm_p, h0, step_bytes, sample_aos = build_weights(args.layers, log)
     stream = torch.cuda.current_stream()
-    g = chain.capture()
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    gbs = step_bytes / (ms * 1e-3) / 1e9
-    log(f"{args.steps} steps: {ms * 1e3:.1f} us/step, {1e3 / ms:.1f} tok/s, {gbs:.1f} GB/s")
+    timer = time_persistent if args.path == "persistent" else time_graph
+    sec, launches, kernel, tok = timer(cfg, layers, lm_p, h0, args.steps, args.warmup, stream,
+                                       log)
+    ms = sec * 1e3
+    gbs = step_bytes / sec / 1e9
+    log(f"{args.path}: {args.steps} steps, {ms * 1e3:.1f} us/step, {1e3 / ms:.1f} tok/s, "
+        f"{gbs:.1f} GB/s, token {tok}")
     per_launch_bytes = step_bytes / launches
-    per_launch_s = ms * 1e-3 / launches
+    per_launch_s = sec / launches
     achieved = per_launch_bytes / per_launch_s / 1e9
-    traffic = committed_traffic(launches)
+    traffic = committed_traffic(kernel, launches)
+    workload = ("Qwen2.5-0.5B-shaped Q8_0 decode matmul chain, N=1: 24 layers x (qkv 1152x896, "
+                "wo 896x896, gate_up 9728x896 + SwiGLU, down 896x4864) + lm_head 151936x896 + "
+                "argmax, glue fused, " + ("one persistent launch per token"
+                                          if args.path == "persistent" else
+                                          "97 launches replayed from a HIP graph"))
     out = {
         "metric": "Q8_0 GEMV achieved HBM GB/s (% of MI355X peak) + decode matmul-chain tok/s",
         "value": round(gbs, 2),
@@ -194,20 +396,22 @@ def main():
         "data": "synthetic",
         "tok_per_s": round(1e3 / ms, 2),
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-        "config": {"workload": "Qwen2.5-0.5B-shaped Q8_0 decode matmul chain, N=1: 24 layers x "
-                               "(qkv 1152x896, wo 896x896, gate_up 9728x896 + SwiGLU, down "
-                               "896x4864) + lm_head 151936x896 + argmax, glue fused, HIP graph",
+        "config": {"workload": workload, "path": args.path,
                    "layers": args.layers, "launches_per_step": launches,
                    "bytes_per_step": int(step_bytes), "weights": "q8_0 (1.0625 B/weight)",
                    "activations": "fp32"},
-        "roofline": {"bound": "hbm", "kernel": "q8::gemv_kernel<1>",
+        "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic,
                      "bytes_per_launch": int(per_launch_bytes),
                      "avg_launch_us": round(per_launch_s * 1e6, 3)},
+        "rows": None,
         "cpu_baseline": None,
     }
+    del layers, lm_p
+    if not args.no_rows:
+        out["rows"] = measure_rows(log)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(sample_aos, cfg, args.cpu_seconds, log)
     print(json.dumps(out), flush=True)

@@ -13,10 +13,14 @@
 //    wave's 16-byte quant load covers 64 rows x 16 weights = 1 KiB of
 //    contiguous HBM (global_load_dwordx4, non-temporal), and its 8-byte scale
 //    load covers 4 blocks of all 64 rows (512 B contiguous).
-//  * The activation vector is the same for every lane, so it is read with
-//    scalar loads into SGPRs and used directly as the FMA's scalar operand;
-//    each weight costs one int8->fp32 convert (SDWA byte select) and one FMA.
-//    No LDS traffic on the hot loop and no cross-lane reduction per row.
+//  * The activation vector is the same for every lane.  Each wave keeps the
+//    activations of the blocks in flight in VGPRs, 16 lanes' worth replicated
+//    in the four 16-lane rows, loaded one quad ahead with the weights, and the
+//    FMA reads them through a DPP row broadcast (v_fmac_f32_dpp
+//    row_newbcast): each weight costs one int8->fp32 convert (SDWA byte
+//    select) and one FMA per column, with no instruction spent moving the
+//    activation and no scalar-cache latency on the critical path.  No LDS
+//    traffic on the hot loop and no cross-lane reduction per row.
 //  * A tile's K range is split into "units", one per wave; units of one tile
 //    are folded in a fixed order (bitwise reproducible).  When a tile's units
 //    span several workgroups, each writes its partials to the workspace and
@@ -33,6 +37,8 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include <utility>
 
 #include "q8_internal.h"
 
@@ -65,82 +71,135 @@ __device__ __forceinline__ const float* x_block(const float* x, int b, int gqa_g
   return x + (int64_t)b * 32;
 }
 
-// Activations are read through the constant address space: they are not
-// written while a GEMV runs, and wave-uniform constant loads become scalar
-// loads (s_load_dwordx*) whose results feed the FMAs as SGPR operands.
-typedef const __attribute__((address_space(4))) float* cfloat_p;
+// ---- activations in VGPRs, read through a DPP row broadcast ----------------
+// The activations are the same for every lane (row).  Each wave holds them in
+// VGPRs: for block b and column n, lane l of every 16-lane row holds
+// x[n][32b + (l % 16)] in `a` and x[n][32b + 16 + (l % 16)] in `b` (plain
+// dword loads of 64 distinct bytes; the four rows read the same addresses,
+// and they are loaded one quad ahead together with the weights, so their
+// latency hides behind the weight stream).  The FMA of weight j reads
+// lane j % 16 of its row through the DPP row_newbcast operand, so every lane
+// sees the same activation and no instruction is spent moving it.  The DPP
+// source registers are only ever written by loads: a VALU write to a DPP
+// source needs wait states, which inline assembly would not get.
 
-// acc[n] += d * sum_j q[j] * xb[n*xs + j] over the 32 weights of one block.
+// acc += (xv of lane J of this lane's 16-lane row) * q
+template <int J>
+__device__ __forceinline__ void fmac_row_bcast(float& acc, float xv, float q) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc)
+      : "v"(xv), "v"(q), "i"(J));
+}
+
 template <int N>
-__device__ __forceinline__ void block_fma(u32x4 q0, u32x4 q1, const float* xg, int64_t xs,
-                                          float dsc, float (&acc)[N]) {
-  const cfloat_p xb = (cfloat_p)xg;
+struct XBlock {
+  float a[N], b[N];
+};
+
+template <int N>
+__device__ __forceinline__ void load_xblock(const float* xg, int64_t xs, int xl, XBlock<N>& X) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    X.a[n] = xg[n * xs + xl];
+    X.b[n] = xg[n * xs + 16 + xl];
+  }
+}
+
+template <int N, int J>
+__device__ __forceinline__ void xv_step(const uint32_t (&w)[8], const XBlock<N>& X,
+                                        float (&p)[N]) {
+  const float qf = q_at(w[J >> 2], J & 3);
+#pragma unroll
+  for (int n = 0; n < N; ++n) fmac_row_bcast<J & 15>(p[n], J < 16 ? X.a[n] : X.b[n], qf);
+}
+
+template <int N, int... J>
+__device__ __forceinline__ void xv_steps(const uint32_t (&w)[8], const XBlock<N>& X, float (&p)[N],
+                                         std::integer_sequence<int, J...>) {
+  (xv_step<N, J>(w, X, p), ...);
+}
+
+// acc[n] += d * sum_j q[j] * x[n][32b + j] with the activations of XBlock.
+template <int N>
+__device__ __forceinline__ void block_fma_xv(u32x4 q0, u32x4 q1, const XBlock<N>& X, float dsc,
+                                             float (&acc)[N]) {
   const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
   float p[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) p[n] = 0.f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float qf = q_at(w[j >> 2], j & 3);
-#pragma unroll
-    for (int n = 0; n < N; ++n) p[n] = fmaf(qf, xb[n * xs + j], p[n]);
-  }
+  xv_steps<N>(w, X, p, std::make_integer_sequence<int, 32>{});
 #pragma unroll
   for (int n = 0; n < N; ++n) acc[n] = fmaf(dsc, p[n], acc[n]);
 }
 
+// One scale quad of one tile: 8 quant chunks, the scales, the activations.
+template <int N>
+struct QuadBuf {
+  u32x4 q[8];
+  u32x2 sc;
+  XBlock<N> x[4];
+};
+
+template <int N>
+__device__ __forceinline__ void quad_load(QuadBuf<N>& B, const u32x4* qp, const u32x2* dp, int g,
+                                          const float* x, int64_t xs, int xl, int gg, int ghd,
+                                          int64_t goff) {
+  B.sc = __builtin_nontemporal_load(dp + g * 64);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) B.q[i] = __builtin_nontemporal_load(qp + (8 * g + i) * 64);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load_xblock<N>(x_block(x, 4 * g + j, gg, ghd, goff), xs, xl, B.x[j]);
+}
+
+template <int N>
+__device__ __forceinline__ void quad_fma(const QuadBuf<N>& B, float (&acc)[N]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    block_fma_xv<N>(B.q[2 * j], B.q[2 * j + 1], B.x[j], f16_to_f32(quad_bits(B.sc, j)), acc);
+}
+
 // Partial dot products of the 64 rows of one tile over blocks [b0, b1).
-// qs_tile / d_tile point at the tile's packed quants / scales.
+// qs_tile / d_tile point at the tile's packed quants / scales.  Whole quads
+// are double-buffered without loop-carried register copies (two named
+// buffers, two quads per trip).
 template <int N>
 __device__ __forceinline__ void dot_range(const uint8_t* qs_tile, const uint8_t* d_tile, int b0,
-                                          int b1, int lane, const float* x, int64_t xs, int gg,
-                                          int ghd, int64_t goff, float (&acc)[N]) {
-  const u32x4* qp = reinterpret_cast<const u32x4*>(qs_tile) + lane;  // chunk c: qp[c * 64]
-  const u32x2* dp = reinterpret_cast<const u32x2*>(d_tile) + lane;   // quad g: dp[g * 64]
+                                             int b1, int lane, const float* x, int64_t xs, int gg,
+                                             int ghd, int64_t goff, float (&acc)[N]) {
+  const u32x4* qp = reinterpret_cast<const u32x4*>(qs_tile) + lane;
+  const u32x2* dp = reinterpret_cast<const u32x2*>(d_tile) + lane;
+  const int xl = lane & 15;
   int b = b0;
-  // Leading blocks up to a quad boundary.
   for (; b < b1 && (b & 3); ++b) {
+    XBlock<N> X;
     const u32x2 sc = __builtin_nontemporal_load(dp + (b >> 2) * 64);
     const u32x4 q0 = __builtin_nontemporal_load(qp + (2 * b) * 64);
     const u32x4 q1 = __builtin_nontemporal_load(qp + (2 * b + 1) * 64);
-    block_fma<N>(q0, q1, x_block(x, b, gg, ghd, goff), xs, f16_to_f32(quad_bits(sc, b & 3)), acc);
+    load_xblock<N>(x_block(x, b, gg, ghd, goff), xs, xl, X);
+    block_fma_xv<N>(q0, q1, X, f16_to_f32(quad_bits(sc, b & 3)), acc);
   }
-  // Whole quads, software-pipelined one quad ahead.
   const int nq = (b1 - b) >> 2;
   if (nq > 0) {
-    int g = b >> 2;
-    u32x4 cq[8];
-    u32x2 csc = __builtin_nontemporal_load(dp + g * 64);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cq[i] = __builtin_nontemporal_load(qp + (8 * g + i) * 64);
-    for (int it = 0; it < nq; ++it, ++g) {
-      u32x4 nq_[8];
-      u32x2 nsc;
-      if (it + 1 < nq) {
-        nsc = __builtin_nontemporal_load(dp + (g + 1) * 64);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) nq_[i] = __builtin_nontemporal_load(qp + (8 * (g + 1) + i) * 64);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int bb = 4 * g + j;
-        block_fma<N>(cq[2 * j], cq[2 * j + 1], x_block(x, bb, gg, ghd, goff), xs,
-                     f16_to_f32(quad_bits(csc, j)), acc);
-      }
-      if (it + 1 < nq) {
-        csc = nsc;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) cq[i] = nq_[i];
-      }
+    const int g0 = b >> 2;
+    QuadBuf<N> A, B;
+    quad_load<N>(A, qp, dp, g0, x, xs, xl, gg, ghd, goff);
+    int it = 0;
+    for (; it + 1 < nq; it += 2) {
+      quad_load<N>(B, qp, dp, g0 + it + 1, x, xs, xl, gg, ghd, goff);
+      quad_fma<N>(A, acc);
+      if (it + 2 < nq) quad_load<N>(A, qp, dp, g0 + it + 2, x, xs, xl, gg, ghd, goff);
+      quad_fma<N>(B, acc);
     }
+    if (it < nq) quad_fma<N>(A, acc);
     b += 4 * nq;
   }
-  // Trailing blocks.
   for (; b < b1; ++b) {
+    XBlock<N> X;
     const u32x2 sc = __builtin_nontemporal_load(dp + (b >> 2) * 64);
     const u32x4 q0 = __builtin_nontemporal_load(qp + (2 * b) * 64);
     const u32x4 q1 = __builtin_nontemporal_load(qp + (2 * b + 1) * 64);
-    block_fma<N>(q0, q1, x_block(x, b, gg, ghd, goff), xs, f16_to_f32(quad_bits(sc, b & 3)), acc);
+    load_xblock<N>(x_block(x, b, gg, ghd, goff), xs, xl, X);
+    block_fma_xv<N>(q0, q1, X, f16_to_f32(quad_bits(sc, b & 3)), acc);
   }
 }
 

@@ -11,7 +11,9 @@
 namespace q8 {
 
 constexpr int kTile = Q8_TILE_ROWS;  // rows per packed tile, one per lane
-constexpr int kMaxWaves = 16;        // most waves per GEMV workgroup
+// Most waves per GEMV workgroup: 8, so that a wave may use up to 256 VGPRs
+// (the activations of a double-buffered quad take 16 N of them).
+constexpr int kMaxWaves = 8;
 constexpr int kMaxThreads = 64 * kMaxWaves;
 constexpr int kMaxSeg = 9;           // K-segments over all problems of one launch
 constexpr int kMaxProb = 9;          // problems (independent GEMVs) per launch
