@@ -321,25 +321,29 @@ def cpu_baseline(sample_aos, cfg, seconds, log):
             "tok_per_s_equiv": round(gbs * 1e9 / 527386624, 4)}
 
 
-def kernel_source_hash():
+def source_hash(files):
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.join(ROOT, "block_quantized_gemv_amd", "csrc"))):
-        with open(os.path.join(ROOT, "block_quantized_gemv_amd", "csrc", name), "rb") as f:
+    for name in files:
+        with open(os.path.join(ROOT, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(kernel, launches):
+def committed_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, when it was taken on the current kernel sources; else None."""
-    name = "chain_kernel_counters.json" if "chain" in kernel else "gemv_kernel_counters.json"
-    path = os.path.join(ROOT, "profiles", name)
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads
+    for a plain copy of known size), when it was taken on the kernel's current
+    sources; else None."""
+    name = {"q8::chain_kernel": "chain_kernel_counters.json"}.get(kernel)
+    if name is None:
+        return None
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_hash") != kernel_source_hash() or c.get("kernel") != kernel:
+    if c.get("kernel") != kernel or c.get("kernel_source_hash") != source_hash(
+            c.get("kernel_sources", [])):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -375,7 +379,7 @@ def main():
     per_launch_bytes = step_bytes / launches
     per_launch_s = sec / launches
     achieved = per_launch_bytes / per_launch_s / 1e9
-    traffic = committed_traffic(kernel, launches)
+    traffic = committed_traffic(kernel)
     workload = ("Qwen2.5-0.5B-shaped Q8_0 decode matmul chain, N=1: 24 layers x (qkv 1152x896, "
                 "wo 896x896, gate_up 9728x896 + SwiGLU, down 896x4864) + lm_head 151936x896 + "
                 "argmax, glue fused, " + ("one persistent launch per token"

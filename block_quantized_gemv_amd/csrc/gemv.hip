@@ -281,7 +281,7 @@ __device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, 
 // ONE: a single problem with a single segment (dense GEMVs and the decode
 // chain): every kernel argument sits at a fixed offset, so no search loops.
 template <int N, bool ONE>
-__global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const GemvParams p) {
+__global__ __launch_bounds__(64 * max_waves_for(N)) void gemv_kernel(const GemvParams p) {
   extern __shared__ float lds_part[];  // [W][N][64]
   __shared__ int s_last;
 
@@ -500,6 +500,21 @@ int min_units() {
   static const int v = env_int("Q8G_MIN_UNITS", 4);
   return v;
 }
+// Compute units of the current device (256 on an MI355X; that value when no
+// device can be queried, e.g. when only sizing a workspace).
+int num_cus() {
+  static const int v = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+      (void)hipGetLastError();
+      return 256;
+    }
+    return n;
+  }();
+  return v;
+}
 int max_waves() {
   static const int v = env_int("Q8G_MAX_WAVES", kMaxWaves);
   return v < kMaxWaves ? v : kMaxWaves;
@@ -570,7 +585,7 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
   }
   if (segc > kMaxSeg || nprob > kMaxProb || total_tout <= 0) return Q8_EINVAL;
   const int64_t want_u = cdiv(target_waves(), total_tout);
-  const int wmax = max_waves();
+  const int wmax = max_waves() < max_waves_for(N) ? max_waves() : max_waves_for(N);
   // units per tile
   int sbase = 0;
   int64_t U[kMaxProb];
@@ -596,12 +611,32 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
     U[i] = usum * pd.R;
     sbase += pd.nseg;
   }
-  // waves per workgroup (common to the launch) and workgroups per tile
-  int64_t W = 1;
-  for (int i = 0; i < nprob; ++i) {
-    const int64_t P = cdiv(U[i], wmax);
-    const int64_t w = cdiv(U[i], P);
-    if (w > W) W = w;
+  // waves per workgroup (common to the launch) and workgroups per tile;
+  // while the launch has fewer workgroups than the device has compute units,
+  // smaller workgroups (more of them per tile) spread it over more units
+  auto waves_per_wg = [&](int64_t cap) {
+    int64_t W = 1;
+    for (int i = 0; i < nprob; ++i) {
+      const int64_t P = cdiv(U[i], cap);
+      const int64_t w = cdiv(U[i], P);
+      if (w > W) W = w;
+    }
+    return W;
+  };
+  auto workgroups = [&](int64_t W) {
+    int64_t n = 0;
+    for (int i = 0; i < nprob; ++i) n += prob_tout(probs[i]) * cdiv(U[i], W);
+    return n;
+  };
+  int64_t cap = wmax;
+  int64_t W = waves_per_wg(cap);
+  // (only launches whose tiles already span several workgroups: a tile that
+  // fits one workgroup keeps its cheaper in-workgroup fold)
+  bool split = false;
+  for (int i = 0; i < nprob; ++i) split |= cdiv(U[i], W) > 1;
+  while (split && cap > 4 && workgroups(W) < num_cus()) {
+    cap /= 2;
+    W = waves_per_wg(cap);
   }
   int64_t cnt = 0;
   size_t data = 0;

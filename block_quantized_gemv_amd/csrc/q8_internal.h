@@ -11,10 +11,12 @@
 namespace q8 {
 
 constexpr int kTile = Q8_TILE_ROWS;  // rows per packed tile, one per lane
-// Most waves per GEMV workgroup: 8, so that a wave may use up to 256 VGPRs
-// (the activations of a double-buffered quad take 16 N of them).
-constexpr int kMaxWaves = 8;
+// Most waves per GEMV workgroup: 16 for N <= 2 (a wave fits in 128 VGPRs);
+// 8 for more columns, so that a wave may use up to 256 VGPRs (the
+// activations of a double-buffered quad take 16 N of them).
+constexpr int kMaxWaves = 16;
 constexpr int kMaxThreads = 64 * kMaxWaves;
+constexpr int max_waves_for(int N) { return N <= 2 ? 16 : 8; }
 constexpr int kMaxSeg = 9;           // K-segments over all problems of one launch
 constexpr int kMaxProb = 9;          // problems (independent GEMVs) per launch
 // Every workspace starts with a fixed region of 32-bit counters that each
