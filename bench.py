@@ -196,7 +196,8 @@ def measure_rows(log, cold_bytes=1.2e9):
     cold weight copies (more than `cold_bytes` in rotation, beyond the 256 MB
     Infinity Cache): C1 896x896; the 0.5B layer shapes; lm_head with the fused
     RMSNorm/argmax and the standalone argmax; the 9B-class shapes at N = 1, 2,
-    4, 8; the Qwen1.5-MoE-shaped FFN (router, scatter + SwiGLU, combine)."""
+    4, 8; the verify-chunk LM head with one argmax per column; the
+    Qwen1.5-MoE-shaped FFN (router, scatter + SwiGLU, combine)."""
     import torch
     import block_quantized_gemv_amd as q
     import workloads as W
@@ -223,6 +224,10 @@ def measure_rows(log, cold_bytes=1.2e9):
         if epi is None:
             ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_GEMV, M, K, N))
             sec = graph_time(lambda i: q.q8_0_gemv(views[i % n], x, y, ws), n)
+        elif epi == "col_argmax":
+            am = torch.empty(N, dtype=torch.int32, device=dev)
+            ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_GEMV_ARGMAX, M, K, N))
+            sec = graph_time(lambda i: q.q8_0_gemv_argmax(views[i % n], x, y, am, ws), n)
         else:
             tok = torch.empty(1, dtype=torch.int32, device=dev)
             fus = q.make_fusion(q.Q8_PRO_RMSNORM, q.Q8_EPI_ARGMAX, 1e-6, argmax_out=tok)
@@ -256,6 +261,9 @@ def measure_rows(log, cold_bytes=1.2e9):
     for N in (1, 2, 4, 8):
         gemv_row("a3" if N > 1 else "a2", 24576, 4096, N, f"C4 gate_up 24576x4096 N={N}")
         gemv_row("a3" if N > 1 else "a2", 4096, 12288, N, f"C4 down 4096x12288 N={N}")
+    for N in (2, 8):
+        gemv_row("f4", 151936, 896, N, f"lm_head 151936x896 N={N} + argmax per column (2 launches)",
+                 epi="col_argmax")
 
     # Qwen1.5-MoE-shaped FFN, one token per call, routing from seeded N(0,1) logits
     E, H, I, Ish, S, T, NSH = 60, 2048, 1408, 5632, 4, 32, 8

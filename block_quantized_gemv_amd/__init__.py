@@ -24,11 +24,13 @@ Q8_PRO_NONE, Q8_PRO_RMSNORM, Q8_PRO_GQA = 0, 1, 2
 Q8_EPI_RESIDUAL, Q8_EPI_SWIGLU, Q8_EPI_ARGMAX = 1, 2, 4
 Q8_MOE_SCATTER, Q8_MOE_COMBINE, Q8_MOE_SWIGLU = 1, 2, 4
 Q8_OP_GEMV, Q8_OP_GEMV_FUSED, Q8_OP_ARGMAX, Q8_OP_MOE_SCATTER, Q8_OP_MOE_COMBINE = 1, 2, 3, 4, 5
+Q8_OP_GEMV_ARGMAX = 6
 
 Q8_LAYOUT_ROWS, Q8_LAYOUT_GATE_UP_PAIRS = 0, 1
 Q8_CHAIN_QKV, Q8_CHAIN_H_ATTN, Q8_CHAIN_SWIGLU, Q8_CHAIN_H_OUT = 0, 1, 2, 3
 
-EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv", "q8_0_gemv_fused", "q8_0_argmax",
+EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv", "q8_0_gemv_fused",
+           "q8_0_gemv_argmax", "q8_0_argmax",
            "q8_0_route_topk", "q8_0_moe_gemv", "q8_0_workspace_bytes", "q8_0_gemv_plan",
            "q8_0_strerror", "q8_0_version", "q8_0_chain_workspace_bytes", "q8_0_chain_prepare",
            "q8_0_chain_run", "q8_0_chain_read", "q8_0_chain_status")
@@ -96,6 +98,7 @@ def lib() -> ctypes.CDLL:
         L.q8_0_repack_layout.argtypes = [P, I64, I64, I32, P, P, P]
         L.q8_0_gemv.argtypes = [PW, P, P, I64, I64, I64, P, SZ, P]
         L.q8_0_gemv_fused.argtypes = [PW, P, P, I64, I64, ctypes.POINTER(q8_0_fusion), P, SZ, P]
+        L.q8_0_gemv_argmax.argtypes = [PW, P, P, I64, I64, I64, P, P, SZ, P]
         L.q8_0_argmax.argtypes = [P, I64, P, P, SZ, P]
         L.q8_0_route_topk.argtypes = [P, I32, I32, P, P, P]
         L.q8_0_moe_gemv.argtypes = [PW, P, P, P, P, I64, I64, I32, I32, PW, P, P, P, SZ, P]
@@ -291,6 +294,29 @@ def q8_0_gemv_fused(W: PackedQ8, x: torch.Tensor, y: torch.Tensor, fusion: q8_0_
                                                     y.data_ptr(), W.M, W.K, ctypes.byref(fusion),
                                                     wsp, wsb, _stream(stream)))
     return y
+
+
+def q8_0_gemv_argmax(W: PackedQ8, x: torch.Tensor, y: torch.Tensor | None = None,
+                     argmax_out: torch.Tensor | None = None, workspace=None, stream=None):
+    """y[N][M] = x[N][K] @ W^T and argmax_out[n] = lowest index of the largest
+    y[n][*], one pick per column; returns (y, argmax_out)."""
+    _need(x, torch.float32, "x")
+    N = 1 if x.dim() == 1 else x.shape[0]
+    if y is None:
+        y = torch.empty((W.M,) if x.dim() == 1 else (N, W.M), dtype=torch.float32,
+                        device=x.device)
+    if argmax_out is None:
+        argmax_out = torch.empty(N, dtype=torch.int32, device=x.device)
+    _need(y, torch.float32, "y")
+    _need(argmax_out, torch.int32, "argmax_out")
+    if argmax_out.numel() < N:
+        raise ValueError("argmax_out needs one entry per column")
+    wsp, wsb = _ws(workspace, q8_0_workspace_bytes(Q8_OP_GEMV_ARGMAX, W.M, W.K, N), x.device)
+    _check("q8_0_gemv_argmax", lib().q8_0_gemv_argmax(ctypes.byref(W.desc), x.data_ptr(),
+                                                      y.data_ptr(), W.M, W.K, N,
+                                                      argmax_out.data_ptr(), wsp, wsb,
+                                                      _stream(stream)))
+    return y, argmax_out
 
 
 def q8_0_argmax(v: torch.Tensor, out: torch.Tensor | None = None, workspace=None,

@@ -242,13 +242,18 @@ int q8_0_repack_layout(const void* aos, int64_t M, int64_t K, int32_t layout, vo
 }
 
 static int gemv_common(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,
-                       int64_t N, const q8_0_fusion* f, void* ws, size_t wsb, void* stream) {
+                       int64_t N, const q8_0_fusion* f, int32_t* col_argmax, void* ws,
+                       size_t wsb, void* stream) {
   int rc = check_weights_shape(W, M, K, false);
   if (rc) return rc;
   if (N < 1 || N > Q8_MAX_N) return Q8_EINVAL;
   if (!x || !y) return Q8_ENULL;
   ProbDesc pd;
   if ((rc = build_gemv(W, x, y, M, K, N, f, &pd))) return rc;
+  if (col_argmax) {
+    pd.flags |= F_ARGMAX;
+    pd.argmax_out = col_argmax;
+  }
   if (M == 0) return Q8_OK;
   if ((rc = check_weights_ptrs(W)) || (rc = check_dev_aligned(x, 4)) ||
       (rc = check_dev_aligned(y, 4)))
@@ -261,14 +266,21 @@ static int gemv_common(const q8_0_weights* W, const float* x, float* y, int64_t 
 
 int q8_0_gemv(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
               void* workspace, size_t workspace_bytes, void* stream) {
-  return gemv_common(W, x, y, M, K, N, nullptr, workspace, workspace_bytes, stream);
+  return gemv_common(W, x, y, M, K, N, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+int q8_0_gemv_argmax(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,
+                     int64_t N, int32_t* argmax_out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (!argmax_out) return Q8_ENULL;
+  return gemv_common(W, x, y, M, K, N, nullptr, argmax_out, workspace, workspace_bytes, stream);
 }
 
 int q8_0_gemv_fused(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,
                     const q8_0_fusion* fusion, void* workspace, size_t workspace_bytes,
                     void* stream) {
   if (!fusion) return Q8_ENULL;
-  return gemv_common(W, x, y, M, K, 1, fusion, workspace, workspace_bytes, stream);
+  return gemv_common(W, x, y, M, K, 1, fusion, nullptr, workspace, workspace_bytes, stream);
 }
 
 int q8_0_argmax(const float* v, int64_t n, int32_t* out_idx, void* workspace,
@@ -332,7 +344,7 @@ size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t
                             int32_t flags) {
   Plan plan;
   if (op == Q8_OP_ARGMAX) return argmax_ws_bytes(M);
-  if (op == Q8_OP_GEMV || op == Q8_OP_GEMV_FUSED) {
+  if (op == Q8_OP_GEMV || op == Q8_OP_GEMV_FUSED || op == Q8_OP_GEMV_ARGMAX) {
     if (!shape_ok(M, K) || M == 0) return 0;
     q8_0_weights W = {nullptr, nullptr, M, K, 1, 0, 0};
     q8_0_fusion f;
@@ -348,6 +360,7 @@ size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t
     }
     ProbDesc pd;
     if (build_gemv(&W, nullptr, nullptr, M, K, n, fp, &pd)) return 0;
+    if (op == Q8_OP_GEMV_ARGMAX) pd.flags |= F_ARGMAX;
     if (plan_problems(&pd, 1, (int)n, &plan)) return 0;
     return plan.ws_bytes;
   }

@@ -424,14 +424,17 @@ __global__ __launch_bounds__(64 * max_waves_for(N)) void gemv_kernel(const GemvP
     if (valid) pr.y[n * pr.y_stride + row] = v;
   }
   if (pr.flags & F_ARGMAX) {
-    // per-tile (max, lowest index); the fold over tiles runs in the next
-    // kernel of the same call, ordered by the kernel boundary
-    float mv = valid ? out[0] : -INFINITY;
-    int mi = row;
-    wave_argmax(mv, mi);
-    if (lane == 0) {
-      pr.am_val[ot] = mv;
-      pr.am_idx[ot] = mi;
+    // per tile and column (max, lowest index); the fold over tiles runs in
+    // the next kernel of the same call, ordered by the kernel boundary
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      float mv = valid ? out[n] : -INFINITY;
+      int mi = row;
+      wave_argmax(mv, mi);
+      if (lane == 0) {
+        pr.am_val[n * pr.Tout + ot] = mv;
+        pr.am_idx[n * pr.Tout + ot] = mi;
+      }
     }
   }
 }
@@ -440,6 +443,10 @@ __global__ __launch_bounds__(64 * max_waves_for(N)) void gemv_kernel(const GemvP
 __global__ __launch_bounds__(256) void argmax_fold_kernel(const float* __restrict__ v,
                                                           const int32_t* __restrict__ idx, int n,
                                                           int32_t* out) {
+  // block b folds column b: partials [b * n, (b + 1) * n) into out[b]
+  v += (int64_t)blockIdx.x * n;
+  idx += (int64_t)blockIdx.x * n;
+  out += blockIdx.x;
   __shared__ float sv[4];
   __shared__ int si[4];
   float bv = -INFINITY;
@@ -650,7 +657,7 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
     plan->cnt_off[i] = (int32_t)cnt;
     plan->data_off[i] = data;
     if (P > 1) cnt += Tout;
-    if (pd.flags & F_ARGMAX) data += align_up((size_t)Tout * 4, 256) * 2;
+    if (pd.flags & F_ARGMAX) data += align_up((size_t)Tout * N * 4, 256) * 2;
     if (P > 1) data += align_up((size_t)Tout * U[i] * N * 64 * 4, 256);
     wg += Tout * P;
   }
@@ -710,9 +717,9 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
       if (pr.P > 1) pr.tile_tickets = static_cast<uint32_t*>(ws) + plan.cnt_off[i];
       if (pd.flags & F_ARGMAX) {
         pr.am_val = reinterpret_cast<float*>(base);
-        base += align_up((size_t)Tout * 4, 256);
+        base += align_up((size_t)Tout * N * 4, 256);
         pr.am_idx = reinterpret_cast<int32_t*>(base);
-        base += align_up((size_t)Tout * 4, 256);
+        base += align_up((size_t)Tout * N * 4, 256);
       }
       if (pr.P > 1) pr.part = reinterpret_cast<float*>(base);
     }
@@ -761,7 +768,7 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
   for (int i = 0; i < nprob; ++i) {
     const Prob& pr = gp.prob[i];
     if (!(pr.flags & F_ARGMAX)) continue;
-    hipLaunchKernelGGL(argmax_fold_kernel, dim3(1), dim3(256), 0, stream, pr.am_val, pr.am_idx,
+    hipLaunchKernelGGL(argmax_fold_kernel, dim3(N), dim3(256), 0, stream, pr.am_val, pr.am_idx,
                        pr.Tout, pr.argmax_out);
     if (hipGetLastError() != hipSuccess) return Q8_ELAUNCH;
   }

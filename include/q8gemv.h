@@ -181,6 +181,19 @@ int q8_0_gemv_fused(const q8_0_weights* W, const float* x, float* y, int64_t M, 
                     const q8_0_fusion* fusion, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* ---- GEMV with one argmax per column (verify chunk) --------------------------
+ * y as q8_0_gemv (1 <= N <= Q8_MAX_N columns), and argmax_out[n] (device int32
+ * [N]) = min{ r : y[n][r] == max_j y[n][j] }: the greedy pick of each of the
+ * N logit rows of a verify chunk ("skuznetsov/cogni-ml" README, "Qwen 3.5
+ * Native Metal": target-verifier chunks and the resident top-1 over logits)
+ * with ties to the earliest index ("fusedtok 1.3.0", "API stability").  The
+ * picks compare the same fp32 values the call writes to y.  One GEMV launch
+ * (per-tile maxima in its epilogue) plus one small fold launch.
+ * Errors as q8_0_gemv; argmax_out must be 4-byte aligned device memory. */
+int q8_0_gemv_argmax(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,
+                     int64_t N, int32_t* argmax_out, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* ---- argmax ------------------------------------------------------------------
  * *out_idx = min{ i : v[i] == max_j v[j] } over fp32 v[0..n) (device), as
  * int32 (device).  Inputs are finite (NaN is outside the contract).
@@ -339,6 +352,7 @@ int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
 /* ---- workspace sizes --------------------------------------------------------
  * op Q8_OP_GEMV: (M, K, N) of q8_0_gemv.
  * op Q8_OP_GEMV_FUSED: (M, K, epilogue flags in N) of q8_0_gemv_fused.
+ * op Q8_OP_GEMV_ARGMAX: (M, K, N) of q8_0_gemv_argmax.
  * op Q8_OP_ARGMAX: (n, 0, 0).
  * op Q8_OP_MOE_SCATTER / Q8_OP_MOE_COMBINE: (M, K, n_slots) with the
  *   shared expert's shape in (M2, K2) (0, 0 for none) and mode flags in flags.
@@ -348,6 +362,7 @@ int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
 #define Q8_OP_ARGMAX 3
 #define Q8_OP_MOE_SCATTER 4
 #define Q8_OP_MOE_COMBINE 5
+#define Q8_OP_GEMV_ARGMAX 6
 size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t M2, int64_t K2,
                             int32_t flags);
 

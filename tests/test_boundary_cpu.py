@@ -187,3 +187,21 @@ def test_chain_workspace_bytes_and_host_validation():
     plan = q.q8_0_chain_plan()
     assert L.q8_0_chain_run(ctypes.byref(plan), None, None, None, None, None, None) == q.Q8_EINVAL
     assert L.q8_0_chain_read(ctypes.byref(plan), None, 0, 0, None, None) == q.Q8_EINVAL
+
+
+def test_gemv_argmax_rejects_bad_arguments_on_host():
+    L = q.lib()
+    dummy = ctypes.c_void_p(16)
+    W = _desc(64, 32)
+    assert L.q8_0_gemv_argmax(ctypes.byref(W), dummy, dummy, 64, 32, 2, None, None, 0,
+                              None) == q.Q8_ENULL
+    for N in (0, 9):
+        assert L.q8_0_gemv_argmax(ctypes.byref(W), dummy, dummy, 64, 32, N, dummy, None, 0,
+                                  None) == q.Q8_EINVAL
+    assert L.q8_0_gemv_argmax(ctypes.byref(W), dummy, dummy, 64, 33, 1, dummy, None, 0,
+                              None) == q.Q8_EINVAL
+    # the per-column partials need workspace for every column
+    one = q.q8_0_workspace_bytes(q.Q8_OP_GEMV_ARGMAX, 151936, 896, 1)
+    eight = q.q8_0_workspace_bytes(q.Q8_OP_GEMV_ARGMAX, 151936, 896, 8)
+    assert 0 < one < eight
+    assert q.q8_0_workspace_bytes(q.Q8_OP_GEMV_ARGMAX, 151936, 896, 9) == 0

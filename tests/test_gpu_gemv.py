@@ -217,3 +217,83 @@ def test_fused_rmsnorm_swiglu_pairs_layout(M, K):
          + 0.5 * tg * tg * np.abs(ur) + 8 * U * np.abs(sil * ur))
     err = np.abs(host(y).astype(np.float64) - oracle.swiglu(gr, ur))
     assert np.all(err <= b), float((err / b).max())
+
+
+# ---- one argmax per column (verify chunk) ------------------------------------
+@pytest.mark.parametrize("M,K", [(1, 32), (65, 96), (1000, 128), (4097, 896), (2816, 2048)])
+@pytest.mark.parametrize("N", [1, 2, 4, 8])
+def test_gemv_argmax_columns(M, K, N):
+    """Each column's pick is the lowest index of that column's largest GPU
+    logit (bit-exact against numpy on the GPU's own values), the logits equal
+    the plain GEMV's bit for bit, and they match the oracle."""
+    g = W.rng(30, M * 5 + N, K)
+    m = W.draw_matrix(g, M, K)
+    x = W.draw_x(g, N, K)
+    p = pack(m)
+    y, am = q.q8_0_gemv_argmax(p, to_dev(x))
+    yh, amh = host(y).reshape(N, M), host(am)
+    assert np.array_equal(amh, np.argmax(yh, axis=1)), (amh, np.argmax(yh, axis=1))
+    y_plain = host(q.q8_0_gemv(p, to_dev(x))).reshape(N, M)
+    assert np.array_equal(yh.view(np.uint32), y_plain.view(np.uint32))
+    yr, S = oracle.gemv(m.aos(), x)
+    q8tol.check(yh, yr.reshape(N, M), S.reshape(N, M), f"gemv_argmax {M}x{K} N={N}")
+
+
+@pytest.mark.parametrize("N", [2, 8])
+def test_gemv_argmax_lm_head_shape_and_planted_ties(N):
+    """lm_head 151936 x 896 with N verify columns.  Copies of the best row of
+    each column planted at a lower and a higher index give bitwise-equal
+    logits (per-row arithmetic does not depend on the row index); the pick
+    must be the lowest copy.  Against the fp64 oracle the pick lies within the
+    tolerance band of the true maximum."""
+    M, K = 151936, 896
+    m = W.matrix(3, 0, W.MAT_LM_HEAD, M, K)
+    x = W.activations(31, N, K)
+    qs, d = m.qs.copy(), m.d.copy()
+    # the oracle's best row of column 0, copied to a lower and a higher index
+    y0, S0 = oracle.gemv(m.aos(), x[:1])
+    order = np.argsort(-y0[0])
+    best = int(order[0])
+    lo = best // 2 if best > 0 else M - 2
+    hi = (best + M) // 2 if best < M - 1 else 1
+    for r in (lo, hi):
+        qs[r], d[r] = qs[best], d[best]
+    planted = W.Q8Matrix(qs, d)
+    p = pack(planted)
+    y, am = q.q8_0_gemv_argmax(p, to_dev(x))
+    yh, amh = host(y).reshape(N, M), host(am)
+    assert np.array_equal(amh, np.argmax(yh, axis=1))
+    assert yh[0, lo] == yh[0, best] == yh[0, hi]
+    # the runner-up among rows that are not copies of the best one
+    second = next(int(r) for r in order[1:] if r not in (lo, hi))
+    tol = 2e-5 * S0[0] + 1e-6
+    if y0[0][best] - y0[0][second] > tol[best] + tol[second]:
+        assert amh[0] == min(lo, best, hi)
+    for n in range(N):
+        pick = int(amh[n])
+        cand = np.unique(np.concatenate([[pick], np.argsort(-yh[n])[:8]]))
+        yr, S = oracle.gemv(planted.aos()[cand], x[n:n + 1])
+        top = float(yr[0].max())
+        tol = 2e-5 * S[0] + 1e-6
+        assert yr[0][list(cand).index(pick)] >= top - 2 * tol.max()
+
+
+def test_gemv_argmax_rejects_bad_arguments():
+    M, K = 64, 64
+    m = W.draw_matrix(W.rng(32, M, K), M, K)
+    p = pack(m)
+    x = to_dev(W.draw_x(W.rng(33, 2, K), 2, K))
+    y = torch.empty(2, M, device=DEV)
+    lib = q.lib()
+    ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_GEMV_ARGMAX, M, K, 2))
+    wsp, wsb = ws.get(ws.buf.numel())
+    assert lib.q8_0_gemv_argmax(p.desc, x.data_ptr(), y.data_ptr(), M, K, 2, None, wsp, wsb,
+                                None) == q.Q8_ENULL
+    am = torch.empty(2, dtype=torch.int32, device=DEV)
+    assert lib.q8_0_gemv_argmax(p.desc, x.data_ptr(), y.data_ptr(), M, K, 9, am.data_ptr(), wsp,
+                                wsb, None) == q.Q8_EINVAL
+    host_am = np.zeros(2, dtype=np.int32)
+    assert lib.q8_0_gemv_argmax(p.desc, x.data_ptr(), y.data_ptr(), M, K, 2,
+                                host_am.ctypes.data, wsp, wsb, None) == q.Q8_EHOSTPTR
+    assert lib.q8_0_gemv_argmax(p.desc, x.data_ptr(), y.data_ptr(), M, K, 2, am.data_ptr() + 2,
+                                wsp, wsb, None) == q.Q8_EALIGN
