@@ -24,17 +24,20 @@
 // Work split.  A layer projection is cut into items of 4 output rows (gate
 // and up pairs: 2 gate + the 2 matching up rows) over the full K, spread
 // round-robin over the workgroups, so no K-split partials cross workgroups.
-// Inside a workgroup a wave task is (item, 64 consecutive 16-weight chunks),
-// taken in 4 rounds of 16 chunks: in round k lane 4m + r holds the 16 quants
-// of row r in chunk 16k + m and its scale, so the four lanes of a chunk read
-// the item's 64 contiguous packed bytes of that chunk (16 cache lines per
-// load instruction, not 64) and share one broadcast 16-float slice of the
-// input from LDS.  A lane adds its 4 rounds in order, the 16 lanes of a row
-// are summed by a butterfly, and the tasks of one item are added in task
-// order.  Each weight wave keeps its first task of the next projection in
-// registers.  Waves 0-5 poll the inputs and run the epilogues (RMS scale,
-// grouped-query remap, residual, SwiGLU); waves 6-15 hold the weights.  The LM head is
-// streamed: one 64-row tile per wave, lane = row, input broadcast from LDS.
+// Inside a workgroup a wave task is (item, 16 consecutive 16-weight chunks):
+// lane 4m + r holds the 16 quants of row r in chunk m of the task and its
+// scale, so the four lanes of a chunk read the item's 64 contiguous packed
+// bytes of that chunk (16 cache lines per load instruction, not 64) and share
+// one broadcast 16-float slice of the input from LDS (laid out with 4 floats
+// of padding after every 16, so the 16 slices a wave reads fall in distinct
+// banks).  The 16 lanes of a row are summed by DPP/permlane rotations, and
+// the tasks of one item are added in task order by whichever of them
+// finishes last, which also runs the epilogue (RMS scale, residual, SwiGLU,
+// tagged store).  Small tasks spread even the smallest projections over many
+// waves.  Each weight wave keeps its first kPre tasks of the next projection
+// with work for it in registers.  Waves 0-5 poll the inputs into LDS; waves
+// 6-15 hold the weights.  The LM head is streamed: one 64-row tile per wave,
+// lane = row, input broadcast from LDS.
 //
 // Every spin is bounded; on expiry bit 1 of the status word is set and the
 // kernel runs to completion with whatever it read.
@@ -56,9 +59,10 @@ constexpr int kPL = 64 * kPW;   // poll lanes
 constexpr int kXW = kCW - kPW;  // waves holding prefetched weights
 constexpr int kSlots = 7;       // 16-byte poll slots per poll lane
 constexpr int kMaxIn = 2 * kPL * kSlots;  // longest polled vector (5376 entries)
-constexpr int kMaxTasks = 256;  // wave tasks of one workgroup in one projection
-constexpr int kTaskChunks = 64; // 16-weight chunks per wave task
-constexpr int kRounds = 4;      // rounds of 16 chunks (4 lanes each) per task
+constexpr int kMaxTasks = 1024; // wave tasks of one workgroup in one projection
+constexpr int kRounds = 4;      // rounds of 16 chunks (4 lanes each) per wave task
+constexpr int kTaskChunks = 16 * kRounds;  // 16-weight chunks per wave task
+constexpr int kPre = 1;         // tasks of the next projection a wave holds in registers
 constexpr int kSpinMax = 1 << 18;
 // Cache policy of the polling loads: sc1 (device scope: coherent across the
 // XCDs' separate L2s).
@@ -144,7 +148,7 @@ __device__ __forceinline__ T ld_w(const void* p) {
 // per launch (integer divisions kept off the per-stage path).
 struct KindInfo {
   int K, C, tpi, ntask;
-  int tpi_mul;  // ceil(2^16 / tpi): tau / tpi == (tau * tpi_mul) >> 16 for tau < 256
+  int tpi_mul;  // ceil(2^20 / tpi): tau / tpi == (tau * tpi_mul) >> 20 for tau < 1024
 };
 
 __device__ __forceinline__ KindInfo kind_info(const ChainArgs& P, int kind, int vwg) {
@@ -162,7 +166,7 @@ __device__ __forceinline__ KindInfo kind_info(const ChainArgs& P, int kind, int 
   const int n_items = M >> 2;
   const int n_it = n_items > vwg ? (n_items - 1 - vwg) / P.G + 1 : 0;
   ki.ntask = n_it * ki.tpi;
-  ki.tpi_mul = (65536 + ki.tpi - 1) / ki.tpi;
+  ki.tpi_mul = ((1 << 20) + ki.tpi - 1) / ki.tpi;
   return ki;
 }
 
@@ -191,7 +195,7 @@ __device__ __forceinline__ Stage stage_of(const KindInfo* ki, const ChainMat* wt
 
 // item (within this workgroup) and chunk block of wave task tau
 __device__ __forceinline__ int task_item(const Stage& st, int tau) {
-  return (tau * st.tpi_mul) >> 16;
+  return (tau * st.tpi_mul) >> 20;
 }
 
 // Packed-tile position of row r (0..3) of item j (0..15) of a tile.
@@ -204,11 +208,15 @@ __device__ __forceinline__ int task_chunk(const Stage& st, int tau, int k, int l
   return (tau - task_item(st, tau) * st.tpi) * kTaskChunks + 16 * k + (lane >> 2);
 }
 
-// The weights of one lane for one wave task: 4 rounds of 16 quants + scale.
+// The weights of one lane for one wave task: kRounds x (16 quants + scale).
 struct TaskRegs {
   u32x4 q[kRounds];
   uint32_t d[kRounds];
 };
+
+// LDS position of input entry k: 4 floats of padding after every 16, so the
+// 16 chunks that the lanes of a wave read at once fall in distinct banks.
+__device__ __forceinline__ int xpad(int k) { return k + ((k >> 4) << 2); }
 
 // The 16 quants of row (lane & 3) in chunk c of item `item`, and its scale.
 __device__ __forceinline__ void load_lane(const Stage& st, int item, int c, int lane, u32x4& q,
@@ -347,13 +355,15 @@ __device__ __forceinline__ float lm_tile_dot(const ChainMat& W, int K, int tile,
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
       if (jb < nb) {
-        const float4* xb = reinterpret_cast<const float4*>(xs + 32 * (4 * g + jb));
+        // the block's two 16-entry chunks, each followed by 4 floats of padding
+        const float4* xb0 = reinterpret_cast<const float4*>(xs + 40 * (4 * g + jb));
+        const float4* xb1 = reinterpret_cast<const float4*>(xs + 40 * (4 * g + jb) + 20);
         const uint32_t w[8] = {q[2 * jb].x, q[2 * jb].y, q[2 * jb].z, q[2 * jb].w,
                                q[2 * jb + 1].x, q[2 * jb + 1].y, q[2 * jb + 1].z, q[2 * jb + 1].w};
         float p = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float4 xv = xb[i];
+          const float4 xv = i < 4 ? xb0[i] : xb1[i - 4];
           p = fmaf(q_at(w[i], 0), xv.x, p);
           p = fmaf(q_at(w[i], 1), xv.y, p);
           p = fmaf(q_at(w[i], 2), xv.z, p);
@@ -372,7 +382,6 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   __shared__ float s_ss[2][kPW];     // poll waves' sums of squares, by stage parity
   __shared__ int s_cnt[kMaxTasks];   // per-item arrivals of wave tasks
   __shared__ KindInfo s_ki[4];
-  __shared__ int s_xoff[kMaxIn / 16]; // input offset of each wo chunk
   __shared__ float s_cv[kCW];
   __shared__ int s_ci[kCW];
   __shared__ int s_last;
@@ -396,7 +405,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   // poll waves can stage projection s+1 while the weight waves work on s
   const int XS = P.I > H ? (P.I > P.NH * P.HD ? P.I : P.NH * P.HD)
                         : (H > P.NH * P.HD ? H : P.NH * P.HD);
-  const int XSa = (XS + 3) & ~3, Ha = (H + 3) & ~3;
+  const int XSa = (xpad(XS) + 3) & ~3, Ha = (H + 3) & ~3;
   float* const xsb = lds;                    // [2][XSa] inputs by stage parity
   float* const hres = xsb + 2 * XSa;         // [2][Ha]: before attention, before MLP
   float* const red = hres + 2 * Ha;          // [task][4] row partial sums
@@ -406,13 +415,6 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
     for (int i = threadIdx.x; i < 4 * L; i += kCT) wt[i] = wg[i];
     for (int i = threadIdx.x; i < kMaxTasks; i += kCT) s_cnt[i] = 0;
     if (threadIdx.x < 4) s_ki[threadIdx.x] = kind_info(P, threadIdx.x, vwg);
-    // the position-0 attention output of head h is its key/value head's
-    // value vector: wo reads v at head h / (n_heads / n_kv_heads)
-    const int grp = P.NH / P.NKV;
-    for (int c = threadIdx.x; c < (P.NH * P.HD) >> 4; c += kCT) {
-      const int k = 16 * c, h = k / P.HD;
-      s_xoff[c] = (h / grp) * P.HD + (k - h * P.HD);
-    }
   }
   __syncthreads();
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -438,27 +440,32 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
       if (s == 0) {
         for (int k = pl; k < H; k += kPL) {
           const float v = P.h_in[k];
-          xs[k] = v;
+          xs[xpad(k)] = v;
           hr[k] = v;
           ss = fmaf(v, v, ss);
         }
       } else {
         const int64_t off = kind == ST_GU && s < NS ? rec(l, ST_WO) : rec(l - 1, ST_DN);
         ss = poll_tagged(rs, off, H, step, pl, &hdr->status, [&](int k, float v) {
-          xs[k] = v;
+          xs[xpad(k)] = v;
           hr[k] = v;
         });
       }
       ss = wave_sum_dpp(ss);
       if (lane == 0) s_ss[s & 1][wave] = ss;
     } else if (kind == ST_WO) {
-      // value heads as they are; the attention remap is an input offset
+      // the position-0 attention output: query head h returns the value
+      // vector of key/value head h / (n_heads / n_kv_heads), so value entry
+      // k goes to every query head of its group
       const int64_t off = rec(l, ST_QKV) + (int64_t)(P.NH + P.NKV) * P.HD * 8;
-      poll_tagged(rs, off, P.NKV * P.HD, step, pl, &hdr->status,
-                  [&](int k, float v) { xs[k] = v; });
+      const int grp = P.NH / P.NKV;
+      poll_tagged(rs, off, P.NKV * P.HD, step, pl, &hdr->status, [&](int k, float v) {
+        const int g = k / P.HD, j = k - g * P.HD;
+        for (int h = g * grp; h < (g + 1) * grp; ++h) xs[xpad(h * P.HD + j)] = v;
+      });
     } else {
       poll_tagged(rs, rec(l, ST_GU), P.I, step, pl, &hdr->status,
-                  [&](int k, float v) { xs[k] = v; });
+                  [&](int k, float v) { xs[xpad(k)] = v; });
     }
   };
 
@@ -484,18 +491,27 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
       if (first_task(s2 & 3) < nt[s2 & 3]) return s2;
     return -1;
   };
-  TaskRegs pf;
+  TaskRegs pf[kPre];
   int pf_s = -1;
+  // the weights of this wave's first kPre tasks of projection s
   auto prefetch = [&](int s) {
     pf_s = s;
     if (s < 0) return;
     const Stage nx = stage_of(s_ki, wt, s);
-    const int tau = first_task(nx.kind);
-    const int item = vwg + task_item(nx, tau) * G;
+    const int tau0 = first_task(nx.kind);
 #pragma unroll
-    for (int k = 0; k < kRounds; ++k) {
-      const int c = task_chunk(nx, tau, k, lane);
-      if (c < nx.C) load_lane(nx, item, c, lane, pf.q[k], pf.d[k]);
+    for (int j = 0; j < kPre; ++j) {
+      const int tau = tau0 + j * kXW;
+      if (tau < nx.ntask) {
+        const int item = vwg + task_item(nx, tau) * G;
+#pragma unroll
+        for (int k = 0; k < kRounds; ++k) {
+          const int c = task_chunk(nx, tau, k, lane);
+          pf[j].q[k] = u32x4{0, 0, 0, 0};
+          pf[j].d[k] = 0;
+          if (c < nx.C) load_lane(nx, item, c, lane, pf[j].q[k], pf[j].d[k]);
+        }
+      }
     }
   };
 
@@ -518,26 +534,19 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
     const Stage st = stage_of(s_ki, wt, s);
     const int l = st.layer;
     const float* xs = xsb + (s & 1) * XSa;
-    auto x_off = [&](int c) { return st.kind == ST_WO ? s_xoff[c] : 16 * c; };
-    const int tau0 = first_task(st.kind);
-    for (int tau = tau0; tau < st.ntask; tau += kXW) {
-      TaskRegs w;
-      if (tau == tau0 && pf_s == s) {
-        w = pf;
-        __asm__ volatile("" : "+v"(w.q[0]), "+v"(w.q[1]), "+v"(w.q[2]), "+v"(w.q[3]),
-                         "+v"(w.d[0]), "+v"(w.d[1]), "+v"(w.d[2]), "+v"(w.d[3]));
-      } else {
-#pragma unroll
-        for (int k = 0; k < kRounds; ++k) {
-          const int c = task_chunk(st, tau, k, lane);
-          if (c < st.C) load_lane(st, vwg + task_item(st, tau) * G, c, lane, w.q[k], w.d[k]);
-        }
-      }
+    auto x_off = [&](int c) { return 20 * c; };
+    // one wave task: 16 chunks of one item (4 rows); the last task of an item
+    // to finish folds the item's partials in task order and writes its outputs
+    auto run_task = [&](int tau, const TaskRegs& w) {
       float v = 0.f;
 #pragma unroll
       for (int k = 0; k < kRounds; ++k) {
+        // every round reads a valid chunk (its own, else chunk 0), with no
+        // branch, so that the rounds' LDS reads can be issued together; the
+        // weights of a chunk past the row end are zero and its sum is dropped
         const int c = task_chunk(st, tau, k, lane);
-        if (c < st.C) v += lane_dot(w.q[k], w.d[k], xs, x_off(c));
+        const float t = lane_dot(w.q[k], w.d[k], xs, x_off(c < st.C ? c : 0));
+        v += c < st.C ? t : 0.f;
       }
       v = row_sum(v);
       const int it = task_item(st, tau);
@@ -548,9 +557,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
         int arrived = 0;
         if (lane == 0) arrived = atomicAdd(&s_cnt[it], 1);
         arrived = __builtin_amdgcn_readfirstlane(arrived);
-        if (arrived != st.tpi - 1) continue;
-        // the last task of this item to finish folds the item's partials in
-        // task order and writes its outputs
+        if (arrived != st.tpi - 1) return;
         if (lane == 0) s_cnt[it] = 0;
         y = 0.f;
         if (lane < 4) {
@@ -575,6 +582,32 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
           if (st.kind == ST_DN && l == L - 1 && P.h_out) P.h_out[row] = out;
         }
       }
+    };
+    int tau = first_task(st.kind);
+    if (pf_s == s) {
+#pragma unroll
+      for (int j = 0; j < kPre; ++j) {
+        if (tau < st.ntask) {
+          TaskRegs w = pf[j];
+          // keep arithmetic on the prefetched registers after barrier A
+#pragma unroll
+          for (int k = 0; k < kRounds; ++k) __asm__ volatile("" : "+v"(w.q[k]), "+v"(w.d[k]));
+          run_task(tau, w);
+        }
+        tau += kXW;
+      }
+    }
+    for (; tau < st.ntask; tau += kXW) {
+      TaskRegs w;
+      const int item = vwg + task_item(st, tau) * G;
+#pragma unroll
+      for (int k = 0; k < kRounds; ++k) {
+        const int c = task_chunk(st, tau, k, lane);
+        w.q[k] = u32x4{0, 0, 0, 0};
+        w.d[k] = 0;
+        if (c < st.C) load_lane(st, item, c, lane, w.q[k], w.d[k]);
+      }
+      run_task(tau, w);
     }
     __syncthreads();  // B(s)
     // the next projection with work for this wave streams in from now on
@@ -692,7 +725,8 @@ int layout_of(const q8_0_chain_desc* c, Layout* lo) {
   lo->am_off = o;
   o += kMaxGrid * 8;
   lo->total = o;
-  const int64_t lds = 4 * (2 * ((lo->XS + 3) & ~3) + 2 * ((H + 3) & ~3) + kMaxTasks * 4) +
+  const int64_t XSp = lo->XS + (lo->XS >> 4) * 4;  // padded input length
+  const int64_t lds = 4 * (2 * ((XSp + 3) & ~3) + 2 * ((H + 3) & ~3) + kMaxTasks * 4) +
                       (int64_t)sizeof(ChainMat) * 4 * L;
   lo->lds_bytes = (int32_t)lds;
   return Q8_OK;
