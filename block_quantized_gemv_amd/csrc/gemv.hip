@@ -211,16 +211,47 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // (value, index) maximum with ties to the lower index; all lanes agree.
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oi = __shfl_xor(i, o, 64);
-    if (ov > v || (ov == v && oi < i)) {
-      v = ov;
-      i = oi;
-    }
+// VALU data movement only: DPP rotations within each 16-lane row, then
+// v_permlane16/32_swap across rows (inline asm: the swap builtins are not
+// used because both of their results are needed; the nop covers the
+// VALU-write to permlane-read hazard).  The combination is symmetric, so the
+// result does not depend on the order in which lanes are combined.
+__device__ __forceinline__ void argmax_comb(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
   }
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_ror(float& v, int& i) {
+  const float ov = __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+  const int oi = dpp_i<CTRL>(i);
+  argmax_comb(v, i, ov, oi);
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_ror<0x121>(v, i);  // row_ror:1
+  argmax_ror<0x122>(v, i);  // row_ror:2
+  argmax_ror<0x124>(v, i);  // row_ror:4
+  argmax_ror<0x128>(v, i);  // row_ror:8
+  int a = __builtin_bit_cast(int, v), b = a, ia = i, ib = i;
+  __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3"
+                   : "+v"(a), "+v"(b), "+v"(ia), "+v"(ib));
+  v = __builtin_bit_cast(float, a);
+  i = ia;
+  argmax_comb(v, i, __builtin_bit_cast(float, b), ib);
+  a = __builtin_bit_cast(int, v);
+  b = a;
+  ia = i;
+  ib = i;
+  __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3"
+                   : "+v"(a), "+v"(b), "+v"(ia), "+v"(ib));
+  v = __builtin_bit_cast(float, a);
+  i = ia;
+  argmax_comb(v, i, __builtin_bit_cast(float, b), ib);
 }
 
 __device__ __forceinline__ float seg_alpha(const Seg& s) {
@@ -591,8 +622,15 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
     segc += pd.nseg;
   }
   if (segc > kMaxSeg || nprob > kMaxProb || total_tout <= 0) return Q8_EINVAL;
-  const int64_t want_u = cdiv(target_waves(), total_tout);
-  const int wmax = max_waves() < max_waves_for(N) ? max_waves() : max_waves_for(N);
+  // Many columns with at least one tile per compute unit: the kernel holds
+  // only 2 waves per SIMD, so twice the waves in smaller workgroups (more of
+  // them resident and more evenly spread over the units) keep the VALUs busy
+  // (C4 gate_up 24576x4096, N=8: 69 -> 53 us); with fewer tiles the K split
+  // such a plan needs costs more than it gains.
+  const bool wide = N >= 3 && total_tout >= num_cus();
+  const int64_t want_u = cdiv(wide ? 2 * target_waves() : target_waves(), total_tout);
+  int wmax = max_waves() < max_waves_for(N) ? max_waves() : max_waves_for(N);
+  if (wide && wmax > 4) wmax = 4;
   // units per tile
   int sbase = 0;
   int64_t U[kMaxProb];
