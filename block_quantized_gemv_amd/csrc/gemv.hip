@@ -622,13 +622,13 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
     segc += pd.nseg;
   }
   if (segc > kMaxSeg || nprob > kMaxProb || total_tout <= 0) return Q8_EINVAL;
-  // Many columns with at least one tile per compute unit: the kernel holds
-  // only 2 waves per SIMD, so twice the waves in smaller workgroups (more of
-  // them resident and more evenly spread over the units) keep the VALUs busy
-  // (C4 gate_up 24576x4096, N=8: 69 -> 53 us); with fewer tiles the K split
-  // such a plan needs costs more than it gains.
-  const bool wide = N >= 3 && total_tout >= num_cus();
-  const int64_t want_u = cdiv(wide ? 2 * target_waves() : target_waves(), total_tout);
+  // Several columns with at least one tile per compute unit: one workgroup
+  // of 4 waves per tile (4 K-units, longer-lived waves, more workgroups
+  // resident) measured best for every N >= 2 (C4 gate_up 24576x4096: N=2
+  // 28.3 -> 25.4 us, N=8 69 -> 52 us); with fewer tiles the K split such a
+  // plan needs costs more than it gains.
+  const bool wide = N >= 2 && total_tout >= num_cus();
+  const int64_t want_u = wide ? 4 : cdiv(target_waves(), total_tout);
   int wmax = max_waves() < max_waves_for(N) ? max_waves() : max_waves_for(N);
   if (wide && wmax > 4) wmax = 4;
   // units per tile
