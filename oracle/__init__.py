@@ -54,6 +54,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_q8_0_gemv.restype = ctypes.c_int
         L.oracle_q8_0_gemv_f64.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P, ctypes.c_int]
         L.oracle_q8_0_gemv_f64.restype = ctypes.c_int
+        L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_f16.restype = ctypes.c_uint16
+        L.oracle_quantize_act.argtypes = [_P, _I64, _I64, _P, _P]
+        L.oracle_quantize_act.restype = ctypes.c_int
+        L.oracle_q8_0_gemv_q8act.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P, _P]
+        L.oracle_q8_0_gemv_q8act.restype = ctypes.c_int
         L.oracle_argmax_f32.argtypes = [_P, _I64]
         L.oracle_argmax_f32.restype = _I64
         L.oracle_argmax_f64.argtypes = [_P, _I64]
@@ -138,6 +144,40 @@ def gemv(aos: np.ndarray, x: np.ndarray, threads: int = 0):
         raise ValueError(f"oracle_q8_0_gemv failed ({rc})")
     if squeeze:
         return y[0], S[0]
+    return y, S
+
+
+def f32_to_f16(v: float) -> int:
+    """binary16 bits of an fp32 value, round to nearest even."""
+    return int(lib().oracle_f32_to_f16(ctypes.c_float(float(v))))
+
+
+def quantize_act(x: np.ndarray):
+    """Integer-activation variant: x [N][K] fp32 -> (qx int8 [N][K], dx
+    binary16 bits [N][K/32]); see oracle_quantize_act."""
+    x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+    N, K = x.shape
+    qx = np.zeros((N, K), dtype=np.int8)
+    dx = np.zeros((N, K // 32), dtype=np.uint16)
+    rc = lib().oracle_quantize_act(_ptr(x), N, K, _ptr(qx), _ptr(dx))
+    if rc:
+        raise ValueError(f"oracle_quantize_act: {rc}")
+    return qx, dx
+
+
+def gemv_q8act(aos: np.ndarray, qx: np.ndarray, dx: np.ndarray):
+    """y [N][M] of the integer-activation variant and its magnitude sums S."""
+    aos = _c(aos, np.uint8)
+    M, nb = aos.shape[0], aos.shape[1]
+    K = nb * 32
+    qx = np.ascontiguousarray(np.atleast_2d(qx), dtype=np.int8)
+    dx = np.ascontiguousarray(np.atleast_2d(dx), dtype=np.uint16)
+    N = qx.shape[0]
+    y = np.zeros((N, M))
+    S = np.zeros((N, M))
+    rc = lib().oracle_q8_0_gemv_q8act(_ptr(aos), M, K, _ptr(qx), _ptr(dx), N, _ptr(y), _ptr(S))
+    if rc:
+        raise ValueError(f"oracle_q8_0_gemv_q8act: {rc}")
     return y, S
 
 

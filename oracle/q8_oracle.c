@@ -147,6 +147,102 @@ int oracle_q8_0_gemv(const uint8_t* aos, int64_t M, int64_t K, const float* x, i
 }
 
 /* ---------------------------------------------------------------------------
+ * Integer-activation variant (opt-in; never the graded fp32 path).  [MOE "Key
+ * implementation notes": each fp32 activation block is quantized to int8
+ * before the dot product, then int8 x int8 products are accumulated and
+ * scaled with the Q8_0 scales.]  The pages leave the quantizer open; the
+ * reading taken makes each block of 32 activations a Q8_0 block like the
+ * weights:
+ *   amax = max_j |x_j|,  d = amax / 127  (fp32 division, round to nearest)
+ *   q_j  = x_j / d (fp32 division) rounded to the nearest integer, ties to
+ *          even; every q_j = 0 when amax == 0
+ *   the block's stored scale is binary16(d), rounded to nearest even, and
+ *   the dot product uses the stored scale:
+ *   y[n][r] = sum_b dw[r][b] * dx[n][b] * sum_j qw[r][b][j] * qx[n][b][j].
+ * ------------------------------------------------------------------------- */
+
+/* double (holding a finite fp32 value) -> binary16 bits, round to nearest
+ * even, by the definition of the format (subnormals below 2^-14, infinity
+ * from 65520 up). */
+static uint16_t f64_to_f16_bits(double v) {
+  uint16_t sign = 0;
+  if (v < 0 || (v == 0 && signbit(v))) {
+    sign = 0x8000;
+    v = -v;
+  }
+  if (v == 0) return sign;
+  if (v >= 65520.0) return (uint16_t)(sign | 0x7c00);
+  int ex;
+  const double m = frexp(v, &ex);  /* v = m * 2^ex, m in [0.5, 1) */
+  const int E = ex - 1;            /* v = (2m) * 2^E, 2m in [1, 2) */
+  if (E < -14) {                   /* subnormal: v = units * 2^-24 */
+    const double units = nearbyint(ldexp(v, 24));
+    return (uint16_t)(sign | (uint16_t)units);  /* 1024 becomes 2^-14 */
+  }
+  double frac = nearbyint((2.0 * m - 1.0) * 1024.0);
+  int e = E;
+  if (frac == 1024.0) {
+    frac = 0.0;
+    ++e;
+  }
+  if (e + 15 >= 31) return (uint16_t)(sign | 0x7c00);
+  return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)frac);
+}
+
+uint16_t oracle_f32_to_f16(float f) { return f64_to_f16_bits((double)f); }
+
+/* x [N][K] fp32 -> qx [N][K] int8, dx [N][K/32] binary16 bits. */
+int oracle_quantize_act(const float* x, int64_t N, int64_t K, int8_t* qx, uint16_t* dx) {
+  if (N < 1 || K <= 0 || K % QK) return -1;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t b = 0; b < K / QK; ++b) {
+      const float* xb = x + n * K + b * QK;
+      float amax = 0.0f;
+      for (int j = 0; j < QK; ++j) {
+        const float a = fabsf(xb[j]);
+        if (a > amax) amax = a;
+      }
+      const float d = amax / 127.0f;
+      for (int j = 0; j < QK; ++j) {
+        float q = 0.0f;
+        if (amax > 0.0f) q = nearbyintf(xb[j] / d);
+        qx[n * K + b * QK + j] = (int8_t)q;
+      }
+      dx[n * (K / QK) + b] = f64_to_f16_bits((double)d);
+    }
+  }
+  return 0;
+}
+
+/* y[n][r] and the magnitude sum S[n][r] = sum_b |dw dx isum_b| (the
+ * tolerance's scale): exact integer block sums, scales applied in double
+ * (each term is exact: 11 + 11 + 20 bits). */
+int oracle_q8_0_gemv_q8act(const uint8_t* aos, int64_t M, int64_t K, const int8_t* qx,
+                           const uint16_t* dx, int64_t N, double* y, double* S) {
+  if (M < 0 || K <= 0 || K % QK || N < 1) return -1;
+  const int64_t nb = K / QK;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t r = 0; r < M; ++r) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t* blk = aos + (r * nb + b) * BLOCK_BYTES;
+        const uint16_t dbits = (uint16_t)((blk[1] << 8) | blk[0]);  /* little-endian */
+        int64_t isum = 0;
+        for (int j = 0; j < QK; ++j)
+          isum += (int64_t)(int8_t)blk[2 + j] * (int64_t)qx[n * K + b * QK + j];
+        const double t =
+            oracle_f16_to_f64(dbits) * oracle_f16_to_f64(dx[n * nb + b]) * (double)isum;
+        acc += t;
+        mag += fabs(t);
+      }
+      y[n * M + r] = acc;
+      if (S) S[n * M + r] = mag;
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Greedy pick: the lowest index among the maxima [AUGUR "Greedy generation";
  * FUSED "API stability": ties resolve to the earliest index].
  * ------------------------------------------------------------------------- */

@@ -397,9 +397,87 @@ def check_qwen_layer():
     assert np.allclose(out, ref, rtol=1e-11, atol=1e-11 * np.abs(ref).max())
 
 
+# ---- integer-activation variant (opt-in path) ---------------------------------
+def check_f32_to_f16_numpy():
+    """The oracle's binary16 encoder against numpy's fp32 -> fp16 conversion
+    (round to nearest even) over all exponent ranges, subnormals, ties and the
+    overflow threshold."""
+    g = np.random.default_rng(40)
+    vals = [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 7e4, 2.0 ** -24, 2.0 ** -25,
+            3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11,
+            2049.0, 2051.0]
+    vals += list(g.standard_normal(3000) * np.exp2(g.integers(-30, 17, 3000)))
+    for v in vals:
+        f = np.float32(v)
+        want = int(np.array([f], dtype=np.float32).astype(np.float16).view(np.uint16)[0])
+        assert oracle.f32_to_f16(f) == want, (v, oracle.f32_to_f16(f), want)
+
+
+def check_quantize_act_closed_forms():
+    """Quantizer: constant blocks map to +-127 with scale |c|/127; integer
+    grids k * 2^e with max |k| = 127 are reproduced exactly (scale 2^e);
+    halves round to even; a zero block gives zeros; negation flips the codes;
+    every code is the nearest integer to x / d."""
+    f16 = lambda a: np.asarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+    for c in (1.0, -3.25, 1e-3, 250.0):
+        q, d = oracle.quantize_act(np.full((1, 32), c, np.float32))
+        assert np.all(q == 127 * np.sign(c)), c
+        assert d[0, 0] == f16(np.float32(abs(c)) / np.float32(127))[()], c
+    g = np.random.default_rng(41)
+    for e in (-12, -3, 0, 5, 9):
+        k = g.integers(-127, 128, (3, 64))
+        k[:, 0], k[:, 32] = 127, -127
+        x = (k * 2.0 ** e).astype(np.float32)
+        q, d = oracle.quantize_act(x)
+        assert np.array_equal(q, k), e
+        assert np.all(d == f16(2.0 ** e)[()]), e
+    x = np.array([[127, 2.5, 3.5, -2.5, 0.5, -0.5, 1.5, -3.5] + [0] * 24], np.float32) * 0.25
+    q, _ = oracle.quantize_act(x)
+    assert list(q[0, :8]) == [127, 2, 4, -2, 0, 0, 2, -4]
+    q, d = oracle.quantize_act(np.zeros((1, 32), np.float32))
+    assert not q.any() and d[0, 0] == 0
+    x = (g.standard_normal((4, 96)) * 3).astype(np.float32)
+    q, d = oracle.quantize_act(x)
+    qn, dn = oracle.quantize_act(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(dn, d)
+    dd = (np.float32(1) * np.abs(x).reshape(4, 3, 32).max(axis=2) / np.float32(127))
+    r = x.reshape(4, 3, 32).astype(np.float64) / dd[..., None].astype(np.float64)
+    assert np.all(np.abs(q.reshape(4, 3, 32) - r) <= 0.5 + 1e-5)
+    assert np.abs(q).max() <= 127
+
+
+def check_gemv_q8act():
+    """The integer-activation product equals (a) exact rational brute force at
+    small sizes and (b) the pinned fp32-path oracle applied to the dequantized
+    activations dx * qx (exact in fp32), at several shapes."""
+    g = np.random.default_rng(42)
+    m = W.draw_matrix(g, 5, 64)
+    x = W.draw_x(g, 2, 64)
+    qx, dx = oracle.quantize_act(x)
+    y, S = oracle.gemv_q8act(m.aos(), qx, dx)
+    dxf = [[Fraction(float(v)) for v in row] for row in dx.view(np.float16).astype(np.float64)]
+    for n in range(2):
+        for r in range(5):
+            tot = Fraction(0)
+            for b in range(2):
+                isum = sum(int(m.qs[r, 32 * b + j]) * int(qx[n, 32 * b + j]) for j in range(32))
+                tot += Fraction(float(m.d[r, b])) * dxf[n][b] * isum
+            assert abs(float(tot) - y[n, r]) <= 4 * 2.0 ** -53 * S[n, r] + 1e-300, (n, r)
+    for (M, K, N) in [(7, 96, 1), (64, 896, 3), (33, 1408, 2)]:
+        m = W.draw_matrix(g, M, K)
+        x = W.draw_x(g, N, K)
+        qx, dx = oracle.quantize_act(x)
+        y, S = oracle.gemv_q8act(m.aos(), qx, dx)
+        xd = (qx.astype(np.float32).reshape(N, -1, 32) *
+              dx.view(np.float16).astype(np.float32)[:, :, None]).reshape(N, K)
+        yr, Sr = oracle.gemv(m.aos(), xd)
+        assert np.all(np.abs(y - yr) <= fp64_tol(K, Sr)), (M, K, N)
+
+
 ALL_CHECKS = [
     check_f16_exhaustive, check_f16_golden, check_hand_examples, check_closed_form_constant,
     check_one_hot, check_bruteforce_k32, check_dense_matvec_shapes, check_invariants,
     check_columns_independent, check_threads_identical, check_argmax, check_router,
-    check_glue, check_moe, check_qwen_layer,
+    check_glue, check_moe, check_qwen_layer, check_f32_to_f16_numpy,
+    check_quantize_act_closed_forms, check_gemv_q8act,
 ]

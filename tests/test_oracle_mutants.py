@@ -47,6 +47,13 @@ MUTANTS = {
     "layer_residual_dropped": ("for (int64_t i = 0; i < hidden; ++i) h[i] += t[i];\n  oracle_rmsnorm",
                                "for (int64_t i = 0; i < hidden; ++i) h[i] = t[i];\n  oracle_rmsnorm"),
     "layer_v_offset": ("qkv + qdim + kvdim,", "qkv + qdim,"),
+    "act_divisor_128": ("const float d = amax / 127.0f;", "const float d = amax / 128.0f;"),
+    "act_round_floor": ("q = nearbyintf(xb[j] / d);", "q = floorf(xb[j] / d);"),
+    "act_amax_signed": ("const float a = fabsf(xb[j]);", "const float a = xb[j];"),
+    "act_f16_truncated": ("double frac = nearbyint((2.0 * m - 1.0) * 1024.0);",
+                          "double frac = floor((2.0 * m - 1.0) * 1024.0);"),
+    "act_dot_column0": ("(int64_t)qx[n * K + b * QK + j];", "(int64_t)qx[b * QK + j];"),
+    "act_weight_unsigned": ("(int64_t)(int8_t)blk[2 + j] *", "(int64_t)blk[2 + j] *"),
 }
 
 RUNNER = r"""
