@@ -196,7 +196,8 @@ def measure_rows(log, cold_bytes=1.2e9):
     cold weight copies (more than `cold_bytes` in rotation, beyond the 256 MB
     Infinity Cache): C1 896x896; the 0.5B layer shapes; lm_head with the fused
     RMSNorm/argmax and the standalone argmax; the 9B-class shapes at N = 1, 2,
-    4, 8; the verify-chunk LM head with one argmax per column; the
+    4, 8; the integer-activation variant on the 9B gate_up shape; the
+    verify-chunk LM head with one argmax per column; the
     Qwen1.5-MoE-shaped FFN (router, scatter + SwiGLU, combine)."""
     import torch
     import block_quantized_gemv_amd as q
@@ -224,6 +225,21 @@ def measure_rows(log, cold_bytes=1.2e9):
         if epi is None:
             ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_GEMV, M, K, N))
             sec = graph_time(lambda i: q.q8_0_gemv(views[i % n], x, y, ws), n)
+        elif epi in ("q8act", "q8act+quant"):
+            # integer activations: codes + binary16 scales replace the fp32 vector
+            qx, dx = q.q8_0_quantize_act(x)
+            ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_GEMV, M, K, N))
+            if epi == "q8act":
+                call = lambda i: q.q8_0_gemv_q8act(views[i % n], qx, dx, y, ws)
+            else:
+                def call(i):
+                    q.q8_0_quantize_act(x, qx, dx)
+                    q.q8_0_gemv_q8act(views[i % n], qx, dx, y, ws)
+            sec = graph_time(call, n)
+            rec(row, what, sec, 1.0625 * M * K + 1.0625 * K * N + 4 * M * N)
+            del views, Wm
+            torch.cuda.empty_cache()
+            return
         elif epi == "col_argmax":
             am = torch.empty(N, dtype=torch.int32, device=dev)
             ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_GEMV_ARGMAX, M, K, N))
@@ -261,6 +277,11 @@ def measure_rows(log, cold_bytes=1.2e9):
     for N in (1, 2, 4, 8):
         gemv_row("a3" if N > 1 else "a2", 24576, 4096, N, f"C4 gate_up 24576x4096 N={N}")
         gemv_row("a3" if N > 1 else "a2", 4096, 12288, N, f"C4 down 4096x12288 N={N}")
+    for N in (1, 8):
+        gemv_row("f3", 24576, 4096, N, f"C4 gate_up 24576x4096 N={N}, int8 activations",
+                 epi="q8act")
+    gemv_row("f3", 24576, 4096, 8, "C4 gate_up 24576x4096 N=8, quantize + int8 activations",
+             epi="q8act+quant")
     for N in (2, 8):
         gemv_row("f4", 151936, 896, N, f"lm_head 151936x896 N={N} + argmax per column (2 launches)",
                  epi="col_argmax")

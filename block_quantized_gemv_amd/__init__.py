@@ -30,7 +30,7 @@ Q8_LAYOUT_ROWS, Q8_LAYOUT_GATE_UP_PAIRS = 0, 1
 Q8_CHAIN_QKV, Q8_CHAIN_H_ATTN, Q8_CHAIN_SWIGLU, Q8_CHAIN_H_OUT = 0, 1, 2, 3
 
 EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv", "q8_0_gemv_fused",
-           "q8_0_gemv_argmax", "q8_0_argmax",
+           "q8_0_gemv_argmax", "q8_0_quantize_act", "q8_0_gemv_q8act", "q8_0_argmax",
            "q8_0_route_topk", "q8_0_moe_gemv", "q8_0_workspace_bytes", "q8_0_gemv_plan",
            "q8_0_strerror", "q8_0_version", "q8_0_chain_workspace_bytes", "q8_0_chain_prepare",
            "q8_0_chain_run", "q8_0_chain_read", "q8_0_chain_status")
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.q8_0_gemv.argtypes = [PW, P, P, I64, I64, I64, P, SZ, P]
         L.q8_0_gemv_fused.argtypes = [PW, P, P, I64, I64, ctypes.POINTER(q8_0_fusion), P, SZ, P]
         L.q8_0_gemv_argmax.argtypes = [PW, P, P, I64, I64, I64, P, P, SZ, P]
+        L.q8_0_quantize_act.argtypes = [P, I64, I64, P, P, P]
+        L.q8_0_gemv_q8act.argtypes = [PW, P, P, P, I64, I64, I64, P, SZ, P]
         L.q8_0_argmax.argtypes = [P, I64, P, P, SZ, P]
         L.q8_0_route_topk.argtypes = [P, I32, I32, P, P, P]
         L.q8_0_moe_gemv.argtypes = [PW, P, P, P, P, I64, I64, I32, I32, PW, P, P, P, SZ, P]
@@ -317,6 +319,42 @@ def q8_0_gemv_argmax(W: PackedQ8, x: torch.Tensor, y: torch.Tensor | None = None
                                                       argmax_out.data_ptr(), wsp, wsb,
                                                       _stream(stream)))
     return y, argmax_out
+
+
+def q8_0_quantize_act(x: torch.Tensor, qx: torch.Tensor | None = None,
+                      dx: torch.Tensor | None = None, stream=None):
+    """Integer-activation variant: x [N][K] fp32 -> (qx int8 [N][K], dx
+    binary16 bits as int16 [N][K/32]); see q8_0_quantize_act in q8gemv.h."""
+    _need(x, torch.float32, "x")
+    x2 = x.reshape(1, -1) if x.dim() == 1 else x
+    N, K = x2.shape
+    if qx is None:
+        qx = torch.empty((N, K), dtype=torch.int8, device=x.device)
+    if dx is None:
+        dx = torch.empty((N, K // 32), dtype=torch.int16, device=x.device)
+    _need(qx, torch.int8, "qx")
+    _need(dx, torch.int16, "dx")
+    if qx.numel() != N * K or dx.numel() != N * (K // 32):
+        raise ValueError("qx / dx sizes do not match x")
+    _check("q8_0_quantize_act", lib().q8_0_quantize_act(x2.data_ptr(), K, N, qx.data_ptr(),
+                                                        dx.data_ptr(), _stream(stream)))
+    return qx, dx
+
+
+def q8_0_gemv_q8act(W: PackedQ8, qx: torch.Tensor, dx: torch.Tensor,
+                    y: torch.Tensor | None = None, workspace=None, stream=None) -> torch.Tensor:
+    """y[N][M] from packed weights and integer activations (q8_0_quantize_act)."""
+    _need(qx, torch.int8, "qx")
+    _need(dx, torch.int16, "dx")
+    N = qx.shape[0]
+    if y is None:
+        y = torch.empty((N, W.M), dtype=torch.float32, device=qx.device)
+    _need(y, torch.float32, "y")
+    wsp, wsb = _ws(workspace, q8_0_workspace_bytes(Q8_OP_GEMV, W.M, W.K, N), qx.device)
+    _check("q8_0_gemv_q8act", lib().q8_0_gemv_q8act(ctypes.byref(W.desc), qx.data_ptr(),
+                                                    dx.data_ptr(), y.data_ptr(), W.M, W.K, N,
+                                                    wsp, wsb, _stream(stream)))
+    return y
 
 
 def q8_0_argmax(v: torch.Tensor, out: torch.Tensor | None = None, workspace=None,

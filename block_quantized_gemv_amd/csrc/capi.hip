@@ -283,6 +283,37 @@ int q8_0_gemv_fused(const q8_0_weights* W, const float* x, float* y, int64_t M, 
   return gemv_common(W, x, y, M, K, 1, fusion, nullptr, workspace, workspace_bytes, stream);
 }
 
+int q8_0_quantize_act(const float* x, int64_t K, int64_t N, int8_t* qx, uint16_t* dx,
+                      void* stream) {
+  if (!shape_ok(1, K) || N < 1 || N > Q8_MAX_N) return Q8_EINVAL;
+  if (!x || !qx || !dx) return Q8_ENULL;
+  int rc;
+  if ((rc = check_dev_aligned(x, 4)) || (rc = check_dev_aligned(qx, 4)) ||
+      (rc = check_dev_aligned(dx, 2)))
+    return rc;
+  return launch_quantize_act(x, K, N, qx, dx, static_cast<hipStream_t>(stream));
+}
+
+int q8_0_gemv_q8act(const q8_0_weights* W, const int8_t* qx, const uint16_t* dx, float* y,
+                    int64_t M, int64_t K, int64_t N, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int rc = check_weights_shape(W, M, K, false);
+  if (rc) return rc;
+  if (N < 1 || N > Q8_MAX_N) return Q8_EINVAL;
+  if (!qx || !dx || !y) return Q8_ENULL;
+  ProbDesc pd;
+  if ((rc = build_gemv(W, nullptr, y, M, K, N, nullptr, &pd))) return rc;
+  pd.seg[0].qx = qx;
+  pd.seg[0].dx = dx;
+  if (M == 0) return Q8_OK;
+  if ((rc = check_weights_ptrs(W)) || (rc = check_dev_aligned(qx, 4)) ||
+      (rc = check_dev_aligned(dx, 2)) || (rc = check_dev_aligned(y, 4)))
+    return rc;
+  if (workspace && (rc = check_dev(workspace))) return rc;
+  return launch_problems(&pd, 1, (int)N, workspace, workspace_bytes,
+                         static_cast<hipStream_t>(stream));
+}
+
 int q8_0_argmax(const float* v, int64_t n, int32_t* out_idx, void* workspace,
                 size_t workspace_bytes, void* stream) {
   if (n < 0 || n >= ((int64_t)1 << 31)) return Q8_EINVAL;

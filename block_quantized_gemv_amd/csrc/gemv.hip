@@ -203,6 +203,152 @@ __device__ __forceinline__ void dot_range(const uint8_t* qs_tile, const uint8_t*
   }
 }
 
+// ---- integer activations (opt-in variant) ------------------------------------
+// Activations quantized per 32-entry block to int8 with a binary16 scale
+// (q8_0_quantize_act).  Per block and column the 32 int8 x int8 products are
+// accumulated exactly in int32 with v_dot4c_i32_i8, whose first operand is
+// read through the DPP row broadcast like the fp32 path: lanes 0..15 of every
+// 16-lane row hold 64 consecutive codes (two blocks) of a column, one dword
+// each, and the dot of dword i of a block reads lane 8 (block & 1) + i.
+// Then acc += float(isum) * (dw * dx).  (The DPP source registers are only
+// written by loads.)  A dot instruction's result must not be read by another
+// VALU instruction within three wait states; chained dots reading it as
+// their accumulator need none.  The compiler does not see through the asm,
+// so the last dot of a chain carries its own s_nop 2.
+
+template <int I, bool LAST>
+__device__ __forceinline__ int dot4_row_bcast(int acc, int xv, uint32_t w) {
+  if (LAST)
+    asm("v_dot4c_i32_i8_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf\n\ts_nop 2"
+        : "+v"(acc)
+        : "v"(xv), "v"(w), "i"(I));
+  else
+    asm("v_dot4c_i32_i8_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc)
+        : "v"(xv), "v"(w), "i"(I));
+  return acc;
+}
+
+// int32 sum of the 32 products of one block: weights q0|q1 (this lane's row),
+// codes in lanes 8 * half + 0..7 of xv's 16-lane row.
+template <int HALF>
+__device__ __forceinline__ int block_isum(u32x4 q0, u32x4 q1, int xv) {
+  int s = 0;
+  s = dot4_row_bcast<8 * HALF + 0, false>(s, xv, q0.x);
+  s = dot4_row_bcast<8 * HALF + 1, false>(s, xv, q0.y);
+  s = dot4_row_bcast<8 * HALF + 2, false>(s, xv, q0.z);
+  s = dot4_row_bcast<8 * HALF + 3, false>(s, xv, q0.w);
+  s = dot4_row_bcast<8 * HALF + 4, false>(s, xv, q1.x);
+  s = dot4_row_bcast<8 * HALF + 5, false>(s, xv, q1.y);
+  s = dot4_row_bcast<8 * HALF + 6, false>(s, xv, q1.z);
+  s = dot4_row_bcast<8 * HALF + 7, true>(s, xv, q1.w);
+  return s;
+}
+
+// One quad of one tile for the integer path: weights, scales, the codes of
+// the quad (two dwords per column and lane) and the 4 activation scales.
+template <int N>
+struct QuadI {
+  u32x4 q[8];
+  u32x2 sc;
+  int xa[N], xb[N];    // codes of blocks 0-1 / 2-3 of the quad
+  uint32_t dxb[N][4];  // binary16 activation scales of the quad's blocks
+};
+
+template <int N>
+__device__ __forceinline__ void quadi_load(QuadI<N>& B, const u32x4* qp, const u32x2* dp, int g,
+                                           const int8_t* qx, const uint16_t* dx, int64_t K,
+                                           int nblk, int lane) {
+  B.sc = __builtin_nontemporal_load(dp + g * 64);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) B.q[i] = __builtin_nontemporal_load(qp + (8 * g + i) * 64);
+  const int xl = lane & 15;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int* xq = reinterpret_cast<const int*>(qx + n * K + 128 * g);
+    B.xa[n] = xq[xl];
+    B.xb[n] = xq[16 + xl];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) B.dxb[n][j] = dx[n * nblk + 4 * g + j];
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void quadi_fma(const QuadI<N>& B, float (&acc)[N]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float dw = f16_to_f32(quad_bits(B.sc, j));
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int xv = j < 2 ? B.xa[n] : B.xb[n];
+      const int isum = (j & 1) ? block_isum<1>(B.q[2 * j], B.q[2 * j + 1], xv)
+                               : block_isum<0>(B.q[2 * j], B.q[2 * j + 1], xv);
+      acc[n] = fmaf((float)isum, dw * f16_to_f32(B.dxb[n][j]), acc[n]);
+    }
+  }
+}
+
+// Integer-activation dot products of the 64 rows of one tile over blocks
+// [b0, b1): whole quads double-buffered, then the blocks of a short last quad.
+template <int N>
+__device__ __forceinline__ void dot_range_i8(const uint8_t* qs_tile, const uint8_t* d_tile, int b0,
+                                             int b1, int lane, const int8_t* qx,
+                                             const uint16_t* dx, int64_t K, int nblk,
+                                             float (&acc)[N]) {
+  const u32x4* qp = reinterpret_cast<const u32x4*>(qs_tile) + lane;
+  const u32x2* dp = reinterpret_cast<const u32x2*>(d_tile) + lane;
+  const int nq = (b1 - b0) >> 2;
+  int b = b0;
+  if (nq > 0) {
+    const int g0 = b0 >> 2;
+    QuadI<N> A, B;
+    quadi_load<N>(A, qp, dp, g0, qx, dx, K, nblk, lane);
+    int it = 0;
+    for (; it + 1 < nq; it += 2) {
+      quadi_load<N>(B, qp, dp, g0 + it + 1, qx, dx, K, nblk, lane);
+      quadi_fma<N>(A, acc);
+      if (it + 2 < nq) quadi_load<N>(A, qp, dp, g0 + it + 2, qx, dx, K, nblk, lane);
+      quadi_fma<N>(B, acc);
+    }
+    if (it < nq) quadi_fma<N>(A, acc);
+    b += 4 * nq;
+  }
+  // blocks of a row's short last quad: lanes 0..7 of each 16-lane row read
+  // the block's 8 code dwords
+  for (; b < b1; ++b) {
+    const u32x2 sc = __builtin_nontemporal_load(dp + (b >> 2) * 64);
+    const u32x4 q0 = __builtin_nontemporal_load(qp + (2 * b) * 64);
+    const u32x4 q1 = __builtin_nontemporal_load(qp + (2 * b + 1) * 64);
+    const float dw = f16_to_f32(quad_bits(sc, b & 3));
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int xv = reinterpret_cast<const int*>(qx + n * K + 32 * b)[lane & 7];
+      const int isum = block_isum<0>(q0, q1, xv);
+      acc[n] = fmaf((float)isum, dw * f16_to_f32(dx[n * nblk + b]), acc[n]);
+    }
+  }
+}
+
+// Quantize fp32 activations [N][K] to int8 codes and binary16 block scales:
+// d = amax / 127, q = x / d rounded to nearest even (fp32 IEEE divisions),
+// zeros for an all-zero block.  32 lanes per block.
+__global__ __launch_bounds__(256) void quantize_act_kernel(const float* __restrict__ x, int64_t K,
+                                                           int64_t nblocks, int8_t* __restrict__ qx,
+                                                           uint16_t* __restrict__ dx) {
+  const int64_t blk = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (blk >= nblocks) return;
+  const int j = threadIdx.x & 31;
+  const int64_t i = blk * 32 + j;  // K % 32 == 0: blocks never cross columns
+  const float v = x[i];
+  float amax = fabsf(v);
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+  const float d = __fdiv_rn(amax, 127.0f);
+  const float q = amax > 0.0f ? __builtin_rintf(__fdiv_rn(v, d)) : 0.0f;
+  qx[i] = (int8_t)(int)q;
+  if (j == 0) dx[blk] = __builtin_bit_cast(uint16_t, (_Float16)d);
+}
+
 // Butterfly all-reduce over the wave; every lane ends with the same bits.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -311,7 +457,7 @@ __device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, 
 
 // ONE: a single problem with a single segment (dense GEMVs and the decode
 // chain): every kernel argument sits at a fixed offset, so no search loops.
-template <int N, bool ONE>
+template <int N, bool ONE, bool I8>
 __global__ __launch_bounds__(64 * max_waves_for(N)) void gemv_kernel(const GemvParams p) {
   extern __shared__ float lds_part[];  // [W][N][64]
   __shared__ int s_last;
@@ -372,8 +518,11 @@ __global__ __launch_bounds__(64 * max_waves_for(N)) void gemv_kernel(const GemvP
       const int b0 = 4 * (int)((int64_t)v * s.G / s.units);
       const int b1e = 4 * (int)((int64_t)(v + 1) * s.G / s.units);
       const int b1 = b1e < s.nblk ? b1e : s.nblk;
-      dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
-                   s.gqa_off, acc);
+      if (I8)
+        dot_range_i8<N>(qs_tile, d_tile, b0, b1, lane, s.qx, s.dx, s.K, s.nblk, acc);
+      else
+        dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
+                     s.gqa_off, acc);
     } else if (lane == 0 && pr.dev_status) {
       atomicOr(pr.dev_status, 1);
     }
@@ -709,10 +858,14 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
 template <int N>
 static hipError_t launch_n(const GemvParams& gp, int wgs, hipStream_t stream) {
   const size_t lds = (size_t)gp.W * N * 64 * sizeof(float);
-  if (gp.nprob == 1 && gp.prob[0].nseg == 1)
-    hipLaunchKernelGGL((gemv_kernel<N, true>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
+  if (gp.seg[0].qx)  // the integer-activation path: one plain problem
+    hipLaunchKernelGGL((gemv_kernel<N, true, true>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
+  else if (gp.nprob == 1 && gp.prob[0].nseg == 1)
+    hipLaunchKernelGGL((gemv_kernel<N, true, false>), dim3(wgs), dim3(64 * gp.W), lds, stream,
+                       gp);
   else
-    hipLaunchKernelGGL((gemv_kernel<N, false>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
+    hipLaunchKernelGGL((gemv_kernel<N, false, false>), dim3(wgs), dim3(64 * gp.W), lds, stream,
+                       gp);
   return hipGetLastError();
 }
 
@@ -783,6 +936,8 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
       sg.gqa_group = sd.gqa_group;
       sg.gqa_hd = sd.gqa_hd;
       sg.gqa_off = sd.gqa_off;
+      sg.qx = sd.qx;
+      sg.dx = sd.dx;
     }
     sbase += pd.nseg;
     wg += (int)(Tout * pr.P);
@@ -811,6 +966,15 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
     if (hipGetLastError() != hipSuccess) return Q8_ELAUNCH;
   }
   return Q8_OK;
+}
+
+int launch_quantize_act(const float* x, int64_t K, int64_t N, int8_t* qx, uint16_t* dx,
+                        hipStream_t stream) {
+  const int64_t nblocks = N * (K / 32);
+  if (nblocks <= 0) return Q8_OK;
+  hipLaunchKernelGGL(quantize_act_kernel, dim3((unsigned)((nblocks + 7) / 8)), dim3(256), 0,
+                     stream, x, K, nblocks, qx, dx);
+  return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
 }
 
 }  // namespace q8

@@ -55,6 +55,8 @@ struct Seg {
   int32_t gqa_group;     // > 0: x index mapping of grouped-query attention
   int32_t gqa_hd;
   int64_t gqa_off;
+  const int8_t* qx;      // integer activations [N][K] (opt-in path), or nullptr
+  const uint16_t* dx;    // their binary16 block scales [N][K / 32]
 };
 
 // One problem: an output of Mout rows computed from R row-tiles per output
@@ -95,6 +97,8 @@ struct GemvParams {
 
 // Host-side launcher shared by the C entry points (gemv.hip).
 struct SegDesc {
+  const int8_t* qx;      // integer activations (opt-in path), or nullptr
+  const uint16_t* dx;
   const q8_0_weights* W;
   const int32_t* eid;
   int32_t slot;
@@ -144,6 +148,8 @@ int launch_argmax(const float* v, int64_t n, int32_t* out, void* ws, size_t ws_b
                   hipStream_t stream);
 int launch_route(const float* logits, int32_t E, int32_t k, int32_t* ids, float* w,
                  hipStream_t stream);
+int launch_quantize_act(const float* x, int64_t K, int64_t N, int8_t* qx, uint16_t* dx,
+                        hipStream_t stream);
 int launch_repack(const void* aos, int64_t M, int64_t K, int32_t layout, void* qs, void* d,
                   hipStream_t stream);
 

@@ -194,6 +194,36 @@ int q8_0_gemv_argmax(const q8_0_weights* W, const float* x, float* y, int64_t M,
                      int64_t N, int32_t* argmax_out, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* ---- integer-activation variant (opt-in; not the fp32 path) ---------------------
+ * The Qwen1.5-MoE PR ("#144", "Key implementation notes") quantizes each
+ * fp32 activation block to int8 before the dot product and accumulates
+ * int8 x int8 products with the Q8_0 scales.  Reading taken for the
+ * quantizer (the page does not give it): each block of 32 activations
+ * becomes a Q8_0 block like the weights,
+ *   d = max_j |x_j| / 127 (fp32 division, round to nearest even),
+ *   q_j = x_j / d (fp32 division) rounded to the nearest integer, ties to
+ *         even (all zero when max_j |x_j| == 0),
+ *   stored scale dx = binary16(d), round to nearest even;
+ * the product uses the stored scale:
+ *   y[n][r] = sum_b dw[r][b] * dx[n][b] * sum_j qw[r][b][j] * qx[n][b][j],
+ * with each block's integer sum exact (int32) and the rest in fp32.  Results
+ * differ from q8_0_gemv by the activation rounding (about 0.4 % of a block's
+ * largest activation per entry), so this is a separate, opt-in product.
+ *
+ * q8_0_quantize_act: x device fp32 [N][K] (4-byte aligned) -> qx device
+ *   int8 [N][K] (4-byte aligned) and dx device binary16 bits [N][K/32]
+ *   (2-byte aligned); K % 32 == 0, 1 <= N <= Q8_MAX_N.  Activation blocks
+ *   whose d would be an fp32 subnormal (max |x| below about 1.5e-36) are
+ *   outside the contract.
+ * q8_0_gemv_q8act: y [N][M] from packed weights W (as q8_0_gemv) and the
+ *   output of q8_0_quantize_act; workspace as q8_0_gemv (Q8_OP_GEMV).
+ * Errors as q8_0_gemv. */
+int q8_0_quantize_act(const float* x, int64_t K, int64_t N, int8_t* qx, uint16_t* dx,
+                      void* stream);
+int q8_0_gemv_q8act(const q8_0_weights* W, const int8_t* qx, const uint16_t* dx, float* y,
+                    int64_t M, int64_t K, int64_t N, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* ---- argmax ------------------------------------------------------------------
  * *out_idx = min{ i : v[i] == max_j v[j] } over fp32 v[0..n) (device), as
  * int32 (device).  Inputs are finite (NaN is outside the contract).

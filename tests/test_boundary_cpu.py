@@ -205,3 +205,24 @@ def test_gemv_argmax_rejects_bad_arguments_on_host():
     eight = q.q8_0_workspace_bytes(q.Q8_OP_GEMV_ARGMAX, 151936, 896, 8)
     assert 0 < one < eight
     assert q.q8_0_workspace_bytes(q.Q8_OP_GEMV_ARGMAX, 151936, 896, 9) == 0
+
+
+def test_q8act_rejects_bad_arguments_on_host():
+    """Shape and null checks of the integer-activation entry points run
+    before any device access."""
+    L = q.lib()
+    dummy = ctypes.c_void_p(16)
+    for K, N in ((33, 1), (0, 1), (64, 0), (64, 9)):
+        assert L.q8_0_quantize_act(dummy, K, N, dummy, dummy, None) == q.Q8_EINVAL, (K, N)
+    assert L.q8_0_quantize_act(None, 64, 1, dummy, dummy, None) == q.Q8_ENULL
+    assert L.q8_0_quantize_act(dummy, 64, 1, dummy, None, None) == q.Q8_ENULL
+    W = _desc(64, 32)
+    for N in (0, 9):
+        assert L.q8_0_gemv_q8act(ctypes.byref(W), dummy, dummy, dummy, 64, 32, N, None, 0,
+                                 None) == q.Q8_EINVAL
+    assert L.q8_0_gemv_q8act(ctypes.byref(W), dummy, dummy, dummy, 64, 33, 1, None, 0,
+                             None) == q.Q8_EINVAL
+    assert L.q8_0_gemv_q8act(ctypes.byref(W), None, dummy, dummy, 64, 32, 1, None, 0,
+                             None) == q.Q8_ENULL
+    assert L.q8_0_gemv_q8act(ctypes.byref(W), dummy, None, dummy, 64, 32, 1, None, 0,
+                             None) == q.Q8_ENULL

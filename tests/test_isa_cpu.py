@@ -7,6 +7,10 @@ cross-compiles, nothing runs).
   inline assembly for that hazard.  The kernels are written so that DPP
   sources are only produced by memory loads; this test scans the generated
   code to hold them to it (every DPP instruction, compiler-made ones too).
+* The integer-activation GEMV chains v_dot4c_i32_i8 in inline assembly; a
+  dot result read by another VALU instruction needs three wait states,
+  which the compiler does not see through the asm.  The scan holds every
+  dot (compiler-made ones too) to that.
 * The path is bandwidth-bound at N <= 8 and uses no matrix cores: no MFMA
   instruction may appear in any kernel.
 """
@@ -83,6 +87,55 @@ def dpp_hazards(insts):
     return n, bad
 
 
+def dot_result_hazards(insts):
+    """Return (n_dot, problems): a problem is a VALU instruction that reads
+    the result of a v_dot* within the three wait states after it (another
+    dot of the same opcode accumulating into that register excepted), or a
+    label inside that window."""
+    n, bad = 0, []
+    for i, (kind, t) in enumerate(insts):
+        if kind != "I" or not t.split()[0].startswith("v_dot"):
+            continue
+        n += 1
+        op = t.split()[0]
+        dst = vregs(t.split(None, 1)[1].split(",")[0])
+        ws, j = 0, i + 1
+        while j < len(insts) and ws < 3:
+            kj, tj = insts[j]
+            if kj == "L":
+                bad.append(f"label after {t}")
+                break
+            mn = tj.split()[0]
+            if mn == "s_nop":
+                ws += int(tj.split()[1], 0) + 1
+            else:
+                if mn.startswith("v_") and len(tj.split()) > 1:
+                    ops = tj.split(None, 1)[1].split(",")
+                    same_acc = mn == op and vregs(ops[0]) == dst
+                    reads = set().union(*(vregs(o.split()[0]) for o in ops[1:] if o.strip()))
+                    if not same_acc and (reads & dst or (mn.endswith("c") or "fmac" in mn)
+                                         and vregs(ops[0]) & dst):
+                        bad.append(f"{t} -> {tj}")
+                ws += 1
+            j += 1
+    return n, bad
+
+
+def test_dot_scanner_finds_planted_hazards():
+    """A conversion reading a dot result one instruction later is flagged;
+    after s_nop 2, or as the next dot's accumulator, it is not."""
+    dot = "v_dot4c_i32_i8_dpp v15, v66, v5 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+    bad_code = [dot, "v_mul_f32_e32 v5, v10, v20", "v_cvt_f32_i32_e32 v4, v15"]
+    ok_code = [dot, "s_nop 2", "v_cvt_f32_i32_e32 v4, v15"]
+    chain = [dot, "v_dot4c_i32_i8_dpp v15, v66, v6 row_newbcast:14 row_mask:0xf bank_mask:0xf",
+             "s_nop 2", "v_cvt_f32_i32_e32 v4, v15"]
+    acc_code = [dot, "v_fmac_f32_e32 v15, v1, v2"]
+    assert len(dot_result_hazards(instructions(bad_code))[1]) == 1
+    assert dot_result_hazards(instructions(ok_code))[1] == []
+    assert dot_result_hazards(instructions(chain))[1] == []
+    assert len(dot_result_hazards(instructions(acc_code))[1]) == 1
+
+
 def test_hazard_scanner_finds_planted_hazards():
     """The scanner itself: a VALU write of the DPP source right before the
     read is flagged, one covered by s_nop 1 is not."""
@@ -105,5 +158,9 @@ def test_kernel_assembly(unit, tmp_path):
     assert bad == [], f"{unit}: {len(bad)} DPP source hazards, first: {bad[:3]}"
     if unit == "gemv.hip":
         assert n > 0, "the GEMV inner loop should use DPP row-broadcast FMAs"
+    nd, badd = dot_result_hazards(insts)
+    assert badd == [], f"{unit}: {len(badd)} dot result hazards, first: {badd[:3]}"
+    if unit == "gemv.hip":
+        assert nd > 0, "the integer-activation GEMV should use v_dot4c"
     mfma = [t for k, t in insts if k == "I" and t.split()[0].startswith("v_mfma")]
     assert mfma == [], f"{unit}: matrix-core instructions found: {mfma[:3]}"
