@@ -103,6 +103,18 @@ def test_persistent_small_ragged_config():
     assert pc.status() == 0
 
 
+def test_persistent_wide_heads():
+    """4 query heads over 4 KV heads of 128 (no grouping, 512 value rows),
+    hidden 512, intermediate 512, 2 layers."""
+    cfg = ChainConfig(hidden=512, n_heads=4, n_kv_heads=4, head_dim=128, intermediate=512,
+                      vocab=2000)
+    aos, lm, pc, h0 = build(cfg, 2, 63)
+    logits, tok, h_out = outputs(pc, cfg)
+    run(pc, h0, logits, tok, h_out)
+    check_stagewise(aos, lm, pc, h0, cfg, logits, tok, h_out, lm_rows=2000)
+    assert pc.status() == 0
+
+
 def test_persistent_lm_head_only_and_no_lm_head():
     cfg = ChainConfig(vocab=3000)
     aos, lm, pc, h0 = build(cfg, 0, 61)
