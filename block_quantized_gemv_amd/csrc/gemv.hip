@@ -795,6 +795,21 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
     if (us > us_max) us = us_max;
     if (us < pd.nseg) us = pd.nseg;
     if (us > blocks) us = blocks;
+    // With few tiles per compute unit the slowest wave sets the pace: prefer
+    // the nearest larger unit count that splits the quads evenly, while the
+    // tile still fits one workgroup (C4 gate_up 24576x4096 at N = 1: 6 units
+    // of 5-6 quads 24.7 us, 8 units of 4 quads 23.0 us).  With many tiles per
+    // compute unit the overlap of workgroups hides the imbalance instead.  (Not
+    // for the integer-activation path or several problems, where it measured
+    // slower.)
+    if (nprob == 1 && pd.nseg == 1 && pd.R == 1 && !pd.seg[0].qx &&
+        total_tout < 2 * (int64_t)num_cus() && blocks % us) {
+      for (int64_t c = us + 1; c < 2 * us && c <= wmax && c <= us_max; ++c)
+        if (blocks % c == 0) {
+          us = c;
+          break;
+        }
+    }
     int64_t su[kMaxSeg];
     distribute(pd, us, blocks, su);
     int64_t usum = 0;
