@@ -631,13 +631,24 @@ __global__ __launch_bounds__(256) void argmax_fold_kernel(const float* __restric
   __shared__ int si[4];
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const float tv = v[i];
-    const int ti = idx[i];
-    if (tv > bv || (tv == bv && ti < bi)) {
-      bv = tv;
-      bi = ti;
+  // loads of 16 entries per thread are issued before any compare, so a
+  // launch waits about one memory round trip per 4096 partials
+  constexpr int kU = 16;
+  for (int i0 = 0; i0 < n; i0 += 256 * kU) {
+    float tv[kU];
+    int ti[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int i = i0 + j * 256 + (int)threadIdx.x;
+      tv[j] = i < n ? v[i] : -INFINITY;
+      ti[j] = i < n ? idx[i] : 0x7fffffff;
     }
+#pragma unroll
+    for (int j = 0; j < kU; ++j)
+      if (tv[j] > bv || (tv[j] == bv && ti[j] < bi)) {
+        bv = tv[j];
+        bi = ti[j];
+      }
   }
   wave_argmax(bv, bi);
   const int wave = threadIdx.x >> 6;

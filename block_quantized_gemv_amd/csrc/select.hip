@@ -56,7 +56,21 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const float* __rest
   const int hi = min(n, lo + per);
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = lo + threadIdx.x; i < hi; i += kArgThreads) better(bv, bi, v[i], i);
+  // kArgPerThread loads per thread are issued before any compare (one memory
+  // round trip per batch rather than one per element)
+  for (int i0 = lo + (int)threadIdx.x; i0 < hi; i0 += kArgThreads * kArgPerThread) {
+    float tv[kArgPerThread];
+#pragma unroll
+    for (int j = 0; j < kArgPerThread; ++j) {
+      const int i = i0 + j * kArgThreads;
+      tv[j] = i < hi ? v[i] : -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < kArgPerThread; ++j) {
+      const int i = i0 + j * kArgThreads;
+      if (i < hi) better(bv, bi, tv[j], i);
+    }
+  }
   wave_best(bv, bi);
   if (lane == 0) {
     sv[wave] = bv;
@@ -74,7 +88,18 @@ __global__ __launch_bounds__(kArgThreads) void argmax_kernel(const float* __rest
   if (!s_last || wave != 0) return;
   bv = -INFINITY;
   bi = 0x7fffffff;
-  for (int g = lane; g < (int)gridDim.x; g += 64) better(bv, bi, ld_dev(wv + g), ld_dev(wi + g));
+  for (int g0 = 0; g0 < (int)gridDim.x; g0 += 256) {
+    float tv[4];
+    int ti[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int g = g0 + 64 * j + lane;
+      tv[j] = g < (int)gridDim.x ? ld_dev(wv + g) : -INFINITY;
+      ti[j] = g < (int)gridDim.x ? ld_dev(wi + g) : 0x7fffffff;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) better(bv, bi, tv[j], ti[j]);
+  }
   wave_best(bv, bi);
   if (lane == 0) {
     *out = bi;
