@@ -48,3 +48,23 @@ def test_verify_chunk_9b_shapes_sampled(mat):
         y = host(q.q8_0_gemv(p, to_dev(x)))
         yr, S = oracle.gemv(aos_rows, x)
         q8tol.check(y[:, rows], yr, S, f"C4 {M}x{K} N={N}")
+
+
+@pytest.mark.parametrize("N", [1, 8])
+def test_integer_activation_9b_gate_up_sampled(N):
+    """The opt-in integer-activation pair at the benchmarked shape: codes and
+    binary16 scales bit-exact over the whole activation, the product on
+    sampled rows within the tolerance of the oracle on the same codes."""
+    c = W.C4
+    M, K = W.C4_SHAPES[W.MAT_GATE_UP]
+    m = W.matrix(c["cfg"], 0, W.MAT_GATE_UP, M, K)
+    x = W.activations(c["cfg"], N, K, layer=10 + N)
+    qx, dx = q.q8_0_quantize_act(to_dev(x))
+    eq, ed = oracle.quantize_act(x)
+    assert np.array_equal(host(qx), eq)
+    assert np.array_equal(host(dx).view(np.uint16), ed)
+    y = host(q.q8_0_gemv_q8act(pack(m), qx, dx))
+    g = np.random.default_rng(77)
+    rows = np.unique(np.concatenate([g.integers(0, M, 512), [0, 63, 64, M - 1]]))
+    yr, S = oracle.gemv_q8act(m.aos()[rows], eq, ed)
+    q8tol.check(y[:, rows], yr, S, f"C4 gate_up int8 activations N={N}")
