@@ -243,6 +243,69 @@ int oracle_q8_0_gemv_q8act(const uint8_t* aos, int64_t M, int64_t K, const int8_
 }
 
 /* ---------------------------------------------------------------------------
+ * Q4_K weights (NEXT-2).  [COGNI "Qwen 3.5 Native Metal": cuda_q4k_gemv_probe
+ * reads the raw GGUF Q4_K block: d, dmin, 12 bytes of packed scales/mins and
+ * 128 bytes of packed nibbles.]  The page lists the fields only; the reading
+ * of their packing is the GGUF one.  A 144-byte block holds 256 consecutive
+ * weights of one row as 8 sub-blocks of 32:
+ *   bytes 0-1    d     binary16, little-endian
+ *   bytes 2-3    dmin  binary16, little-endian
+ *   bytes 4-15   sc[12]: the 6-bit scale s_j and 6-bit min m_j of sub-block j
+ *                  j < 4 : s_j = low 6 bits of sc[j],   m_j = low 6 bits of sc[j+4]
+ *                  j >= 4: s_j = low nibble of sc[j+4]  + 16 * (top 2 bits of sc[j-4])
+ *                          m_j = high nibble of sc[j+4] + 16 * (top 2 bits of sc[j])
+ *   bytes 16-143 qs[128]: the 4-bit quant of weight k lives in byte
+ *                  32 * (k / 64) + k % 32, in its low nibble when k % 64 < 32
+ *                  (sub-block 2 (k / 64)) and its high nibble otherwise
+ *   weight k = d * s_j * q_k - dmin * m_j,  j = k / 32.
+ * Blocks of a row are consecutive; rows are consecutive.
+ * ------------------------------------------------------------------------- */
+#define QKK 256
+#define Q4K_BYTES 144
+
+static double q4k_weight(const uint8_t* blocks, int64_t K, int64_t r, int64_t k) {
+  const uint8_t* b = blocks + (r * (K / QKK) + k / QKK) * Q4K_BYTES;
+  const int kk = (int)(k % QKK), j = kk / 32;
+  const double d = oracle_f16_to_f64((uint16_t)(b[0] | (b[1] << 8)));
+  const double dmin = oracle_f16_to_f64((uint16_t)(b[2] | (b[3] << 8)));
+  const uint8_t* sc = b + 4;
+  int sj, mj;
+  if (j < 4) {
+    sj = sc[j] & 63;
+    mj = sc[j + 4] & 63;
+  } else {
+    sj = (sc[j + 4] & 15) + 16 * (sc[j - 4] >> 6);
+    mj = (sc[j + 4] >> 4) + 16 * (sc[j] >> 6);
+  }
+  const uint8_t byte = b[16 + 32 * (kk / 64) + kk % 32];
+  const int q = (kk % 64 < 32) ? (byte & 15) : (byte >> 4);
+  return d * (double)sj * (double)q - dmin * (double)mj;
+}
+
+void oracle_q4k_dequant_row(const uint8_t* blocks, int64_t K, int64_t r, double* out) {
+  for (int64_t k = 0; k < K; ++k) out[k] = q4k_weight(blocks, K, r, k);
+}
+
+/* y[n][r] = sum_k w[r][k] * x[n][k] over Q4_K rows (ascending k), with the
+ * magnitude sums S; x is fp32 [N][K], widened exactly. */
+int oracle_q4k_gemv(const uint8_t* blocks, int64_t M, int64_t K, const float* x, int64_t N,
+                    double* y, double* S) {
+  if (M < 0 || K <= 0 || K % QKK || N < 1) return -1;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t r = 0; r < M; ++r) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double p = q4k_weight(blocks, K, r, k) * (double)x[n * K + k];
+        acc = acc + p;
+        mag = mag + fabs(p);
+      }
+      y[n * M + r] = acc;
+      if (S) S[n * M + r] = mag;
+    }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Greedy pick: the lowest index among the maxima [AUGUR "Greedy generation";
  * FUSED "API stability": ties resolve to the earliest index].
  * ------------------------------------------------------------------------- */

@@ -474,10 +474,81 @@ def check_gemv_q8act():
         assert np.all(np.abs(y - yr) <= fp64_tol(K, Sr)), (M, K, N)
 
 
+def q4k_weights_from_fields(mtx: W.Q4KMatrix) -> list:
+    """Exact rational weights d * s * q - dmin * m from the drawn fields (never
+    from the packed bytes)."""
+    M, K = mtx.q.shape
+    rows = []
+    for r in range(M):
+        row = []
+        for k in range(K):
+            d = Fraction(float(mtx.d[r, k // 256]))
+            dmin = Fraction(float(mtx.dmin[r, k // 256]))
+            row.append(d * int(mtx.s[r, k // 32]) * int(mtx.q[r, k])
+                       - dmin * int(mtx.m[r, k // 32]))
+        rows.append(row)
+    return rows
+
+
+def check_q4k_bruteforce():
+    """Q4_K oracle against exact rational arithmetic on the drawn fields: the
+    packed bytes are decoded only by the oracle, so a wrong scale/min unpack,
+    nibble position, sub-block index or sign fails here."""
+    g = np.random.default_rng(50)
+    mtx = W.draw_q4k(g, 3, 512)
+    # extremes of every field in some sub-blocks
+    mtx.s[0, :4], mtx.m[0, :4] = [0, 63, 1, 62], [63, 0, 62, 1]
+    mtx.s[1, 8:16], mtx.m[1, 8:16] = 63, 63
+    mtx.q[2, :64] = 15
+    x = W.draw_x(g, 2, 512)
+    y, S = oracle.q4k_gemv(mtx.blocks(), x)
+    wq = q4k_weights_from_fields(mtx)
+    for n in range(2):
+        for r in range(3):
+            tot = sum((w * Fraction(float(xv)) for w, xv in zip(wq[r], x[n])), Fraction(0))
+            mag = sum((abs(w * Fraction(float(xv))) for w, xv in zip(wq[r], x[n])), Fraction(0))
+            assert abs(float(tot) - y[n, r]) <= 512 * 2.0 ** -52 * float(mag) + 1e-300, (n, r)
+            assert abs(float(mag) - S[n, r]) <= 512 * 2.0 ** -52 * float(mag), (n, r)
+
+
+def check_q4k_one_hot_every_position():
+    """x = e_k returns weight k exactly for every k of two blocks, with every
+    sub-block given a distinct (scale, min) pair."""
+    g = np.random.default_rng(51)
+    mtx = W.draw_q4k(g, 2, 512)
+    mtx.s[:] = np.arange(16)[None, :] * 4 + 1
+    mtx.m[:] = 62 - np.arange(16)[None, :] * 3
+    mtx.q[:] = (np.arange(512)[None, :] * 7 + np.array([[0], [5]])) % 16
+    wq = q4k_weights_from_fields(mtx)
+    deq = oracle.q4k_dequant_rows(mtx.blocks(), 512)
+    for r in range(2):
+        assert [float(w) for w in wq[r]] == list(deq[r]), r
+    x = np.eye(512, dtype=np.float32)[[0, 31, 32, 63, 64, 200, 255, 256, 300, 511]]
+    y, _ = oracle.q4k_gemv(mtx.blocks(), x)
+    for i, k in enumerate([0, 31, 32, 63, 64, 200, 255, 256, 300, 511]):
+        assert y[i, 0] == float(wq[0][k]) and y[i, 1] == float(wq[1][k]), k
+
+
+def check_q4k_closed_form_constant():
+    """Constant fields: every weight is d * s * q - dmin * m, so
+    y = (d s q - dmin m) * sum(x), exact with power-of-two d and dmin."""
+    K = 768
+    for (qv, sv, mv) in [(15, 63, 0), (0, 0, 63), (7, 33, 21), (1, 1, 1)]:
+        mtx = W.Q4KMatrix(np.full((2, K), qv, np.uint8), np.full((2, K // 32), sv, np.uint8),
+                          np.full((2, K // 32), mv, np.uint8),
+                          np.full((2, K // 256), np.float16(0.25)),
+                          np.full((2, K // 256), np.float16(0.5)))
+        x = np.random.default_rng(qv).integers(-3, 4, size=(1, K)).astype(np.float32)
+        y, _ = oracle.q4k_gemv(mtx.blocks(), x)
+        want = (0.25 * sv * qv - 0.5 * mv) * float(x.astype(np.float64).sum())
+        assert np.all(y == want), (qv, sv, mv)
+
+
 ALL_CHECKS = [
     check_f16_exhaustive, check_f16_golden, check_hand_examples, check_closed_form_constant,
     check_one_hot, check_bruteforce_k32, check_dense_matvec_shapes, check_invariants,
     check_columns_independent, check_threads_identical, check_argmax, check_router,
     check_glue, check_moe, check_qwen_layer, check_f32_to_f16_numpy,
-    check_quantize_act_closed_forms, check_gemv_q8act,
+    check_quantize_act_closed_forms, check_gemv_q8act, check_q4k_bruteforce,
+    check_q4k_one_hot_every_position, check_q4k_closed_form_constant,
 ]

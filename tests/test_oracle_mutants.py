@@ -54,6 +54,17 @@ MUTANTS = {
                           "double frac = floor((2.0 * m - 1.0) * 1024.0);"),
     "act_dot_column0": ("(int64_t)qx[n * K + b * QK + j];", "(int64_t)qx[b * QK + j];"),
     "act_weight_unsigned": ("(int64_t)(int8_t)blk[2 + j] *", "(int64_t)blk[2 + j] *"),
+    "q4k_scale_min_swapped": ("sj = sc[j] & 63;\n    mj = sc[j + 4] & 63;",
+                              "sj = sc[j + 4] & 63;\n    mj = sc[j] & 63;"),
+    "q4k_high_bits_wrong_byte": ("16 * (sc[j - 4] >> 6);", "16 * (sc[j] >> 6);"),
+    "q4k_high_bits_unshifted": ("+ 16 * (sc[j] >> 6);", "+ (sc[j] >> 6);"),
+    "q4k_nibble_swapped": ("(byte & 15) : (byte >> 4);", "(byte >> 4) : (byte & 15);"),
+    "q4k_group_stride": ("b[16 + 32 * (kk / 64) + kk % 32]", "b[16 + 32 * (kk / 64) + kk % 16]"),
+    "q4k_min_sign": ("- dmin * (double)mj;", "+ dmin * (double)mj;"),
+    "q4k_d_dmin_swapped": ("(uint16_t)(b[0] | (b[1] << 8)));\n  const double dmin",
+                           "(uint16_t)(b[2] | (b[3] << 8)));\n  const double dmin"),
+    "q4k_wrong_subblock": ("const int kk = (int)(k % QKK), j = kk / 32;",
+                           "const int kk = (int)(k % QKK), j = (kk / 32) ^ 1;"),
 }
 
 RUNNER = r"""

@@ -81,6 +81,74 @@ def draw_matrix(g: np.random.Generator, M: int, K: int) -> Q8Matrix:
     return Q8Matrix(qs, d)
 
 
+# --------------------------------------------------------------------------
+# Q4_K (GGUF k-quant, named on the cogni-ml page, "Qwen 3.5 Native Metal" /
+# cuda_q4k_gemv_probe: d, dmin, 12-byte packed scales/mins, 128-byte packed
+# nibbles).  A 144-byte block holds 256 weights of one row as 8 sub-blocks of
+# 32, each with a 6-bit scale s and a 6-bit min m.  The byte arrangement (the
+# GGUF one):
+#   [0:2] d, [2:4] dmin (binary16, little-endian)
+#   [4:16] sc: for j < 4, sc[j] low 6 bits = s_j, sc[j+4] low 6 bits = m_j;
+#          for j >= 4, sc[j+4] = (s_j & 15) | (m_j & 15) << 4, and the top
+#          two bits of sc[j-4] and sc[j] hold s_j >> 4 and m_j >> 4
+#   [16:144] qs: weight k's 4-bit quant in byte 32 (k // 64) + k % 32, low
+#          nibble when k % 64 < 32, high nibble otherwise.
+# Value distributions: quants uniform 0..15, s and m uniform 0..63,
+# d = |N(0,1)| * 0.001 and dmin = |N(0,1)| * 0.004 as binary16.
+# --------------------------------------------------------------------------
+QKK = 256
+Q4K_BYTES = 144
+
+
+@dataclasses.dataclass
+class Q4KMatrix:
+    """A Q4_K matrix as drawn: quants [M][K] 0..15, sub-block scales and mins
+    [M][K/32] 0..63, super-block d and dmin [M][K/256] float16."""
+    q: np.ndarray
+    s: np.ndarray
+    m: np.ndarray
+    d: np.ndarray
+    dmin: np.ndarray
+
+    @property
+    def M(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.q.shape[1]
+
+    def blocks(self) -> np.ndarray:
+        """GGUF Q4_K bytes, shape [M, K/256, 144] uint8."""
+        M, K = self.q.shape
+        if K % QKK:
+            raise ValueError("K must be a multiple of 256")
+        B = K // QKK
+        out = np.zeros((M, B, Q4K_BYTES), dtype=np.uint8)
+        out[:, :, 0:2] = np.ascontiguousarray(self.d, np.float16).view(np.uint8).reshape(M, B, 2)
+        out[:, :, 2:4] = np.ascontiguousarray(self.dmin, np.float16).view(np.uint8).reshape(M, B, 2)
+        s = self.s.astype(np.uint8).reshape(M, B, 8)
+        m = self.m.astype(np.uint8).reshape(M, B, 8)
+        sc = np.zeros((M, B, 12), dtype=np.uint8)
+        sc[:, :, 0:4] = (s[:, :, 0:4] & 63) | ((s[:, :, 4:8] >> 4) << 6)
+        sc[:, :, 4:8] = (m[:, :, 0:4] & 63) | ((m[:, :, 4:8] >> 4) << 6)
+        sc[:, :, 8:12] = (s[:, :, 4:8] & 15) | ((m[:, :, 4:8] & 15) << 4)
+        out[:, :, 4:16] = sc
+        q = self.q.astype(np.uint8).reshape(M, B, 4, 2, 32)  # [group][half][32]
+        out[:, :, 16:] = (q[:, :, :, 0, :] | (q[:, :, :, 1, :] << 4)).reshape(M, B, 128)
+        return out
+
+
+def draw_q4k(g: np.random.Generator, M: int, K: int) -> Q4KMatrix:
+    """Quants, then scales, mins, d, dmin, from one generator."""
+    q = g.integers(0, 16, size=(M, K), dtype=np.uint8)
+    s = g.integers(0, 64, size=(M, K // 32), dtype=np.uint8)
+    m = g.integers(0, 64, size=(M, K // 32), dtype=np.uint8)
+    d = (np.abs(g.standard_normal((M, K // QKK))) * 0.001).astype(np.float16)
+    dmin = (np.abs(g.standard_normal((M, K // QKK))) * 0.004).astype(np.float16)
+    return Q4KMatrix(q, s, m, d, dmin)
+
+
 def draw_x(g: np.random.Generator, N: int, K: int) -> np.ndarray:
     return g.standard_normal((N, K)).astype(np.float32)
 
