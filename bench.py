@@ -191,12 +191,32 @@ def rand_packed(M, K, n_mats, gen):
     return q.PackedQ8(qs.view(torch.uint8), d.view(torch.uint8), M, K, n_mats)
 
 
+def rand_packed_q4k(M, K, n_mats, gen):
+    """Seeded packed Q4_K weights drawn on the device: every nibble and every
+    6-bit scale/min uniform (random bytes), d = |N(0,1)|*0.001 and
+    dmin = |N(0,1)|*0.004 in binary16.  Returns one tensor pair holding n_mats
+    packed matrices back to back (M % 64 == 0, K % 256 == 0)."""
+    import torch
+    import block_quantized_gemv_amd as q
+    assert M % 64 == 0 and K % 256 == 0
+    qb, mb = q.q4k_packed_size(M, K)
+    dev = torch.device("cuda", 0)
+    qs = torch.randint(0, 256, (n_mats * qb,), dtype=torch.uint8, device=dev, generator=gen)
+    meta = torch.randint(0, 256, (n_mats * mb // 16, 16), dtype=torch.uint8, device=dev,
+                         generator=gen)
+    hdr = torch.randn(n_mats * mb // 16, 2, device=dev, generator=gen).abs()
+    hdr = (hdr * torch.tensor([0.001, 0.004], device=dev)).half()
+    meta[:, 0:4] = hdr.view(torch.uint8).view(-1, 4)
+    return qs, meta.view(-1), qb, mb
+
+
 def measure_rows(log, cold_bytes=1.2e9):
     """Every kernel of the path on its own workload, graph-timed over rotating
     cold weight copies (more than `cold_bytes` in rotation, beyond the 256 MB
     Infinity Cache): C1 896x896; the 0.5B layer shapes; lm_head with the fused
     RMSNorm/argmax and the standalone argmax; the 9B-class shapes at N = 1, 2,
-    4, 8; the integer-activation variant on the 9B gate_up shape; the
+    4, 8; the integer-activation variant on the 9B gate_up shape; Q4_K
+    weights on the 9B shapes; the
     verify-chunk LM head with one argmax per column; the
     Qwen1.5-MoE-shaped FFN (router, scatter + SwiGLU, combine)."""
     import torch
@@ -282,6 +302,22 @@ def measure_rows(log, cold_bytes=1.2e9):
                  epi="q8act")
     gemv_row("f3", 24576, 4096, 8, "C4 gate_up 24576x4096 N=8, quantize + int8 activations",
              epi="q8act+quant")
+    # Q4_K weights (NEXT-2) on the same 9B-class shapes
+    for (M, K) in ((24576, 4096), (4096, 12288)):
+        for N in (1, 8):
+            n = max(2, min(64, int(cold_bytes // (0.5625 * M * K)) + 1))
+            qs, meta, qb, mb = rand_packed_q4k(M, K, n, gen)
+            views = [q.PackedQ4K(qs[i * qb:(i + 1) * qb], meta[i * mb:(i + 1) * mb], M, K)
+                     for i in range(n)]
+            x = torch.randn(N, K, device=dev, generator=gen)
+            y = torch.empty(N, M, device=dev)
+            ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_Q4K_GEMV, M, K, N))
+            sec = graph_time(lambda i: q.q4k_gemv(views[i % n], x, y, ws), n)
+            launches = "" if N <= 4 else " (2 launches)"
+            rec("n2", f"C4-shaped {M}x{K} Q4_K N={N}{launches}", sec,
+                0.5625 * M * K + 4 * K * N + 4 * M * N)
+            del views, qs, meta
+            torch.cuda.empty_cache()
     for N in (2, 8):
         gemv_row("f4", 151936, 896, N, f"lm_head 151936x896 N={N} + argmax per column (2 launches)",
                  epi="col_argmax")

@@ -283,6 +283,55 @@ int q8_0_gemv_fused(const q8_0_weights* W, const float* x, float* y, int64_t M, 
   return gemv_common(W, x, y, M, K, 1, fusion, nullptr, workspace, workspace_bytes, stream);
 }
 
+// ---- Q4_K ----------------------------------------------------------------------
+static bool q4k_shape_ok(int64_t M, int64_t K) { return shape_ok(M, K) && K % 256 == 0; }
+
+int q4k_packed_size(int64_t M, int64_t K, size_t* qs_bytes, size_t* meta_bytes) {
+  if (!qs_bytes || !meta_bytes) return Q8_ENULL;
+  if (!q4k_shape_ok(M, K)) return Q8_EINVAL;
+  const int64_t T = cdiv(M, kTile);
+  *qs_bytes = (size_t)(T * kTile * (K / 2));
+  *meta_bytes = (size_t)(T * kTile * (K / 256) * 16);
+  return Q8_OK;
+}
+
+int q4k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* meta, void* stream) {
+  if (!q4k_shape_ok(M, K)) return Q8_EINVAL;
+  if (!blocks || !qs || !meta) return Q8_ENULL;
+  if (M == 0) return Q8_OK;
+  int rc;
+  if ((rc = check_dev_aligned(blocks, 4)) || (rc = check_dev_aligned(qs, 16)) ||
+      (rc = check_dev_aligned(meta, 16)))
+    return rc;
+  return launch_q4k_repack(blocks, M, K, qs, meta, static_cast<hipStream_t>(stream));
+}
+
+int q4k_gemv(const q4k_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!W) return Q8_ENULL;
+  if (W->M != M || W->K != K || !q4k_shape_ok(M, K) || N < 1 || N > Q8_MAX_N) return Q8_EINVAL;
+  if (!x || !y || !W->qs || !W->meta) return Q8_ENULL;
+  if (M == 0) return Q8_OK;
+  int rc;
+  if ((rc = check_dev_aligned(W->qs, 16)) || (rc = check_dev_aligned(W->meta, 16)) ||
+      (rc = check_dev_aligned(x, 4)) || (rc = check_dev_aligned(y, 4)))
+    return rc;
+  if (workspace && (rc = check_dev(workspace))) return rc;
+  // the launch machinery sees the nibbles as qs and the block headers as d;
+  // columns go kMaxQ4kN at a time (each launch reads the weights once)
+  const q8_0_weights w8 = {W->qs, W->meta, M, K, 1, 0, 0, Q8_LAYOUT_ROWS, 0};
+  for (int64_t n0 = 0; n0 < N; n0 += kMaxQ4kN) {
+    const int64_t n = N - n0 < kMaxQ4kN ? N - n0 : kMaxQ4kN;
+    ProbDesc pd;
+    if ((rc = build_gemv(&w8, x + n0 * K, y + n0 * M, M, K, n, nullptr, &pd))) return rc;
+    pd.seg[0].fmt = FMT_Q4K;
+    if ((rc = launch_problems(&pd, 1, (int)n, workspace, workspace_bytes,
+                              static_cast<hipStream_t>(stream))))
+      return rc;
+  }
+  return Q8_OK;
+}
+
 int q8_0_quantize_act(const float* x, int64_t K, int64_t N, int8_t* qx, uint16_t* dx,
                       void* stream) {
   if (!shape_ok(1, K) || N < 1 || N > Q8_MAX_N) return Q8_EINVAL;
@@ -375,6 +424,11 @@ size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t
                             int32_t flags) {
   Plan plan;
   if (op == Q8_OP_ARGMAX) return argmax_ws_bytes(M);
+  if (op == Q8_OP_Q4K_GEMV) {
+    // the same plan as a Q8_0 GEMV of this shape
+    if (K % 256) return 0;
+    op = Q8_OP_GEMV;
+  }
   if (op == Q8_OP_GEMV || op == Q8_OP_GEMV_FUSED || op == Q8_OP_GEMV_ARGMAX) {
     if (!shape_ok(M, K) || M == 0) return 0;
     q8_0_weights W = {nullptr, nullptr, M, K, 1, 0, 0};

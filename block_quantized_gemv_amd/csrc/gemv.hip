@@ -203,6 +203,126 @@ __device__ __forceinline__ void dot_range(const uint8_t* qs_tile, const uint8_t*
   }
 }
 
+// ---- Q4_K weights ------------------------------------------------------------
+// A quad is half of a 256-weight block: 4 sub-blocks of 32.  Sub-block j of
+// a row is 16 bytes whose byte i holds weights i (low nibble) and i + 16 (high
+// nibble), matching the activations' lanes (lanes 0..15 of a row hold x[i]
+// and x[i + 16]), so weight i and i + 16 both read lane i through the row
+// broadcast.  Per sub-block and column: y += d s * sum(q x) - dmin m * sum(x),
+// the sum of the 32 activations taken by DPP rotations within the row.
+
+template <int N>
+struct QuadQ4 {
+  u32x4 q[4];
+  u32x4 meta;  // d, dmin (binary16), 12 bytes of 6-bit scales and mins
+  XBlock<N> x[4];
+};
+
+template <int N>
+__device__ __forceinline__ void q4_load(QuadQ4<N>& B, const u32x4* qp, const u32x4* mp, int g,
+                                        const float* x, int64_t xs, int xl) {
+  B.meta = __builtin_nontemporal_load(mp + (g >> 1) * 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) B.q[i] = __builtin_nontemporal_load(qp + (4 * g + i) * 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_xblock<N>(x + 32 * (4 * g + i), xs, xl, B.x[i]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Scale s and min m (6 bits each) of sub-block i of quad half h.
+__device__ __forceinline__ void q4_scale_min(u32x4 meta, int h, int i, float& s, float& m) {
+  if (h == 0) {
+    s = (float)((meta.y >> (8 * i)) & 63u);
+    m = (float)((meta.z >> (8 * i)) & 63u);
+  } else {
+    s = (float)(((meta.w >> (8 * i)) & 15u) | (((meta.y >> (8 * i + 6)) & 3u) << 4));
+    m = (float)(((meta.w >> (8 * i + 4)) & 15u) | (((meta.z >> (8 * i + 6)) & 3u) << 4));
+  }
+}
+
+template <int N, int I>
+__device__ __forceinline__ void q4_dword(uint32_t w, const XBlock<N>& X, float (&p)[N]) {
+  // Byte b of a dword to fp32 is one v_cvt_f32_ubyteN; the nibble masks are
+  // written as opaque VALU ops so the compiler keeps that form instead of
+  // folding each mask into a per-weight bit-field extract (two ops a weight).
+  uint32_t lo, hi;
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w));
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w >> 4));
+  const float l0 = (float)(lo & 255u), l1 = (float)((lo >> 8) & 255u);
+  const float l2 = (float)((lo >> 16) & 255u), l3 = (float)(lo >> 24);
+  const float h0 = (float)(hi & 255u), h1 = (float)((hi >> 8) & 255u);
+  const float h2 = (float)((hi >> 16) & 255u), h3 = (float)(hi >> 24);
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    fmac_row_bcast<4 * I + 0>(p[n], X.a[n], l0);
+    fmac_row_bcast<4 * I + 1>(p[n], X.a[n], l1);
+    fmac_row_bcast<4 * I + 2>(p[n], X.a[n], l2);
+    fmac_row_bcast<4 * I + 3>(p[n], X.a[n], l3);
+    fmac_row_bcast<4 * I + 0>(p[n], X.b[n], h0);
+    fmac_row_bcast<4 * I + 1>(p[n], X.b[n], h1);
+    fmac_row_bcast<4 * I + 2>(p[n], X.b[n], h2);
+    fmac_row_bcast<4 * I + 3>(p[n], X.b[n], h3);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void q4_fma(const QuadQ4<N>& B, int h, float (&acc)[N]) {
+  const float d = f16_to_f32(B.meta.x & 0xffffu), dmin = f16_to_f32(B.meta.x >> 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float s, m;
+    q4_scale_min(B.meta, h, i, s, m);
+    float p[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) p[n] = 0.f;
+    q4_dword<N, 0>(B.q[i].x, B.x[i], p);
+    q4_dword<N, 1>(B.q[i].y, B.x[i], p);
+    q4_dword<N, 2>(B.q[i].z, B.x[i], p);
+    q4_dword<N, 3>(B.q[i].w, B.x[i], p);
+    const float ds = d * s, dm = dmin * m;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      // sum of the sub-block's 32 activations: every lane of a 16-lane row
+      // holds two of them; rotations add the row
+      float sx = B.x[i].a[n] + B.x[i].b[n];
+      sx = dpp_add<0x128>(sx);  // row_ror:8
+      sx = dpp_add<0x124>(sx);  // row_ror:4
+      sx = dpp_add<0x122>(sx);  // row_ror:2
+      sx = dpp_add<0x121>(sx);  // row_ror:1
+      acc[n] = fmaf(ds, p[n], acc[n]);
+      acc[n] = fmaf(-dm, sx, acc[n]);
+    }
+  }
+}
+
+// Q4_K dot products of the 64 rows of one tile over 32-weight blocks
+// [b0, b1) (multiples of 4: whole quads), quads double-buffered.
+template <int N>
+__device__ __forceinline__ void dot_range_q4k(const uint8_t* qs_tile, const uint8_t* meta_tile,
+                                              int b0, int b1, int lane, const float* x,
+                                              int64_t xs, float (&acc)[N]) {
+  const u32x4* qp = reinterpret_cast<const u32x4*>(qs_tile) + lane;
+  const u32x4* mp = reinterpret_cast<const u32x4*>(meta_tile) + lane;
+  const int xl = lane & 15;
+  const int g0 = b0 >> 2, nq = (b1 - b0) >> 2;
+  if (nq <= 0) return;
+  QuadQ4<N> A, B;
+  q4_load<N>(A, qp, mp, g0, x, xs, xl);
+  int it = 0;
+  for (; it + 1 < nq; it += 2) {
+    q4_load<N>(B, qp, mp, g0 + it + 1, x, xs, xl);
+    q4_fma<N>(A, (g0 + it) & 1, acc);
+    if (it + 2 < nq) q4_load<N>(A, qp, mp, g0 + it + 2, x, xs, xl);
+    q4_fma<N>(B, (g0 + it + 1) & 1, acc);
+  }
+  if (it < nq) q4_fma<N>(A, (g0 + it) & 1, acc);
+}
+
 // ---- integer activations (opt-in variant) ------------------------------------
 // Activations quantized per 32-entry block to int8 with a binary16 scale
 // (q8_0_quantize_act).  Per block and column the 32 int8 x int8 products are
@@ -457,7 +577,9 @@ __device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, 
 
 // ONE: a single problem with a single segment (dense GEMVs and the decode
 // chain): every kernel argument sits at a fixed offset, so no search loops.
-template <int N, bool ONE, bool I8>
+// MODE: 0 Q8_0 weights and fp32 activations; 1 integer activations; 2 Q4_K
+// weights and fp32 activations.
+template <int N, bool ONE, int MODE>
 __global__ __launch_bounds__(64 * max_waves_for(N)) void gemv_kernel(const GemvParams p) {
   extern __shared__ float lds_part[];  // [W][N][64]
   __shared__ int s_last;
@@ -512,14 +634,18 @@ __global__ __launch_bounds__(64 * max_waves_for(N)) void gemv_kernel(const GemvP
     }
     if (ok) {
       const int t = ot + tsel * pr.Tout;
-      const uint8_t* qs_tile = s.qs + (int64_t)e * s.qs_stride + (int64_t)t * kTile * s.K;
+      // bytes of one packed tile's quants: 64 rows of K (Q8_0) or K / 2 (Q4_K)
+      const uint8_t* qs_tile =
+          s.qs + (int64_t)e * s.qs_stride + (int64_t)t * kTile * (MODE == 2 ? s.K / 2 : s.K);
       const uint8_t* d_tile = s.d + (int64_t)e * s.d_stride + (int64_t)t * s.G * 512;
       // units own whole scale quads (4 blocks); only a row's last may be short
       const int b0 = 4 * (int)((int64_t)v * s.G / s.units);
       const int b1e = 4 * (int)((int64_t)(v + 1) * s.G / s.units);
       const int b1 = b1e < s.nblk ? b1e : s.nblk;
-      if (I8)
+      if (MODE == 1)
         dot_range_i8<N>(qs_tile, d_tile, b0, b1, lane, s.qx, s.dx, s.K, s.nblk, acc);
+      else if (MODE == 2)
+        dot_range_q4k<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, acc);
       else
         dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
                      s.gqa_off, acc);
@@ -885,13 +1011,16 @@ template <int N>
 static hipError_t launch_n(const GemvParams& gp, int wgs, hipStream_t stream) {
   const size_t lds = (size_t)gp.W * N * 64 * sizeof(float);
   if (gp.seg[0].qx)  // the integer-activation path: one plain problem
-    hipLaunchKernelGGL((gemv_kernel<N, true, true>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
-  else if (gp.nprob == 1 && gp.prob[0].nseg == 1)
-    hipLaunchKernelGGL((gemv_kernel<N, true, false>), dim3(wgs), dim3(64 * gp.W), lds, stream,
-                       gp);
+    hipLaunchKernelGGL((gemv_kernel<N, true, 1>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
+  else if (gp.seg[0].fmt == FMT_Q4K) {  // Q4_K weights: one plain problem, N <= 4
+    if constexpr (N <= kMaxQ4kN)
+      hipLaunchKernelGGL((gemv_kernel<N, true, 2>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
+    else
+      return hipErrorInvalidValue;
+  } else if (gp.nprob == 1 && gp.prob[0].nseg == 1)
+    hipLaunchKernelGGL((gemv_kernel<N, true, 0>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
   else
-    hipLaunchKernelGGL((gemv_kernel<N, false, false>), dim3(wgs), dim3(64 * gp.W), lds, stream,
-                       gp);
+    hipLaunchKernelGGL((gemv_kernel<N, false, 0>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
   return hipGetLastError();
 }
 
@@ -964,6 +1093,7 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
       sg.gqa_off = sd.gqa_off;
       sg.qx = sd.qx;
       sg.dx = sd.dx;
+      sg.fmt = sd.fmt;
     }
     sbase += pd.nseg;
     wg += (int)(Tout * pr.P);

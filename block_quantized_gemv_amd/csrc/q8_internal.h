@@ -31,6 +31,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Problem flags (the epilogue/prologue work of one problem).
 enum : int32_t { F_RMSNORM = 1, F_RESIDUAL = 2, F_SWIGLU = 4, F_ARGMAX = 8, F_PAIRED = 16 };
+// Weight formats: Q8_0 (qs = quants, d = scales) or Q4_K (qs = nibbles of
+// 32-weight sub-blocks, d = 16-byte block headers: d, dmin, scales/mins).
+enum : int32_t { FMT_Q8_0 = 0, FMT_Q4K = 1 };
+// Columns per Q4_K launch (more would spill registers; callers split N).
+constexpr int kMaxQ4kN = 4;
 // How a segment's partial sum is weighted in the fold.
 enum : int32_t { A_ONE = 0, A_PTR = 1, A_SIGMOID = 2 };
 
@@ -57,6 +62,7 @@ struct Seg {
   int64_t gqa_off;
   const int8_t* qx;      // integer activations [N][K] (opt-in path), or nullptr
   const uint16_t* dx;    // their binary16 block scales [N][K / 32]
+  int32_t fmt;           // FMT_*: how qs / d are packed
 };
 
 // One problem: an output of Mout rows computed from R row-tiles per output
@@ -99,6 +105,7 @@ struct GemvParams {
 struct SegDesc {
   const int8_t* qx;      // integer activations (opt-in path), or nullptr
   const uint16_t* dx;
+  int32_t fmt;           // FMT_*
   const q8_0_weights* W;
   const int32_t* eid;
   int32_t slot;
@@ -148,6 +155,8 @@ int launch_argmax(const float* v, int64_t n, int32_t* out, void* ws, size_t ws_b
                   hipStream_t stream);
 int launch_route(const float* logits, int32_t E, int32_t k, int32_t* ids, float* w,
                  hipStream_t stream);
+int launch_q4k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* meta,
+                      hipStream_t stream);
 int launch_quantize_act(const float* x, int64_t K, int64_t N, int8_t* qx, uint16_t* dx,
                         hipStream_t stream);
 int launch_repack(const void* aos, int64_t M, int64_t K, int32_t layout, void* qs, void* d,

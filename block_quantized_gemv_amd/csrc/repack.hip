@@ -84,4 +84,78 @@ int launch_repack(const void* aos, int64_t M, int64_t K, int32_t layout, void* q
   return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
 }
 
+// ---- Q4_K ------------------------------------------------------------------
+// GGUF Q4_K blocks ("skuznetsov/cogni-ml" README, cuda_q4k_gemv_probe: d,
+// dmin, 12-byte packed scales/mins, 128-byte packed nibbles; 144 bytes per 256
+// weights of one row) move into:
+//   qs:   per 64-row tile, per 32-weight sub-block, 16 bytes of each of the 64
+//         rows back to back; byte i holds the sub-block's weights i (low
+//         nibble) and i + 16 (high nibble).  In a GGUF block, sub-block j's
+//         weights are the low (j even) or high (j odd) nibbles of the 32 bytes
+//         at 16 + 32 * (j / 2).
+//   meta: per 64-row tile, per 256-weight block, the block's first 16 bytes
+//         (d, dmin, the 12 scale/min bytes) of each of the 64 rows.
+// Byte moves and nibble moves only; padding rows are zeros.
+__global__ __launch_bounds__(256) void q4k_repack_qs_kernel(const uint32_t* __restrict__ src,
+                                                            int64_t M, int64_t K,
+                                                            u32x4* __restrict__ qs,
+                                                            int64_t total) {
+  const int64_t nsub = K / 32, nsb = K / 256;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lane = idx & 63;
+    const int64_t c = (idx >> 6) % nsub;
+    const int64_t t = (idx >> 6) / nsub;
+    const int64_t r = t * 64 + lane;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (r < M) {
+      const int j = (int)(c & 7);
+      // the 32 bytes of sub-block pair j / 2 (144-byte blocks: dword aligned)
+      const uint32_t* g = src + ((r * nsb + c / 8) * 144 + 16 + 32 * (j >> 1)) / 4;
+      const int sh = (j & 1) * 4;
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = ((g[i] >> sh) & 0x0F0F0F0Fu) | (((g[4 + i] >> sh) & 0x0F0F0F0Fu) << 4);
+      out = u32x4{o[0], o[1], o[2], o[3]};
+    }
+    qs[idx] = out;
+  }
+}
+
+__global__ __launch_bounds__(256) void q4k_repack_meta_kernel(const uint32_t* __restrict__ src,
+                                                              int64_t M, int64_t K,
+                                                              u32x4* __restrict__ meta,
+                                                              int64_t total) {
+  const int64_t nsb = K / 256;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lane = idx & 63;
+    const int64_t b = (idx >> 6) % nsb;
+    const int64_t t = (idx >> 6) / nsb;
+    const int64_t r = t * 64 + lane;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (r < M) {
+      const uint32_t* h = src + (r * nsb + b) * 144 / 4;
+      out = u32x4{h[0], h[1], h[2], h[3]};
+    }
+    meta[idx] = out;
+  }
+}
+
+int launch_q4k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* meta,
+                      hipStream_t stream) {
+  const int64_t T = cdiv(M, kTile);
+  const int64_t nq = T * 64 * (K / 32);
+  const int64_t nm = T * 64 * (K / 256);
+  const auto* s32 = static_cast<const uint32_t*>(blocks);
+  auto grid = [](int64_t n) { return (unsigned)(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536); };
+  hipLaunchKernelGGL(q4k_repack_qs_kernel, dim3(grid(nq)), dim3(256), 0, stream, s32, M, K,
+                     static_cast<u32x4*>(qs), nq);
+  if (hipGetLastError() != hipSuccess) return Q8_ELAUNCH;
+  hipLaunchKernelGGL(q4k_repack_meta_kernel, dim3(grid(nm)), dim3(256), 0, stream, s32, M, K,
+                     static_cast<u32x4*>(meta), nm);
+  return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
+}
+
 }  // namespace q8

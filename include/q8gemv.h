@@ -224,6 +224,51 @@ int q8_0_gemv_q8act(const q8_0_weights* W, const int8_t* qx, const uint16_t* dx,
                     int64_t M, int64_t K, int64_t N, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* ---- Q4_K weights (NEXT-2) -------------------------------------------------------
+ * GGUF Q4_K ("skuznetsov/cogni-ml" README, cuda_q4k_gemv_probe: d, dmin,
+ * 12-byte packed scales/mins, 128-byte packed nibbles).  Reading of the packing
+ * (the page lists the fields; the arrangement is GGUF's): a 144-byte block holds
+ * 256 weights of one row as 8 sub-blocks of 32;
+ *   bytes 0-1 d, 2-3 dmin (binary16, little-endian);
+ *   bytes 4-15 sc[12]: sub-block j's 6-bit scale s_j and min m_j are, for
+ *     j < 4, the low 6 bits of sc[j] and sc[j+4]; for j >= 4, the low and high
+ *     nibbles of sc[j+4] plus 16 times the top two bits of sc[j-4] and sc[j];
+ *   bytes 16-143: weight k's 4-bit quant q_k in byte 32 (k / 64) + k % 32,
+ *     low nibble when k % 64 < 32, else high nibble;
+ *   w_k = d * s_j * q_k - dmin * m_j, j = k / 32.
+ *
+ * Packed layout (q4k_repack), T = ceil(M / 64) tiles of 64 rows:
+ *  qs:   T * (K/32) * 64 * 16 bytes; sub-block c of row r is the 16 bytes at
+ *        ((t * (K/32) + c) * 64 + i) * 16 (t = r / 64, i = r % 64), whose byte
+ *        b holds the sub-block's weights b (low nibble) and b + 16 (high).
+ *  meta: T * (K/256) * 64 * 16 bytes; block B of row r: its first 16 GGUF bytes
+ *        (d, dmin, sc) at ((t * (K/256) + B) * 64 + i) * 16.
+ *  Rows M .. 64T-1 are zero.  Both 16-byte aligned. */
+typedef struct {
+  const void* qs;    /* device, packed nibbles */
+  const void* meta;  /* device, packed block headers */
+  int64_t M, K;
+} q4k_weights;
+
+/* Bytes of the packed nibbles and headers of one M x K Q4_K matrix.
+ * Errors: Q8_ENULL, Q8_EINVAL (M < 0, K <= 0, K % 256, K > Q8_MAX_K). */
+int q4k_packed_size(int64_t M, int64_t K, size_t* qs_bytes, size_t* meta_bytes);
+
+/* Load-time repack of GGUF Q4_K blocks (device, M * K/256 blocks of 144 bytes,
+ * row-major, 4-byte aligned) into qs and meta (device, q4k_packed_size() bytes,
+ * 16-byte aligned; every byte written).  Nibble and byte moves only.
+ * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_ELAUNCH. */
+int q4k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* meta, void* stream);
+
+/* y[n][r] = sum_k w[r][k] * x[n][k] with Q4_K weights, x fp32 [N][K] and y
+ * fp32 [N][M] (device, 4-byte aligned), 1 <= N <= Q8_MAX_N, K % 256 == 0.
+ * Each sub-block adds d s_j * sum_k q_k x_k - dmin m_j * sum_k x_k in fp32.
+ * Columns are processed 4 per launch (N > 4 reads the weights twice).
+ * Workspace: q8_0_workspace_bytes(Q8_OP_Q4K_GEMV, M, K, N, 0, 0, 0) bytes
+ * (device; NULL when 0), as for q8_0_gemv.  Errors as q8_0_gemv. */
+int q4k_gemv(const q4k_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
+             void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- argmax ------------------------------------------------------------------
  * *out_idx = min{ i : v[i] == max_j v[j] } over fp32 v[0..n) (device), as
  * int32 (device).  Inputs are finite (NaN is outside the contract).
@@ -383,6 +428,7 @@ int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
  * op Q8_OP_GEMV: (M, K, N) of q8_0_gemv.
  * op Q8_OP_GEMV_FUSED: (M, K, epilogue flags in N) of q8_0_gemv_fused.
  * op Q8_OP_GEMV_ARGMAX: (M, K, N) of q8_0_gemv_argmax.
+ * op Q8_OP_Q4K_GEMV: (M, K, N) of q4k_gemv.
  * op Q8_OP_ARGMAX: (n, 0, 0).
  * op Q8_OP_MOE_SCATTER / Q8_OP_MOE_COMBINE: (M, K, n_slots) with the
  *   shared expert's shape in (M2, K2) (0, 0 for none) and mode flags in flags.
@@ -393,6 +439,7 @@ int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
 #define Q8_OP_MOE_SCATTER 4
 #define Q8_OP_MOE_COMBINE 5
 #define Q8_OP_GEMV_ARGMAX 6
+#define Q8_OP_Q4K_GEMV 7
 size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t M2, int64_t K2,
                             int32_t flags);
 

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "q8gemv.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(q8_0_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b((?:q8_0|q4k)_\w+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -226,3 +226,28 @@ def test_q8act_rejects_bad_arguments_on_host():
                              None) == q.Q8_ENULL
     assert L.q8_0_gemv_q8act(ctypes.byref(W), dummy, None, dummy, 64, 32, 1, None, 0,
                              None) == q.Q8_ENULL
+
+
+def test_q4k_rejects_bad_arguments_on_host():
+    """Shape and null checks of the Q4_K entry points (no device access)."""
+    L = q.lib()
+    dummy = ctypes.c_void_p(16)
+    qb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.q4k_packed_size(130, 512, ctypes.byref(qb), ctypes.byref(mb)) == q.Q8_OK
+    assert (qb.value, mb.value) == (192 * 256, 192 * 2 * 16)  # 3 tiles of 64 rows
+    for K in (0, 32, 288, 500):
+        assert L.q4k_packed_size(64, K, ctypes.byref(qb), ctypes.byref(mb)) == q.Q8_EINVAL, K
+        assert L.q4k_repack(dummy, 64, K, dummy, dummy, None) == q.Q8_EINVAL, K
+    assert L.q4k_packed_size(64, 256, None, ctypes.byref(mb)) == q.Q8_ENULL
+    assert L.q4k_repack(None, 64, 256, dummy, dummy, None) == q.Q8_ENULL
+    W = q.q4k_weights(16, 16, 64, 256)
+    for N in (0, 9):
+        assert L.q4k_gemv(ctypes.byref(W), dummy, dummy, 64, 256, N, None, 0, None) == q.Q8_EINVAL
+    assert L.q4k_gemv(ctypes.byref(W), dummy, dummy, 64, 512, 1, None, 0, None) == q.Q8_EINVAL
+    assert L.q4k_gemv(None, dummy, dummy, 64, 256, 1, None, 0, None) == q.Q8_ENULL
+    assert L.q4k_gemv(ctypes.byref(W), None, dummy, 64, 256, 1, None, 0, None) == q.Q8_ENULL
+    # the workspace of a Q4_K GEMV is that of a Q8_0 GEMV of the same shape
+    for (M, K, N) in [(151936, 1024, 1), (4096, 12288, 2), (64, 256, 4)]:
+        assert (q.q8_0_workspace_bytes(q.Q8_OP_Q4K_GEMV, M, K, N) ==
+                q.q8_0_workspace_bytes(q.Q8_OP_GEMV, M, K, N))
+    assert q.q8_0_workspace_bytes(q.Q8_OP_Q4K_GEMV, 4096, 4000, 1) == 0

@@ -68,3 +68,21 @@ def test_integer_activation_9b_gate_up_sampled(N):
     rows = np.unique(np.concatenate([g.integers(0, M, 512), [0, 63, 64, M - 1]]))
     yr, S = oracle.gemv_q8act(m.aos()[rows], eq, ed)
     q8tol.check(y[:, rows], yr, S, f"C4 gate_up int8 activations N={N}")
+
+
+@pytest.mark.parametrize("mat", [W.MAT_GATE_UP, W.MAT_DOWN])
+def test_q4k_9b_shapes_sampled(mat):
+    """Q4_K weights (NEXT-2) at the 9B-class shapes the benchmark times, N = 1
+    and 8, sampled rows against the oracle; tolerance as in test_gpu_q4k."""
+    from test_gpu_q4k import check, pack4, s2_bound
+    M, K = W.C4_SHAPES[mat]
+    m = W.draw_q4k(W.rng(90, mat), M, K)
+    p = pack4(m)
+    g = np.random.default_rng(91 + mat)
+    rows = np.unique(np.concatenate([g.integers(0, M, 256), [0, 63, 64, M - 1]]))
+    sub = W.Q4KMatrix(m.q[rows], m.s[rows], m.m[rows], m.d[rows], m.dmin[rows])
+    for N in (1, 8):
+        x = W.activations(90, N, K, layer=N)
+        y = host(q.q4k_gemv(p, to_dev(x)))
+        yr, _ = oracle.q4k_gemv(sub.blocks(), x)
+        check(y[:, rows], yr, s2_bound(sub, x), f"Q4_K {M}x{K} N={N}")
