@@ -306,6 +306,57 @@ int oracle_q4k_gemv(const uint8_t* blocks, int64_t M, int64_t K, const float* x,
 }
 
 /* ---------------------------------------------------------------------------
+ * Q6_K weights (NEXT-2).  [COGNI "Qwen 3.5 Native Metal": cuda_q6k_gemv_probe
+ * covers the GGUF Q6_K block: ql, qh, signed scales, d.]  Reading of the
+ * packing (the page lists the fields; the arrangement is GGUF's): a 210-byte
+ * block holds 256 weights of one row;
+ *   bytes 0-127    ql: low 4 bits of the 6-bit quants
+ *   bytes 128-191  qh: high 2 bits
+ *   bytes 192-207  16 signed 8-bit scales, one per 16 weights
+ *   bytes 208-209  d   binary16, little-endian
+ * Weight k (0..255) = 128 h + 32 a + l (h < 2, a < 4, l < 32):
+ *   low 4 bits:  byte ql[64 h + 32 (a % 2) + l], low nibble for a < 2, else high
+ *   high 2 bits: bits 2a, 2a+1 of qh[32 h + l]
+ *   q = low + 16 * high - 32 (so -32..31), weight = d * scale[k / 16] * q.
+ * ------------------------------------------------------------------------- */
+#define Q6K_BYTES 210
+
+static double q6k_weight(const uint8_t* blocks, int64_t K, int64_t r, int64_t k) {
+  const uint8_t* b = blocks + (r * (K / QKK) + k / QKK) * Q6K_BYTES;
+  const int kk = (int)(k % QKK);
+  const int h = kk / 128, a = (kk % 128) / 32, l = kk % 32;
+  const uint8_t lb = b[64 * h + 32 * (a % 2) + l];
+  const int low = (a < 2) ? (lb & 15) : (lb >> 4);
+  const int high = (b[128 + 32 * h + l] >> (2 * a)) & 3;
+  const int q = low + 16 * high - 32;
+  const int sc = (int8_t)b[192 + kk / 16];
+  const double d = oracle_f16_to_f64((uint16_t)(b[208] | (b[209] << 8)));
+  return d * (double)sc * (double)q;
+}
+
+void oracle_q6k_dequant_row(const uint8_t* blocks, int64_t K, int64_t r, double* out) {
+  for (int64_t k = 0; k < K; ++k) out[k] = q6k_weight(blocks, K, r, k);
+}
+
+/* y[n][r] = sum_k w[r][k] * x[n][k] over Q6_K rows, with magnitude sums. */
+int oracle_q6k_gemv(const uint8_t* blocks, int64_t M, int64_t K, const float* x, int64_t N,
+                    double* y, double* S) {
+  if (M < 0 || K <= 0 || K % QKK || N < 1) return -1;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t r = 0; r < M; ++r) {
+      double sum = 0.0, sabs = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double t = q6k_weight(blocks, K, r, k) * (double)x[n * K + k];
+        sum = sum + t;
+        sabs = sabs + fabs(t);
+      }
+      y[n * M + r] = sum;
+      if (S) S[n * M + r] = sabs;
+    }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Greedy pick: the lowest index among the maxima [AUGUR "Greedy generation";
  * FUSED "API stability": ties resolve to the earliest index].
  * ------------------------------------------------------------------------- */

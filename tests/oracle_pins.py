@@ -544,11 +544,65 @@ def check_q4k_closed_form_constant():
         assert np.all(y == want), (qv, sv, mv)
 
 
+def q6k_weights_from_fields(mtx: W.Q6KMatrix) -> list:
+    """Exact rational weights d * scale * (code - 32) from the drawn fields."""
+    M, K = mtx.code.shape
+    return [[Fraction(float(mtx.d[r, k // 256])) * int(mtx.sc[r, k // 16]) *
+             (int(mtx.code[r, k]) - 32) for k in range(K)] for r in range(M)]
+
+
+def check_q6k_bruteforce():
+    """Q6_K oracle against exact rational arithmetic on the drawn fields (the
+    packed bytes are decoded only by the oracle)."""
+    g = np.random.default_rng(60)
+    mtx = W.draw_q6k(g, 3, 512)
+    mtx.code[0, :64], mtx.code[1, 100:200] = 63, 0
+    mtx.sc[2, :8] = [-128, 127, -1, 0, 1, -64, 64, 100]
+    x = W.draw_x(g, 2, 512)
+    y, S = oracle.q6k_gemv(mtx.blocks(), x)
+    wq = q6k_weights_from_fields(mtx)
+    for n in range(2):
+        for r in range(3):
+            terms = [w * Fraction(float(xv)) for w, xv in zip(wq[r], x[n])]
+            tot, mag = sum(terms, Fraction(0)), sum((abs(t) for t in terms), Fraction(0))
+            assert abs(float(tot) - y[n, r]) <= 512 * 2.0 ** -52 * float(mag) + 1e-300, (n, r)
+            assert abs(float(mag) - S[n, r]) <= 512 * 2.0 ** -52 * float(mag), (n, r)
+
+
+def check_q6k_one_hot_every_position():
+    """Every weight of two blocks dequantises to d * scale * (code - 32), each
+    16-weight group with its own scale; one-hot x returns it exactly."""
+    g = np.random.default_rng(61)
+    mtx = W.draw_q6k(g, 2, 512)
+    mtx.code[:] = (np.arange(512)[None, :] * 5 + np.array([[0], [17]])) % 64
+    mtx.sc[:] = (np.arange(32)[None, :] * 7 - 100).astype(np.int8)
+    wq = q6k_weights_from_fields(mtx)
+    deq = oracle.q6k_dequant_rows(mtx.blocks(), 512)
+    for r in range(2):
+        assert [float(w) for w in wq[r]] == list(deq[r]), r
+    ks = [0, 15, 16, 31, 32, 63, 64, 127, 128, 160, 200, 255, 256, 300, 450, 511]
+    y, _ = oracle.q6k_gemv(mtx.blocks(), np.eye(512, dtype=np.float32)[ks])
+    for i, k in enumerate(ks):
+        assert y[i, 0] == float(wq[0][k]) and y[i, 1] == float(wq[1][k]), k
+
+
+def check_q6k_closed_form_constant():
+    """Constant code c, scale s and d: y = d s (c - 32) sum(x), exact."""
+    K = 768
+    for (c, sv) in [(63, 127), (0, -128), (32, 5), (40, -3)]:
+        mtx = W.Q6KMatrix(np.full((2, K), c, np.uint8), np.full((2, K // 16), sv, np.int8),
+                          np.full((2, K // 256), np.float16(0.125)))
+        x = np.random.default_rng(c).integers(-3, 4, size=(1, K)).astype(np.float32)
+        y, _ = oracle.q6k_gemv(mtx.blocks(), x)
+        assert np.all(y == 0.125 * sv * (c - 32) * float(x.astype(np.float64).sum())), (c, sv)
+
+
 ALL_CHECKS = [
     check_f16_exhaustive, check_f16_golden, check_hand_examples, check_closed_form_constant,
     check_one_hot, check_bruteforce_k32, check_dense_matvec_shapes, check_invariants,
     check_columns_independent, check_threads_identical, check_argmax, check_router,
     check_glue, check_moe, check_qwen_layer, check_f32_to_f16_numpy,
     check_quantize_act_closed_forms, check_gemv_q8act, check_q4k_bruteforce,
-    check_q4k_one_hot_every_position, check_q4k_closed_form_constant,
+    check_q4k_one_hot_every_position, check_q4k_closed_form_constant, check_q6k_bruteforce,
+    check_q6k_one_hot_every_position, check_q6k_closed_form_constant,
 ]

@@ -63,6 +63,16 @@ MUTANTS = {
     "q4k_min_sign": ("- dmin * (double)mj;", "+ dmin * (double)mj;"),
     "q4k_d_dmin_swapped": ("(uint16_t)(b[0] | (b[1] << 8)));\n  const double dmin",
                            "(uint16_t)(b[2] | (b[3] << 8)));\n  const double dmin"),
+    "q6k_nibble_swapped": ("const int low = (a < 2) ? (lb & 15) : (lb >> 4);",
+                           "const int low = (a < 2) ? (lb >> 4) : (lb & 15);"),
+    "q6k_high_shift": (">> (2 * a)) & 3;", ">> a) & 3;"),
+    "q6k_offset_dropped": ("const int q = low + 16 * high - 32;", "const int q = low + 16 * high;"),
+    "q6k_high_weight": ("const int q = low + 16 * high - 32;", "const int q = low + 4 * high - 32;"),
+    "q6k_scale_group_32": ("b[192 + kk / 16]", "b[192 + kk / 32]"),
+    "q6k_scale_unsigned": ("const int sc = (int8_t)b[192 + kk / 16];",
+                           "const int sc = (uint8_t)b[192 + kk / 16];"),
+    "q6k_ql_half_dropped": ("b[64 * h + 32 * (a % 2) + l]", "b[64 * h + l]"),
+    "q6k_d_offset": ("(uint16_t)(b[208] | (b[209] << 8))", "(uint16_t)(b[207] | (b[208] << 8))"),
     "q4k_wrong_subblock": ("const int kk = (int)(k % QKK), j = kk / 32;",
                            "const int kk = (int)(k % QKK), j = (kk / 32) ^ 1;"),
 }

@@ -149,6 +149,64 @@ def draw_q4k(g: np.random.Generator, M: int, K: int) -> Q4KMatrix:
     return Q4KMatrix(q, s, m, d, dmin)
 
 
+# --------------------------------------------------------------------------
+# Q6_K (GGUF k-quant, named on the cogni-ml page, cuda_q6k_gemv_probe: ql, qh,
+# signed scales, d).  A 210-byte block holds 256 weights of one row: [0:128]
+# ql (low 4 bits), [128:192] qh (high 2 bits), [192:208] 16 int8 scales (one
+# per 16 weights), [208:210] d (binary16).  Weight k = 128 h + 32 a + l: low
+# bits in ql[64 h + 32 (a % 2) + l] (low nibble for a < 2, else high), high
+# bits at bits 2a..2a+1 of qh[32 h + l]; q = low + 16 high - 32.
+# Value distributions: 6-bit codes uniform 0..63, scales uniform -128..127,
+# d = |N(0,1)| * 0.0002 as binary16.
+# --------------------------------------------------------------------------
+Q6K_BYTES = 210
+
+
+@dataclasses.dataclass
+class Q6KMatrix:
+    """A Q6_K matrix as drawn: 6-bit codes [M][K] 0..63 (weight = d * scale *
+    (code - 32)), int8 scales [M][K/16], d [M][K/256] float16."""
+    code: np.ndarray
+    sc: np.ndarray
+    d: np.ndarray
+
+    @property
+    def M(self) -> int:
+        return self.code.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.code.shape[1]
+
+    def blocks(self) -> np.ndarray:
+        """GGUF Q6_K bytes, shape [M, K/256, 210] uint8."""
+        M, K = self.code.shape
+        if K % QKK:
+            raise ValueError("K must be a multiple of 256")
+        B = K // QKK
+        c = self.code.astype(np.uint8).reshape(M, B, 2, 4, 32)  # [h][a][l]
+        low, high = c & 15, c >> 4
+        out = np.zeros((M, B, Q6K_BYTES), dtype=np.uint8)
+        ql = np.zeros((M, B, 2, 2, 32), dtype=np.uint8)  # [h][a % 2][l]
+        ql[:, :, :, 0, :] = low[:, :, :, 0, :] | (low[:, :, :, 2, :] << 4)
+        ql[:, :, :, 1, :] = low[:, :, :, 1, :] | (low[:, :, :, 3, :] << 4)
+        out[:, :, 0:128] = ql.reshape(M, B, 128)
+        qh = (high[:, :, :, 0, :] | (high[:, :, :, 1, :] << 2) | (high[:, :, :, 2, :] << 4) |
+              (high[:, :, :, 3, :] << 6))
+        out[:, :, 128:192] = qh.reshape(M, B, 64)
+        out[:, :, 192:208] = np.ascontiguousarray(self.sc, np.int8).view(np.uint8).reshape(M, B, 16)
+        out[:, :, 208:210] = np.ascontiguousarray(self.d, np.float16).view(np.uint8).reshape(M, B, 2)
+        return out
+
+
+def draw_q6k(g: np.random.Generator, M: int, K: int) -> Q6KMatrix:
+    """Codes, then scales, then d, from one generator."""
+    code = g.integers(0, 64, size=(M, K), dtype=np.uint8)
+    sc = g.integers(-128, 128, size=(M, K // 16), dtype=np.int8)
+    d = (np.abs(g.standard_normal((M, K // QKK))) * 0.0002).astype(np.float16)
+    return Q6KMatrix(code, sc, d)
+
+
 def draw_x(g: np.random.Generator, N: int, K: int) -> np.ndarray:
     return g.standard_normal((N, K)).astype(np.float32)
 
