@@ -210,13 +210,33 @@ def rand_packed_q4k(M, K, n_mats, gen):
     return qs, meta.view(-1), qb, mb
 
 
+def rand_packed_q6k(M, K, n_mats, gen):
+    """Seeded packed Q6_K weights drawn on the device: every 6-bit code and
+    int8 scale uniform (random bytes), d = |N(0,1)|*0.0002 in binary16.
+    Returns ql, qh, meta tensors holding n_mats packed matrices back to back
+    and their per-matrix byte counts (M % 64 == 0, K % 256 == 0)."""
+    import torch
+    import block_quantized_gemv_amd as q
+    assert M % 64 == 0 and K % 256 == 0
+    a, b, c = q.q6k_packed_size(M, K)
+    dev = torch.device("cuda", 0)
+    ql = torch.randint(0, 256, (n_mats * a,), dtype=torch.uint8, device=dev, generator=gen)
+    qh = torch.randint(0, 256, (n_mats * b,), dtype=torch.uint8, device=dev, generator=gen)
+    meta = torch.zeros(n_mats * c // 16, 16, dtype=torch.uint8, device=dev)
+    meta[:, 0:8] = torch.randint(0, 256, (n_mats * c // 16, 8), dtype=torch.uint8, device=dev,
+                                 generator=gen)
+    d = (torch.randn(n_mats * c // 16, device=dev, generator=gen).abs() * 0.0002).half()
+    meta[:, 8:10] = d.view(torch.uint8).view(-1, 2)
+    return ql, qh, meta.view(-1), (a, b, c)
+
+
 def measure_rows(log, cold_bytes=1.2e9):
     """Every kernel of the path on its own workload, graph-timed over rotating
     cold weight copies (more than `cold_bytes` in rotation, beyond the 256 MB
     Infinity Cache): C1 896x896; the 0.5B layer shapes; lm_head with the fused
     RMSNorm/argmax and the standalone argmax; the 9B-class shapes at N = 1, 2,
     4, 8; the integer-activation variant on the 9B gate_up shape; Q4_K
-    weights on the 9B shapes; the
+    and Q6_K weights on the 9B shapes; the
     verify-chunk LM head with one argmax per column; the
     Qwen1.5-MoE-shaped FFN (router, scatter + SwiGLU, combine)."""
     import torch
@@ -317,6 +337,22 @@ def measure_rows(log, cold_bytes=1.2e9):
             rec("n2", f"C4-shaped {M}x{K} Q4_K N={N}{launches}", sec,
                 0.5625 * M * K + 4 * K * N + 4 * M * N)
             del views, qs, meta
+            torch.cuda.empty_cache()
+    # Q6_K weights (NEXT-2); algorithmic bytes are GGUF's 210 per 256 weights
+    for (M, K) in ((4096, 12288), (24576, 4096)):
+        for N in (1, 8):
+            n = max(2, min(64, int(cold_bytes // (0.875 * M * K)) + 1))
+            ql, qh, meta, (a, b, c) = rand_packed_q6k(M, K, n, gen)
+            views = [q.PackedQ6K(ql[i * a:(i + 1) * a], qh[i * b:(i + 1) * b],
+                                 meta[i * c:(i + 1) * c], M, K) for i in range(n)]
+            x = torch.randn(N, K, device=dev, generator=gen)
+            y = torch.empty(N, M, device=dev)
+            ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_Q6K_GEMV, M, K, N))
+            sec = graph_time(lambda i: q.q6k_gemv(views[i % n], x, y, ws), n)
+            launches = "" if N <= 4 else " (2 launches)"
+            rec("n2", f"C4-shaped {M}x{K} Q6_K N={N}{launches}", sec,
+                210 / 256 * M * K + 4 * K * N + 4 * M * N)
+            del views, ql, qh, meta
             torch.cuda.empty_cache()
     for N in (2, 8):
         gemv_row("f4", 151936, 896, N, f"lm_head 151936x896 N={N} + argmax per column (2 launches)",

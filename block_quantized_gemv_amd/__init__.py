@@ -26,6 +26,7 @@ Q8_MOE_SCATTER, Q8_MOE_COMBINE, Q8_MOE_SWIGLU = 1, 2, 4
 Q8_OP_GEMV, Q8_OP_GEMV_FUSED, Q8_OP_ARGMAX, Q8_OP_MOE_SCATTER, Q8_OP_MOE_COMBINE = 1, 2, 3, 4, 5
 Q8_OP_GEMV_ARGMAX = 6
 Q8_OP_Q4K_GEMV = 7
+Q8_OP_Q6K_GEMV = 8
 
 Q8_LAYOUT_ROWS, Q8_LAYOUT_GATE_UP_PAIRS = 0, 1
 Q8_CHAIN_QKV, Q8_CHAIN_H_ATTN, Q8_CHAIN_SWIGLU, Q8_CHAIN_H_OUT = 0, 1, 2, 3
@@ -35,7 +36,7 @@ EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv",
            "q8_0_route_topk", "q8_0_moe_gemv", "q8_0_workspace_bytes", "q8_0_gemv_plan",
            "q8_0_strerror", "q8_0_version", "q8_0_chain_workspace_bytes", "q8_0_chain_prepare",
            "q8_0_chain_run", "q8_0_chain_read", "q8_0_chain_status", "q4k_packed_size",
-           "q4k_repack", "q4k_gemv")
+           "q4k_repack", "q4k_gemv", "q6k_packed_size", "q6k_repack", "q6k_gemv")
 
 
 class Q8Error(RuntimeError):
@@ -106,6 +107,10 @@ def lib() -> ctypes.CDLL:
         L.q4k_packed_size.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
         L.q4k_repack.argtypes = [P, I64, I64, P, P, P]
         L.q4k_gemv.argtypes = [ctypes.POINTER(q4k_weights), P, P, I64, I64, I64, P, SZ, P]
+        L.q6k_packed_size.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ),
+                                      ctypes.POINTER(SZ)]
+        L.q6k_repack.argtypes = [P, I64, I64, P, P, P, P]
+        L.q6k_gemv.argtypes = [ctypes.POINTER(q6k_weights), P, P, I64, I64, I64, P, SZ, P]
         L.q8_0_argmax.argtypes = [P, I64, P, P, SZ, P]
         L.q8_0_route_topk.argtypes = [P, I32, I32, P, P, P]
         L.q8_0_moe_gemv.argtypes = [PW, P, P, P, P, I64, I64, I32, I32, PW, P, P, P, SZ, P]
@@ -245,6 +250,55 @@ def q4k_gemv(W: PackedQ4K, x: torch.Tensor, y: torch.Tensor | None = None, works
     _need(y, torch.float32, "y")
     wsp, wsb = _ws(workspace, q8_0_workspace_bytes(Q8_OP_Q4K_GEMV, W.M, W.K, N), x.device)
     _check("q4k_gemv", lib().q4k_gemv(ctypes.byref(W.desc), x.data_ptr(), y.data_ptr(), W.M,
+                                      W.K, N, wsp, wsb, _stream(stream)))
+    return y
+
+
+class q6k_weights(ctypes.Structure):
+    _fields_ = [("ql", ctypes.c_void_p), ("qh", ctypes.c_void_p), ("meta", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class PackedQ6K:
+    """Packed device Q6_K weights of one matrix (see q6k_repack in q8gemv.h)."""
+
+    def __init__(self, ql: torch.Tensor, qh: torch.Tensor, meta: torch.Tensor, M: int, K: int):
+        self.ql, self.qh, self.meta, self.M, self.K = ql, qh, meta, M, K
+        self.desc = q6k_weights(ql.data_ptr(), qh.data_ptr(), meta.data_ptr(), M, K)
+
+    @classmethod
+    def from_blocks(cls, blocks: torch.Tensor, M: int, K: int, stream=None) -> "PackedQ6K":
+        """Repack GGUF Q6_K blocks (uint8 device tensor of M*(K/256)*210 bytes)."""
+        _need(blocks, torch.uint8, "blocks")
+        if blocks.numel() != M * (K // 256) * 210:
+            raise ValueError(f"blocks has {blocks.numel()} bytes, expected {M * (K // 256) * 210}")
+        a, b, c = q6k_packed_size(M, K)
+        ql = torch.empty(a, dtype=torch.uint8, device=blocks.device)
+        qh = torch.empty(b, dtype=torch.uint8, device=blocks.device)
+        meta = torch.empty(c, dtype=torch.uint8, device=blocks.device)
+        _check("q6k_repack", lib().q6k_repack(blocks.data_ptr(), M, K, ql.data_ptr(),
+                                              qh.data_ptr(), meta.data_ptr(), _stream(stream)))
+        return cls(ql, qh, meta, M, K)
+
+
+def q6k_packed_size(M: int, K: int) -> tuple[int, int, int]:
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check("q6k_packed_size", lib().q6k_packed_size(M, K, ctypes.byref(a), ctypes.byref(b),
+                                                    ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def q6k_gemv(W: PackedQ6K, x: torch.Tensor, y: torch.Tensor | None = None, workspace=None,
+             stream=None) -> torch.Tensor:
+    """y[N][M] = x[N][K] @ W^T for packed Q6_K weights W (x float32)."""
+    _need(x, torch.float32, "x")
+    N = 1 if x.dim() == 1 else x.shape[0]
+    if y is None:
+        y = torch.empty((W.M,) if x.dim() == 1 else (N, W.M), dtype=torch.float32,
+                        device=x.device)
+    _need(y, torch.float32, "y")
+    wsp, wsb = _ws(workspace, q8_0_workspace_bytes(Q8_OP_Q6K_GEMV, W.M, W.K, N), x.device)
+    _check("q6k_gemv", lib().q6k_gemv(ctypes.byref(W.desc), x.data_ptr(), y.data_ptr(), W.M,
                                       W.K, N, wsp, wsb, _stream(stream)))
     return y
 

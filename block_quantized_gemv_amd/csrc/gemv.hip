@@ -323,6 +323,135 @@ __device__ __forceinline__ void dot_range_q4k(const uint8_t* qs_tile, const uint
   if (it < nq) q4_fma<N>(A, (g0 + it) & 1, acc);
 }
 
+// ---- Q6_K weights ------------------------------------------------------------
+// A quad is half of a 256-weight block: 4 sub-blocks of 32.  Per sub-block
+// and row: 16 bytes of low nibbles laid out as for Q4_K, 8 bytes of dense
+// 2-bit high fields, and per quad 8 signed scales (one per 16 weights) and d.
+// The 6-bit code of a weight is low + 16 high; per 16-weight group and
+// column y += d s * (sum(code x) - 32 sum(x)).
+
+template <int N>
+struct QuadQ6 {
+  u32x4 q[4];
+  u32x2 h[4];
+  u32x4 meta;  // 8 int8 scales, then d (binary16)
+  XBlock<N> x[4];
+};
+
+template <int N>
+__device__ __forceinline__ void q6_load(QuadQ6<N>& B, const u32x4* qp, const u32x2* hp,
+                                        const u32x4* mp, int g, const float* x, int64_t xs,
+                                        int xl) {
+  B.meta = __builtin_nontemporal_load(mp + g * 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    B.q[i] = __builtin_nontemporal_load(qp + (4 * g + i) * 64);
+    B.h[i] = __builtin_nontemporal_load(hp + (4 * g + i) * 64);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_xblock<N>(x + 32 * (4 * g + i), xs, xl, B.x[i]);
+}
+
+// Four 2-bit fields (bits 0-7 of b) to bits 0-1 of the four bytes.
+__device__ __forceinline__ uint32_t spread2(uint32_t b) {
+  uint32_t v = (b | (b << 12)) & 0x000F000Fu;
+  return (v | (v << 6)) & 0x03030303u;
+}
+
+// 6-bit codes of 4 weights as the 4 bytes of a dword: nibbles (4 bits each,
+// one per byte) plus 16 times the matching high fields.  The result is kept
+// opaque so that each byte converts with one v_cvt_f32_ubyteN.
+__device__ __forceinline__ uint32_t q6_codes(uint32_t nib, uint32_t hb) {
+  uint32_t c = nib | (spread2(hb) << 4);
+  asm("" : "+v"(c));
+  return c;
+}
+
+template <int N, int I>
+__device__ __forceinline__ void q6_dword(uint32_t w, uint32_t h0, uint32_t h1, const XBlock<N>& X,
+                                         float (&pl)[N], float (&ph)[N]) {
+  uint32_t lo, hi;
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w));
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w >> 4));
+  const uint32_t cl = q6_codes(lo, (h0 >> (8 * I)) & 255u);
+  const uint32_t ch = q6_codes(hi, (h1 >> (8 * I)) & 255u);
+  const float l0 = (float)(cl & 255u), l1 = (float)((cl >> 8) & 255u);
+  const float l2 = (float)((cl >> 16) & 255u), l3 = (float)(cl >> 24);
+  const float g0 = (float)(ch & 255u), g1 = (float)((ch >> 8) & 255u);
+  const float g2 = (float)((ch >> 16) & 255u), g3 = (float)(ch >> 24);
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    fmac_row_bcast<4 * I + 0>(pl[n], X.a[n], l0);
+    fmac_row_bcast<4 * I + 1>(pl[n], X.a[n], l1);
+    fmac_row_bcast<4 * I + 2>(pl[n], X.a[n], l2);
+    fmac_row_bcast<4 * I + 3>(pl[n], X.a[n], l3);
+    fmac_row_bcast<4 * I + 0>(ph[n], X.b[n], g0);
+    fmac_row_bcast<4 * I + 1>(ph[n], X.b[n], g1);
+    fmac_row_bcast<4 * I + 2>(ph[n], X.b[n], g2);
+    fmac_row_bcast<4 * I + 3>(ph[n], X.b[n], g3);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void q6_fma(const QuadQ6<N>& B, float (&acc)[N]) {
+  const float d = f16_to_f32(B.meta.z & 0xffffu);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t sw = i < 2 ? B.meta.x : B.meta.y;
+    const float sl = d * (float)(int8_t)(sw >> (16 * (i & 1)));
+    const float sh = d * (float)(int8_t)(sw >> (16 * (i & 1) + 8));
+    float pl[N], ph[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) pl[n] = ph[n] = 0.f;
+    q6_dword<N, 0>(B.q[i].x, B.h[i].x, B.h[i].y, B.x[i], pl, ph);
+    q6_dword<N, 1>(B.q[i].y, B.h[i].x, B.h[i].y, B.x[i], pl, ph);
+    q6_dword<N, 2>(B.q[i].z, B.h[i].x, B.h[i].y, B.x[i], pl, ph);
+    q6_dword<N, 3>(B.q[i].w, B.h[i].x, B.h[i].y, B.x[i], pl, ph);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      // sums of the 16 activations of each group, by rotations within the row
+      float sa = B.x[i].a[n], sb = B.x[i].b[n];
+      sa = dpp_add<0x128>(sa);
+      sb = dpp_add<0x128>(sb);
+      sa = dpp_add<0x124>(sa);
+      sb = dpp_add<0x124>(sb);
+      sa = dpp_add<0x122>(sa);
+      sb = dpp_add<0x122>(sb);
+      sa = dpp_add<0x121>(sa);
+      sb = dpp_add<0x121>(sb);
+      acc[n] = fmaf(sl, pl[n], acc[n]);
+      acc[n] = fmaf(-32.0f * sl, sa, acc[n]);
+      acc[n] = fmaf(sh, ph[n], acc[n]);
+      acc[n] = fmaf(-32.0f * sh, sb, acc[n]);
+    }
+  }
+}
+
+// Q6_K dot products of the 64 rows of one tile over 32-weight blocks
+// [b0, b1) (whole quads), quads double-buffered.
+template <int N>
+__device__ __forceinline__ void dot_range_q6k(const uint8_t* qs_tile, const uint8_t* qh_tile,
+                                              const uint8_t* meta_tile, int b0, int b1,
+                                              int lane, const float* x, int64_t xs,
+                                              float (&acc)[N]) {
+  const u32x4* qp = reinterpret_cast<const u32x4*>(qs_tile) + lane;
+  const u32x2* hp = reinterpret_cast<const u32x2*>(qh_tile) + lane;
+  const u32x4* mp = reinterpret_cast<const u32x4*>(meta_tile) + lane;
+  const int xl = lane & 15;
+  const int g0 = b0 >> 2, nq = (b1 - b0) >> 2;
+  if (nq <= 0) return;
+  QuadQ6<N> A, B;
+  q6_load<N>(A, qp, hp, mp, g0, x, xs, xl);
+  int it = 0;
+  for (; it + 1 < nq; it += 2) {
+    q6_load<N>(B, qp, hp, mp, g0 + it + 1, x, xs, xl);
+    q6_fma<N>(A, acc);
+    if (it + 2 < nq) q6_load<N>(A, qp, hp, mp, g0 + it + 2, x, xs, xl);
+    q6_fma<N>(B, acc);
+  }
+  if (it < nq) q6_fma<N>(A, acc);
+}
+
 // ---- integer activations (opt-in variant) ------------------------------------
 // Activations quantized per 32-entry block to int8 with a binary16 scale
 // (q8_0_quantize_act).  Per block and column the 32 int8 x int8 products are
@@ -578,9 +707,9 @@ __device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, 
 // ONE: a single problem with a single segment (dense GEMVs and the decode
 // chain): every kernel argument sits at a fixed offset, so no search loops.
 // MODE: 0 Q8_0 weights and fp32 activations; 1 integer activations; 2 Q4_K
-// weights and fp32 activations.
+// and 3 Q6_K weights with fp32 activations.
 template <int N, bool ONE, int MODE>
-__global__ __launch_bounds__(64 * max_waves_for(N)) void gemv_kernel(const GemvParams p) {
+__global__ __launch_bounds__(64 * max_waves_for(N, MODE == 3)) void gemv_kernel(const GemvParams p) {
   extern __shared__ float lds_part[];  // [W][N][64]
   __shared__ int s_last;
 
@@ -636,7 +765,7 @@ __global__ __launch_bounds__(64 * max_waves_for(N)) void gemv_kernel(const GemvP
       const int t = ot + tsel * pr.Tout;
       // bytes of one packed tile's quants: 64 rows of K (Q8_0) or K / 2 (Q4_K)
       const uint8_t* qs_tile =
-          s.qs + (int64_t)e * s.qs_stride + (int64_t)t * kTile * (MODE == 2 ? s.K / 2 : s.K);
+          s.qs + (int64_t)e * s.qs_stride + (int64_t)t * kTile * (MODE >= 2 ? s.K / 2 : s.K);
       const uint8_t* d_tile = s.d + (int64_t)e * s.d_stride + (int64_t)t * s.G * 512;
       // units own whole scale quads (4 blocks); only a row's last may be short
       const int b0 = 4 * (int)((int64_t)v * s.G / s.units);
@@ -646,6 +775,11 @@ __global__ __launch_bounds__(64 * max_waves_for(N)) void gemv_kernel(const GemvP
         dot_range_i8<N>(qs_tile, d_tile, b0, b1, lane, s.qx, s.dx, s.K, s.nblk, acc);
       else if (MODE == 2)
         dot_range_q4k<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, acc);
+      else if (MODE == 3)
+        // Q6_K: 8 bytes of high fields per sub-block and row, 16 bytes of
+        // scales and d per quad and row
+        dot_range_q6k<N>(qs_tile, s.qh + (int64_t)t * kTile * (s.K / 4),
+                         s.d + (int64_t)t * s.G * 1024, b0, b1, lane, s.x, s.x_stride, acc);
       else
         dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
                      s.gqa_off, acc);
@@ -915,7 +1049,8 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
   // plan needs costs more than it gains.
   const bool wide = N >= 2 && total_tout >= num_cus();
   const int64_t want_u = wide ? 4 : cdiv(target_waves(), total_tout);
-  int wmax = max_waves() < max_waves_for(N) ? max_waves() : max_waves_for(N);
+  const int wfmt = max_waves_for(N, probs[0].seg[0].fmt == FMT_Q6K);
+  int wmax = max_waves() < wfmt ? max_waves() : wfmt;
   if (wide && wmax > 4) wmax = 4;
   // units per tile
   int sbase = 0;
@@ -1012,11 +1147,17 @@ static hipError_t launch_n(const GemvParams& gp, int wgs, hipStream_t stream) {
   const size_t lds = (size_t)gp.W * N * 64 * sizeof(float);
   if (gp.seg[0].qx)  // the integer-activation path: one plain problem
     hipLaunchKernelGGL((gemv_kernel<N, true, 1>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
-  else if (gp.seg[0].fmt == FMT_Q4K) {  // Q4_K weights: one plain problem, N <= 4
-    if constexpr (N <= kMaxQ4kN)
-      hipLaunchKernelGGL((gemv_kernel<N, true, 2>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
-    else
+  else if (gp.seg[0].fmt == FMT_Q4K || gp.seg[0].fmt == FMT_Q6K) {  // one plain problem, N <= 4
+    if constexpr (N <= kMaxQ4kN) {
+      if (gp.seg[0].fmt == FMT_Q4K)
+        hipLaunchKernelGGL((gemv_kernel<N, true, 2>), dim3(wgs), dim3(64 * gp.W), lds, stream,
+                           gp);
+      else
+        hipLaunchKernelGGL((gemv_kernel<N, true, 3>), dim3(wgs), dim3(64 * gp.W), lds, stream,
+                           gp);
+    } else {
       return hipErrorInvalidValue;
+    }
   } else if (gp.nprob == 1 && gp.prob[0].nseg == 1)
     hipLaunchKernelGGL((gemv_kernel<N, true, 0>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
   else
@@ -1094,6 +1235,7 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
       sg.qx = sd.qx;
       sg.dx = sd.dx;
       sg.fmt = sd.fmt;
+      sg.qh = static_cast<const uint8_t*>(sd.qh);
     }
     sbase += pd.nseg;
     wg += (int)(Tout * pr.P);

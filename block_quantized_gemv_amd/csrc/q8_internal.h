@@ -16,7 +16,8 @@ constexpr int kTile = Q8_TILE_ROWS;  // rows per packed tile, one per lane
 // activations of a double-buffered quad take 16 N of them).
 constexpr int kMaxWaves = 16;
 constexpr int kMaxThreads = 64 * kMaxWaves;
-constexpr int max_waves_for(int N) { return N <= 2 ? 16 : 8; }
+// (Q6_K keeps more per column in flight: 16-wave workgroups only at N = 1.)
+constexpr int max_waves_for(int N, bool q6k = false) { return N <= (q6k ? 1 : 2) ? 16 : 8; }
 constexpr int kMaxSeg = 9;           // K-segments over all problems of one launch
 constexpr int kMaxProb = 9;          // problems (independent GEMVs) per launch
 // Every workspace starts with a fixed region of 32-bit counters that each
@@ -33,8 +34,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 enum : int32_t { F_RMSNORM = 1, F_RESIDUAL = 2, F_SWIGLU = 4, F_ARGMAX = 8, F_PAIRED = 16 };
 // Weight formats: Q8_0 (qs = quants, d = scales) or Q4_K (qs = nibbles of
 // 32-weight sub-blocks, d = 16-byte block headers: d, dmin, scales/mins).
-enum : int32_t { FMT_Q8_0 = 0, FMT_Q4K = 1 };
-// Columns per Q4_K launch (more would spill registers; callers split N).
+enum : int32_t { FMT_Q8_0 = 0, FMT_Q4K = 1, FMT_Q6K = 2 };
+// Columns per Q4_K / Q6_K launch (more would spill registers; callers split N).
 constexpr int kMaxQ4kN = 4;
 // How a segment's partial sum is weighted in the fold.
 enum : int32_t { A_ONE = 0, A_PTR = 1, A_SIGMOID = 2 };
@@ -63,6 +64,7 @@ struct Seg {
   const int8_t* qx;      // integer activations [N][K] (opt-in path), or nullptr
   const uint16_t* dx;    // their binary16 block scales [N][K / 32]
   int32_t fmt;           // FMT_*: how qs / d are packed
+  const uint8_t* qh;     // Q6_K: packed high 2-bit fields
 };
 
 // One problem: an output of Mout rows computed from R row-tiles per output
@@ -106,6 +108,7 @@ struct SegDesc {
   const int8_t* qx;      // integer activations (opt-in path), or nullptr
   const uint16_t* dx;
   int32_t fmt;           // FMT_*
+  const void* qh;        // Q6_K high bits
   const q8_0_weights* W;
   const int32_t* eid;
   int32_t slot;
@@ -156,6 +159,8 @@ int launch_argmax(const float* v, int64_t n, int32_t* out, void* ws, size_t ws_b
 int launch_route(const float* logits, int32_t E, int32_t k, int32_t* ids, float* w,
                  hipStream_t stream);
 int launch_q4k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* meta,
+                      hipStream_t stream);
+int launch_q6k_repack(const void* blocks, int64_t M, int64_t K, void* ql, void* qh, void* meta,
                       hipStream_t stream);
 int launch_quantize_act(const float* x, int64_t K, int64_t N, int8_t* qx, uint16_t* dx,
                         hipStream_t stream);

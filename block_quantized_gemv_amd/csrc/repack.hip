@@ -158,4 +158,85 @@ int launch_q4k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* 
   return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
 }
 
+// ---- Q6_K ------------------------------------------------------------------
+// GGUF Q6_K blocks ("skuznetsov/cogni-ml" README, cuda_q6k_gemv_probe: ql, qh,
+// signed scales, d; 210 bytes per 256 weights: ql[128], qh[64], int8
+// scales[16], d) move into, per 64-row tile:
+//   ql:   per 32-weight sub-block, 16 bytes per row: byte i holds the low 4
+//         bits of the sub-block's weights i (low nibble) and i + 16 (high)
+//   qh:   per sub-block, 8 bytes per row: the high 2 bits of weights 0..15
+//         (bits 2i of the first dword) and of 16..31 (the second dword)
+//   meta: per 128-weight half block, 16 bytes per row: its 8 scales (one per
+//         16 weights) and d, then zeros.
+// In a GGUF block weight k = 128 h + 32 a + l has its low bits in
+// ql[64 h + 32 (a % 2) + l] (low nibble for a < 2, else high) and its high
+// bits at bits 2a of qh[32 h + l].  Bit moves only; padding rows are zeros.
+__global__ __launch_bounds__(256) void q6k_repack_bits_kernel(const uint8_t* __restrict__ src,
+                                                              int64_t M, int64_t K,
+                                                              u32x4* __restrict__ ql,
+                                                              u32x2* __restrict__ qh,
+                                                              int64_t total) {
+  const int64_t nsub = K / 32, nsb = K / 256;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lane = idx & 63;
+    const int64_t c = (idx >> 6) % nsub;
+    const int64_t t = (idx >> 6) / nsub;
+    const int64_t r = t * 64 + lane;
+    uint32_t lo[4] = {0u, 0u, 0u, 0u}, hi[2] = {0u, 0u};
+    if (r < M) {
+      const uint8_t* b = src + (r * nsb + c / 8) * 210;
+      const int j = (int)(c & 7), h = j >> 2, a = j & 3;
+      const uint8_t* lb = b + 64 * h + 32 * (a & 1);
+      const uint8_t* hb = b + 128 + 32 * h;
+      const int nsh = 4 * (a >> 1), hsh = 2 * a;
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t l0 = (lb[i] >> nsh) & 15u, l1 = (lb[16 + i] >> nsh) & 15u;
+        lo[i >> 2] |= (l0 | (l1 << 4)) << (8 * (i & 3));
+        hi[0] |= (uint32_t)((hb[i] >> hsh) & 3) << (2 * i);
+        hi[1] |= (uint32_t)((hb[16 + i] >> hsh) & 3) << (2 * i);
+      }
+    }
+    ql[idx] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    qh[idx] = u32x2{hi[0], hi[1]};
+  }
+}
+
+__global__ __launch_bounds__(256) void q6k_repack_meta_kernel(const uint8_t* __restrict__ src,
+                                                              int64_t M, int64_t K,
+                                                              u32x4* __restrict__ meta,
+                                                              int64_t total) {
+  const int64_t nq = K / 128, nsb = K / 256;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lane = idx & 63;
+    const int64_t g = (idx >> 6) % nq;
+    const int64_t t = (idx >> 6) / nq;
+    const int64_t r = t * 64 + lane;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (r < M) {
+      const uint8_t* b = src + (r * nsb + g / 2) * 210;
+      const uint8_t* sc = b + 192 + 8 * (g & 1);
+      for (int i = 0; i < 8; ++i) w[i >> 2] |= (uint32_t)sc[i] << (8 * (i & 3));
+      w[2] = (uint32_t)b[208] | ((uint32_t)b[209] << 8);
+    }
+    meta[idx] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+int launch_q6k_repack(const void* blocks, int64_t M, int64_t K, void* ql, void* qh, void* meta,
+                      hipStream_t stream) {
+  const int64_t T = cdiv(M, kTile);
+  const int64_t nb = T * 64 * (K / 32);
+  const int64_t nm = T * 64 * (K / 128);
+  const auto* s8 = static_cast<const uint8_t*>(blocks);
+  auto grid = [](int64_t n) { return (unsigned)(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536); };
+  hipLaunchKernelGGL(q6k_repack_bits_kernel, dim3(grid(nb)), dim3(256), 0, stream, s8, M, K,
+                     static_cast<u32x4*>(ql), static_cast<u32x2*>(qh), nb);
+  if (hipGetLastError() != hipSuccess) return Q8_ELAUNCH;
+  hipLaunchKernelGGL(q6k_repack_meta_kernel, dim3(grid(nm)), dim3(256), 0, stream, s8, M, K,
+                     static_cast<u32x4*>(meta), nm);
+  return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
+}
+
 }  // namespace q8

@@ -269,6 +269,53 @@ int q4k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* meta, v
 int q4k_gemv(const q4k_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Q6_K weights (NEXT-2) -------------------------------------------------------
+ * GGUF Q6_K ("skuznetsov/cogni-ml" README, cuda_q6k_gemv_probe: ql, qh, signed
+ * scales, d).  Reading of the packing (the page lists the fields; the
+ * arrangement is GGUF's): a 210-byte block holds 256 weights of one row;
+ * bytes 0-127 ql (low 4 bits), 128-191 qh (high 2 bits), 192-207 sixteen int8
+ * scales (one per 16 weights), 208-209 d (binary16).  Weight k = 128 h + 32 a + l
+ * (h < 2, a < 4, l < 32) takes its low bits from ql[64 h + 32 (a % 2) + l]
+ * (low nibble for a < 2, else high) and its high bits from bits 2a, 2a + 1 of
+ * qh[32 h + l]; w_k = d * scale[k / 16] * (low + 16 high - 32).
+ *
+ * Packed layout (q6k_repack), T = ceil(M / 64) tiles of 64 rows, t = r / 64,
+ * i = r % 64, c = 32-weight sub-block, g = 128-weight quad:
+ *  ql:   T * (K/32) * 64 * 16 bytes; at ((t * (K/32) + c) * 64 + i) * 16, byte b
+ *        holds the low bits of the sub-block's weights b (low nibble) and
+ *        b + 16 (high nibble).
+ *  qh:   T * (K/32) * 64 * 8 bytes; at ((t * (K/32) + c) * 64 + i) * 8, two
+ *        dwords: the high bits of weights 0..15 (bits 2b, 2b+1 for weight b),
+ *        then of weights 16..31.
+ *  meta: T * (K/128) * 64 * 16 bytes; at ((t * (K/128) + g) * 64 + i) * 16 the
+ *        quad's 8 scales, d (binary16), then 6 zero bytes.
+ *  Rows M .. 64T-1 are zero.  Alignment: ql, meta 16 bytes; qh 8 bytes. */
+typedef struct {
+  const void* ql;    /* device, packed low bits */
+  const void* qh;    /* device, packed high bits */
+  const void* meta;  /* device, packed scales and d */
+  int64_t M, K;
+} q6k_weights;
+
+/* Bytes of the packed arrays of one M x K Q6_K matrix.
+ * Errors: Q8_ENULL, Q8_EINVAL (M < 0, K <= 0, K % 256, K > Q8_MAX_K). */
+int q6k_packed_size(int64_t M, int64_t K, size_t* ql_bytes, size_t* qh_bytes,
+                    size_t* meta_bytes);
+
+/* Load-time repack of GGUF Q6_K blocks (device, M * K/256 blocks of 210 bytes,
+ * row-major, any alignment) into ql, qh and meta (device, q6k_packed_size()
+ * bytes; every byte written).  Bit moves only.
+ * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_ELAUNCH. */
+int q6k_repack(const void* blocks, int64_t M, int64_t K, void* ql, void* qh, void* meta,
+               void* stream);
+
+/* y[n][r] = sum_k w[r][k] * x[n][k] with Q6_K weights; x, y, N, K and the
+ * workspace (op Q8_OP_Q6K_GEMV) as q4k_gemv.  Each 16-weight group adds
+ * d s * (sum(code x) - 32 sum(x)) in fp32; columns run 4 per launch.
+ * Errors as q8_0_gemv. */
+int q6k_gemv(const q6k_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
+             void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- argmax ------------------------------------------------------------------
  * *out_idx = min{ i : v[i] == max_j v[j] } over fp32 v[0..n) (device), as
  * int32 (device).  Inputs are finite (NaN is outside the contract).
@@ -429,6 +476,7 @@ int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
  * op Q8_OP_GEMV_FUSED: (M, K, epilogue flags in N) of q8_0_gemv_fused.
  * op Q8_OP_GEMV_ARGMAX: (M, K, N) of q8_0_gemv_argmax.
  * op Q8_OP_Q4K_GEMV: (M, K, N) of q4k_gemv.
+ * op Q8_OP_Q6K_GEMV: (M, K, N) of q6k_gemv.
  * op Q8_OP_ARGMAX: (n, 0, 0).
  * op Q8_OP_MOE_SCATTER / Q8_OP_MOE_COMBINE: (M, K, n_slots) with the
  *   shared expert's shape in (M2, K2) (0, 0 for none) and mode flags in flags.
@@ -440,6 +488,7 @@ int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
 #define Q8_OP_MOE_COMBINE 5
 #define Q8_OP_GEMV_ARGMAX 6
 #define Q8_OP_Q4K_GEMV 7
+#define Q8_OP_Q6K_GEMV 8
 size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t M2, int64_t K2,
                             int32_t flags);
 
