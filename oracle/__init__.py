@@ -63,6 +63,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_q4k_dequant_row.argtypes = [_P, _I64, _I64, _P]
         L.oracle_q4k_gemv.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
         L.oracle_q4k_gemv.restype = ctypes.c_int
+        L.oracle_q5k_dequant_row.argtypes = [_P, _I64, _I64, _P]
+        L.oracle_q5k_gemv.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
+        L.oracle_q5k_gemv.restype = ctypes.c_int
         L.oracle_q6k_dequant_row.argtypes = [_P, _I64, _I64, _P]
         L.oracle_q6k_gemv.argtypes = [_P, _I64, _I64, _P, _I64, _P, _P]
         L.oracle_q6k_gemv.restype = ctypes.c_int
@@ -208,6 +211,30 @@ def q4k_gemv(blocks: np.ndarray, x: np.ndarray):
     rc = lib().oracle_q4k_gemv(_ptr(blocks), M, K, _ptr(x), N, _ptr(y), _ptr(S))
     if rc:
         raise ValueError(f"oracle_q4k_gemv: {rc}")
+    return y, S
+
+
+def q5k_dequant_rows(blocks: np.ndarray, K: int) -> np.ndarray:
+    """Dequantised fp64 rows of a Q5_K matrix (blocks: uint8 [M][K/256][176])."""
+    blocks = _c(blocks, np.uint8)
+    M = blocks.shape[0]
+    out = np.zeros((M, K))
+    for r in range(M):
+        lib().oracle_q5k_dequant_row(_ptr(blocks), K, r, _ptr(out[r]))
+    return out
+
+
+def q5k_gemv(blocks: np.ndarray, x: np.ndarray):
+    """y [N][M] and magnitude sums S of a Q5_K matrix times fp32 x [N][K]."""
+    blocks = _c(blocks, np.uint8)
+    M, K = blocks.shape[0], blocks.shape[1] * 256
+    x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
+    N = x.shape[0]
+    y = np.zeros((N, M))
+    S = np.zeros((N, M))
+    rc = lib().oracle_q5k_gemv(_ptr(blocks), M, K, _ptr(x), N, _ptr(y), _ptr(S))
+    if rc:
+        raise ValueError(f"oracle_q5k_gemv: {rc}")
     return y, S
 
 

@@ -263,20 +263,27 @@ int oracle_q8_0_gemv_q8act(const uint8_t* aos, int64_t M, int64_t K, const int8_
 #define QKK 256
 #define Q4K_BYTES 144
 
+/* The 16-byte header that Q4_K and Q5_K blocks share: d, dmin, and the
+ * 6-bit scale and min of sub-block j out of the 12 packed bytes. */
+static void kq_header(const uint8_t* b, int j, double* d, double* dmin, int* sj, int* mj) {
+  *d = oracle_f16_to_f64((uint16_t)(b[0] | (b[1] << 8)));
+  *dmin = oracle_f16_to_f64((uint16_t)(b[2] | (b[3] << 8)));
+  const uint8_t* sc = b + 4;
+  if (j < 4) {
+    *sj = sc[j] & 63;
+    *mj = sc[j + 4] & 63;
+  } else {
+    *sj = (sc[j + 4] & 15) + 16 * (sc[j - 4] >> 6);
+    *mj = (sc[j + 4] >> 4) + 16 * (sc[j] >> 6);
+  }
+}
+
 static double q4k_weight(const uint8_t* blocks, int64_t K, int64_t r, int64_t k) {
   const uint8_t* b = blocks + (r * (K / QKK) + k / QKK) * Q4K_BYTES;
   const int kk = (int)(k % QKK), j = kk / 32;
-  const double d = oracle_f16_to_f64((uint16_t)(b[0] | (b[1] << 8)));
-  const double dmin = oracle_f16_to_f64((uint16_t)(b[2] | (b[3] << 8)));
-  const uint8_t* sc = b + 4;
+  double d, dmin;
   int sj, mj;
-  if (j < 4) {
-    sj = sc[j] & 63;
-    mj = sc[j + 4] & 63;
-  } else {
-    sj = (sc[j + 4] & 15) + 16 * (sc[j - 4] >> 6);
-    mj = (sc[j + 4] >> 4) + 16 * (sc[j] >> 6);
-  }
+  kq_header(b, j, &d, &dmin, &sj, &mj);
   const uint8_t byte = b[16 + 32 * (kk / 64) + kk % 32];
   const int q = (kk % 64 < 32) ? (byte & 15) : (byte >> 4);
   return d * (double)sj * (double)q - dmin * (double)mj;
@@ -301,6 +308,55 @@ int oracle_q4k_gemv(const uint8_t* blocks, int64_t M, int64_t K, const float* x,
       }
       y[n * M + r] = acc;
       if (S) S[n * M + r] = mag;
+    }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Q5_K weights (NEXT-2).  [COGNI "Qwen 3.5 Native Metal": cuda_q5k_gemv_probe
+ * covers the GGUF Q5_K block of the recurrent layers' attn_qkv.]  Reading of
+ * the packing (the page names the format only; the arrangement is GGUF's):
+ * a 176-byte block holds 256 weights of one row as 8 sub-blocks of 32, laid
+ * out like Q4_K with 32 more bytes for a fifth bit:
+ *   bytes 0-15    d, dmin, the 12 scale/min bytes, decoded as for Q4_K
+ *   bytes 16-47   qh[32]: the fifth bit of weight k is bit k / 32 of
+ *                 qh[k % 32]
+ *   bytes 48-175  qs[128]: the low 4 bits of weight k, placed as in Q4_K
+ *   weight k = d * s_j * (q_k + 16 * bit_k) - dmin * m_j,  j = k / 32.
+ * ------------------------------------------------------------------------- */
+#define Q5K_BYTES 176
+
+static double q5k_weight(const uint8_t* blocks, int64_t K, int64_t r, int64_t k) {
+  const uint8_t* b = blocks + (r * (K / QKK) + k / QKK) * Q5K_BYTES;
+  const int kk = (int)(k % QKK);
+  const int j = kk / 32; /* sub-block */
+  double d, dmin;
+  int s5, m5;
+  kq_header(b, j, &d, &dmin, &s5, &m5);
+  const uint8_t byte5 = b[48 + 32 * (kk / 64) + kk % 32];
+  const int low = (kk % 64 < 32) ? (byte5 & 15) : (byte5 >> 4);
+  const int fifth = (b[16 + kk % 32] >> j) & 1;
+  return d * (double)s5 * (double)(low + 16 * fifth) - dmin * (double)m5;
+}
+
+void oracle_q5k_dequant_row(const uint8_t* blocks, int64_t K, int64_t r, double* out) {
+  for (int64_t k = 0; k < K; ++k) out[k] = q5k_weight(blocks, K, r, k);
+}
+
+/* y[n][r] = sum_k w[r][k] * x[n][k] over Q5_K rows, with magnitude sums. */
+int oracle_q5k_gemv(const uint8_t* blocks, int64_t M, int64_t K, const float* x, int64_t N,
+                    double* y, double* S) {
+  if (M < 0 || K <= 0 || K % QKK || N < 1) return -1;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t r = 0; r < M; ++r) {
+      double total = 0.0, absum = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double v = q5k_weight(blocks, K, r, k) * (double)x[n * K + k];
+        total = total + v;
+        absum = absum + fabs(v);
+      }
+      y[n * M + r] = total;
+      if (S) S[n * M + r] = absum;
     }
   return 0;
 }

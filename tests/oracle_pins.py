@@ -597,6 +597,48 @@ def check_q6k_closed_form_constant():
         assert np.all(y == 0.125 * sv * (c - 32) * float(x.astype(np.float64).sum())), (c, sv)
 
 
+def q5k_weights_from_fields(mtx: W.Q5KMatrix) -> list:
+    M, K = mtx.code.shape
+    return [[Fraction(float(mtx.d[r, k // 256])) * int(mtx.s[r, k // 32]) * int(mtx.code[r, k])
+             - Fraction(float(mtx.dmin[r, k // 256])) * int(mtx.m[r, k // 32])
+             for k in range(K)] for r in range(M)]
+
+
+def check_q5k_bruteforce():
+    """Q5_K oracle against exact rational sums on the drawn fields."""
+    g = np.random.default_rng(70)
+    mtx = W.draw_q5k(g, 3, 512)
+    mtx.code[0, :64], mtx.code[1, 64:192] = 31, 16
+    mtx.s[2, :4], mtx.m[2, :4] = [0, 63, 1, 62], [63, 0, 62, 1]
+    x = W.draw_x(g, 2, 512)
+    y, S = oracle.q5k_gemv(mtx.blocks(), x)
+    wq = q5k_weights_from_fields(mtx)
+    for n in range(2):
+        for r in range(3):
+            terms = [w * Fraction(float(xv)) for w, xv in zip(wq[r], x[n])]
+            tot, mag = sum(terms, Fraction(0)), sum((abs(t) for t in terms), Fraction(0))
+            assert abs(float(tot) - y[n, r]) <= 512 * 2.0 ** -52 * float(mag) + 1e-300, (n, r)
+            assert abs(float(mag) - S[n, r]) <= 512 * 2.0 ** -52 * float(mag), (n, r)
+
+
+def check_q5k_one_hot_every_position():
+    """Every weight of two blocks against the fields, with distinct codes per
+    position (fifth bits in every sub-block) and per-sub-block scales/mins."""
+    g = np.random.default_rng(71)
+    mtx = W.draw_q5k(g, 2, 512)
+    mtx.code[:] = (np.arange(512)[None, :] * 11 + np.array([[0], [7]])) % 32
+    mtx.s[:] = np.arange(16)[None, :] * 4 + 2
+    mtx.m[:] = 60 - np.arange(16)[None, :] * 3
+    wq = q5k_weights_from_fields(mtx)
+    deq = oracle.q5k_dequant_rows(mtx.blocks(), 512)
+    for r in range(2):
+        assert [float(w) for w in wq[r]] == list(deq[r]), r
+    ks = [0, 31, 32, 63, 64, 100, 200, 255, 256, 300, 511]
+    y, _ = oracle.q5k_gemv(mtx.blocks(), np.eye(512, dtype=np.float32)[ks])
+    for i, k in enumerate(ks):
+        assert y[i, 0] == float(wq[0][k]) and y[i, 1] == float(wq[1][k]), k
+
+
 ALL_CHECKS = [
     check_f16_exhaustive, check_f16_golden, check_hand_examples, check_closed_form_constant,
     check_one_hot, check_bruteforce_k32, check_dense_matvec_shapes, check_invariants,
@@ -604,5 +646,6 @@ ALL_CHECKS = [
     check_glue, check_moe, check_qwen_layer, check_f32_to_f16_numpy,
     check_quantize_act_closed_forms, check_gemv_q8act, check_q4k_bruteforce,
     check_q4k_one_hot_every_position, check_q4k_closed_form_constant, check_q6k_bruteforce,
-    check_q6k_one_hot_every_position, check_q6k_closed_form_constant,
+    check_q6k_one_hot_every_position, check_q6k_closed_form_constant, check_q5k_bruteforce,
+    check_q5k_one_hot_every_position,
 ]

@@ -54,15 +54,24 @@ MUTANTS = {
                           "double frac = floor((2.0 * m - 1.0) * 1024.0);"),
     "act_dot_column0": ("(int64_t)qx[n * K + b * QK + j];", "(int64_t)qx[b * QK + j];"),
     "act_weight_unsigned": ("(int64_t)(int8_t)blk[2 + j] *", "(int64_t)blk[2 + j] *"),
-    "q4k_scale_min_swapped": ("sj = sc[j] & 63;\n    mj = sc[j + 4] & 63;",
-                              "sj = sc[j + 4] & 63;\n    mj = sc[j] & 63;"),
+    "q4k_scale_min_swapped": ("*sj = sc[j] & 63;\n    *mj = sc[j + 4] & 63;",
+                              "*sj = sc[j + 4] & 63;\n    *mj = sc[j] & 63;"),
     "q4k_high_bits_wrong_byte": ("16 * (sc[j - 4] >> 6);", "16 * (sc[j] >> 6);"),
     "q4k_high_bits_unshifted": ("+ 16 * (sc[j] >> 6);", "+ (sc[j] >> 6);"),
     "q4k_nibble_swapped": ("(byte & 15) : (byte >> 4);", "(byte >> 4) : (byte & 15);"),
     "q4k_group_stride": ("b[16 + 32 * (kk / 64) + kk % 32]", "b[16 + 32 * (kk / 64) + kk % 16]"),
     "q4k_min_sign": ("- dmin * (double)mj;", "+ dmin * (double)mj;"),
-    "q4k_d_dmin_swapped": ("(uint16_t)(b[0] | (b[1] << 8)));\n  const double dmin",
-                           "(uint16_t)(b[2] | (b[3] << 8)));\n  const double dmin"),
+    "q4k_d_dmin_swapped": ("(uint16_t)(b[0] | (b[1] << 8)));\n  *dmin",
+                           "(uint16_t)(b[2] | (b[3] << 8)));\n  *dmin"),
+    "q5k_fifth_bit_index": ("const int fifth = (b[16 + kk % 32] >> j) & 1;",
+                            "const int fifth = (b[16 + kk % 32] >> (j / 2)) & 1;"),
+    "q5k_fifth_weight": ("(double)(low + 16 * fifth)", "(double)(low + 32 * fifth)"),
+    "q5k_qs_offset": ("byte5 = b[48 + 32 * (kk / 64) + kk % 32]", "byte5 = b[16 + 32 * (kk / 64) + kk % 32]"),
+    "q5k_nibble_swapped": ("(byte5 & 15) : (byte5 >> 4);", "(byte5 >> 4) : (byte5 & 15);"),
+    "q5k_min_sign": ("- dmin * (double)m5;", "+ dmin * (double)m5;"),
+    "q5k_wrong_subblock": ("const int j = kk / 32; /* sub-block */",
+                           "const int j = kk / 64; /* sub-block */"),
+    "q5k_qh_byte": ("(b[16 + kk % 32] >> j)", "(b[16 + kk % 16] >> j)"),
     "q6k_nibble_swapped": ("const int low = (a < 2) ? (lb & 15) : (lb >> 4);",
                            "const int low = (a < 2) ? (lb >> 4) : (lb & 15);"),
     "q6k_high_shift": (">> (2 * a)) & 3;", ">> a) & 3;"),

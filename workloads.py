@@ -150,6 +150,60 @@ def draw_q4k(g: np.random.Generator, M: int, K: int) -> Q4KMatrix:
 
 
 # --------------------------------------------------------------------------
+# Q5_K (GGUF k-quant, named on the cogni-ml page, cuda_q5k_gemv_probe).  A
+# 176-byte block: the Q4_K header (d, dmin, 12 scale/min bytes), then qh[32]
+# holding the fifth bit of weight k at bit k // 32 of qh[k % 32], then the
+# 128 nibble bytes of the low 4 bits placed as in Q4_K.  Codes 0..31,
+# weight = d * s * code - dmin * m.  Distributions: codes uniform 0..31, s
+# and m uniform 0..63, d = |N(0,1)| * 0.0005, dmin = |N(0,1)| * 0.004.
+# --------------------------------------------------------------------------
+Q5K_BYTES = 176
+
+
+@dataclasses.dataclass
+class Q5KMatrix:
+    """A Q5_K matrix as drawn: 5-bit codes [M][K], scales and mins [M][K/32],
+    d and dmin [M][K/256] float16."""
+    code: np.ndarray
+    s: np.ndarray
+    m: np.ndarray
+    d: np.ndarray
+    dmin: np.ndarray
+
+    @property
+    def M(self) -> int:
+        return self.code.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.code.shape[1]
+
+    def blocks(self) -> np.ndarray:
+        """GGUF Q5_K bytes, shape [M, K/256, 176] uint8."""
+        M, K = self.code.shape
+        B = K // QKK
+        low = (self.code & 15).astype(np.uint8)
+        q4 = Q4KMatrix(low, self.s, self.m, self.d, self.dmin).blocks()
+        out = np.zeros((M, B, Q5K_BYTES), dtype=np.uint8)
+        out[:, :, 0:16] = q4[:, :, 0:16]
+        out[:, :, 48:176] = q4[:, :, 16:144]
+        fifth = (self.code >> 4).astype(np.uint8).reshape(M, B, 8, 32)  # [j][l]
+        out[:, :, 16:48] = (fifth << np.arange(8, dtype=np.uint8)[None, None, :, None]).sum(
+            axis=2).astype(np.uint8)
+        return out
+
+
+def draw_q5k(g: np.random.Generator, M: int, K: int) -> Q5KMatrix:
+    """Codes, then scales, mins, d, dmin, from one generator."""
+    code = g.integers(0, 32, size=(M, K), dtype=np.uint8)
+    s = g.integers(0, 64, size=(M, K // 32), dtype=np.uint8)
+    m = g.integers(0, 64, size=(M, K // 32), dtype=np.uint8)
+    d = (np.abs(g.standard_normal((M, K // QKK))) * 0.0005).astype(np.float16)
+    dmin = (np.abs(g.standard_normal((M, K // QKK))) * 0.004).astype(np.float16)
+    return Q5KMatrix(code, s, m, d, dmin)
+
+
+# --------------------------------------------------------------------------
 # Q6_K (GGUF k-quant, named on the cogni-ml page, cuda_q6k_gemv_probe: ql, qh,
 # signed scales, d).  A 210-byte block holds 256 weights of one row: [0:128]
 # ql (low 4 bits), [128:192] qh (high 2 bits), [192:208] 16 int8 scales (one
