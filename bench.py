@@ -210,6 +210,27 @@ def rand_packed_q4k(M, K, n_mats, gen):
     return qs, meta.view(-1), qb, mb
 
 
+def rand_packed_q5k(M, K, n_mats, gen):
+    """Seeded packed Q5_K weights drawn on the device: nibbles, fifth bits and
+    6-bit scales/mins uniform (random bytes), d = |N(0,1)|*0.0005 and
+    dmin = |N(0,1)|*0.004 in binary16.  Returns qs, qh, meta tensors holding
+    n_mats packed matrices back to back and their per-matrix byte counts
+    (M % 64 == 0, K % 256 == 0)."""
+    import torch
+    import block_quantized_gemv_amd as q
+    assert M % 64 == 0 and K % 256 == 0
+    a, b, c = q.q5k_packed_size(M, K)
+    dev = torch.device("cuda", 0)
+    qs = torch.randint(0, 256, (n_mats * a,), dtype=torch.uint8, device=dev, generator=gen)
+    qh = torch.randint(0, 256, (n_mats * b,), dtype=torch.uint8, device=dev, generator=gen)
+    meta = torch.randint(0, 256, (n_mats * c // 16, 16), dtype=torch.uint8, device=dev,
+                         generator=gen)
+    hdr = torch.randn(n_mats * c // 16, 2, device=dev, generator=gen).abs()
+    hdr = (hdr * torch.tensor([0.0005, 0.004], device=dev)).half()
+    meta[:, 0:4] = hdr.view(torch.uint8).view(-1, 4)
+    return qs, qh, meta.view(-1), (a, b, c)
+
+
 def rand_packed_q6k(M, K, n_mats, gen):
     """Seeded packed Q6_K weights drawn on the device: every 6-bit code and
     int8 scale uniform (random bytes), d = |N(0,1)|*0.0002 in binary16.
@@ -235,8 +256,8 @@ def measure_rows(log, cold_bytes=1.2e9):
     cold weight copies (more than `cold_bytes` in rotation, beyond the 256 MB
     Infinity Cache): C1 896x896; the 0.5B layer shapes; lm_head with the fused
     RMSNorm/argmax and the standalone argmax; the 9B-class shapes at N = 1, 2,
-    4, 8; the integer-activation variant on the 9B gate_up shape; Q4_K
-    and Q6_K weights on the 9B shapes; the
+    4, 8; the integer-activation variant on the 9B gate_up shape; Q4_K,
+    Q5_K and Q6_K weights on the 9B shapes; the
     verify-chunk LM head with one argmax per column; the
     Qwen1.5-MoE-shaped FFN (router, scatter + SwiGLU, combine)."""
     import torch
@@ -337,6 +358,22 @@ def measure_rows(log, cold_bytes=1.2e9):
             rec("n2", f"C4-shaped {M}x{K} Q4_K N={N}{launches}", sec,
                 0.5625 * M * K + 4 * K * N + 4 * M * N)
             del views, qs, meta
+            torch.cuda.empty_cache()
+    # Q5_K weights (NEXT-2); algorithmic bytes are GGUF's 176 per 256 weights
+    for (M, K) in ((24576, 4096), (4096, 12288)):
+        for N in (1, 8):
+            n = max(2, min(64, int(cold_bytes // (0.6875 * M * K)) + 1))
+            qs, qh, meta, (a, b, c) = rand_packed_q5k(M, K, n, gen)
+            views = [q.PackedQ5K(qs[i * a:(i + 1) * a], qh[i * b:(i + 1) * b],
+                                 meta[i * c:(i + 1) * c], M, K) for i in range(n)]
+            x = torch.randn(N, K, device=dev, generator=gen)
+            y = torch.empty(N, M, device=dev)
+            ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_Q5K_GEMV, M, K, N))
+            sec = graph_time(lambda i: q.q5k_gemv(views[i % n], x, y, ws), n)
+            launches = "" if N <= 4 else " (2 launches)"
+            rec("n2", f"C4-shaped {M}x{K} Q5_K N={N}{launches}", sec,
+                176 / 256 * M * K + 4 * K * N + 4 * M * N)
+            del views, qs, qh, meta
             torch.cuda.empty_cache()
     # Q6_K weights (NEXT-2); algorithmic bytes are GGUF's 210 per 256 weights
     for (M, K) in ((4096, 12288), (24576, 4096)):

@@ -27,6 +27,7 @@ Q8_OP_GEMV, Q8_OP_GEMV_FUSED, Q8_OP_ARGMAX, Q8_OP_MOE_SCATTER, Q8_OP_MOE_COMBINE
 Q8_OP_GEMV_ARGMAX = 6
 Q8_OP_Q4K_GEMV = 7
 Q8_OP_Q6K_GEMV = 8
+Q8_OP_Q5K_GEMV = 9
 
 Q8_LAYOUT_ROWS, Q8_LAYOUT_GATE_UP_PAIRS = 0, 1
 Q8_CHAIN_QKV, Q8_CHAIN_H_ATTN, Q8_CHAIN_SWIGLU, Q8_CHAIN_H_OUT = 0, 1, 2, 3
@@ -36,7 +37,8 @@ EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv",
            "q8_0_route_topk", "q8_0_moe_gemv", "q8_0_workspace_bytes", "q8_0_gemv_plan",
            "q8_0_strerror", "q8_0_version", "q8_0_chain_workspace_bytes", "q8_0_chain_prepare",
            "q8_0_chain_run", "q8_0_chain_read", "q8_0_chain_status", "q4k_packed_size",
-           "q4k_repack", "q4k_gemv", "q6k_packed_size", "q6k_repack", "q6k_gemv")
+           "q4k_repack", "q4k_gemv", "q5k_packed_size", "q5k_repack", "q5k_gemv",
+           "q6k_packed_size", "q6k_repack", "q6k_gemv")
 
 
 class Q8Error(RuntimeError):
@@ -107,6 +109,10 @@ def lib() -> ctypes.CDLL:
         L.q4k_packed_size.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
         L.q4k_repack.argtypes = [P, I64, I64, P, P, P]
         L.q4k_gemv.argtypes = [ctypes.POINTER(q4k_weights), P, P, I64, I64, I64, P, SZ, P]
+        L.q5k_packed_size.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ),
+                                      ctypes.POINTER(SZ)]
+        L.q5k_repack.argtypes = [P, I64, I64, P, P, P, P]
+        L.q5k_gemv.argtypes = [ctypes.POINTER(q5k_weights), P, P, I64, I64, I64, P, SZ, P]
         L.q6k_packed_size.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ),
                                       ctypes.POINTER(SZ)]
         L.q6k_repack.argtypes = [P, I64, I64, P, P, P, P]
@@ -250,6 +256,55 @@ def q4k_gemv(W: PackedQ4K, x: torch.Tensor, y: torch.Tensor | None = None, works
     _need(y, torch.float32, "y")
     wsp, wsb = _ws(workspace, q8_0_workspace_bytes(Q8_OP_Q4K_GEMV, W.M, W.K, N), x.device)
     _check("q4k_gemv", lib().q4k_gemv(ctypes.byref(W.desc), x.data_ptr(), y.data_ptr(), W.M,
+                                      W.K, N, wsp, wsb, _stream(stream)))
+    return y
+
+
+class q5k_weights(ctypes.Structure):
+    _fields_ = [("qs", ctypes.c_void_p), ("qh", ctypes.c_void_p), ("meta", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class PackedQ5K:
+    """Packed device Q5_K weights of one matrix (see q5k_repack in q8gemv.h)."""
+
+    def __init__(self, qs: torch.Tensor, qh: torch.Tensor, meta: torch.Tensor, M: int, K: int):
+        self.qs, self.qh, self.meta, self.M, self.K = qs, qh, meta, M, K
+        self.desc = q5k_weights(qs.data_ptr(), qh.data_ptr(), meta.data_ptr(), M, K)
+
+    @classmethod
+    def from_blocks(cls, blocks: torch.Tensor, M: int, K: int, stream=None) -> "PackedQ5K":
+        """Repack GGUF Q5_K blocks (uint8 device tensor of M*(K/256)*176 bytes)."""
+        _need(blocks, torch.uint8, "blocks")
+        if blocks.numel() != M * (K // 256) * 176:
+            raise ValueError(f"blocks has {blocks.numel()} bytes, expected {M * (K // 256) * 176}")
+        a, b, c = q5k_packed_size(M, K)
+        qs = torch.empty(a, dtype=torch.uint8, device=blocks.device)
+        qh = torch.empty(b, dtype=torch.uint8, device=blocks.device)
+        meta = torch.empty(c, dtype=torch.uint8, device=blocks.device)
+        _check("q5k_repack", lib().q5k_repack(blocks.data_ptr(), M, K, qs.data_ptr(),
+                                              qh.data_ptr(), meta.data_ptr(), _stream(stream)))
+        return cls(qs, qh, meta, M, K)
+
+
+def q5k_packed_size(M: int, K: int) -> tuple[int, int, int]:
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check("q5k_packed_size", lib().q5k_packed_size(M, K, ctypes.byref(a), ctypes.byref(b),
+                                                    ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def q5k_gemv(W: PackedQ5K, x: torch.Tensor, y: torch.Tensor | None = None, workspace=None,
+             stream=None) -> torch.Tensor:
+    """y[N][M] = x[N][K] @ W^T for packed Q5_K weights W (x float32)."""
+    _need(x, torch.float32, "x")
+    N = 1 if x.dim() == 1 else x.shape[0]
+    if y is None:
+        y = torch.empty((W.M,) if x.dim() == 1 else (N, W.M), dtype=torch.float32,
+                        device=x.device)
+    _need(y, torch.float32, "y")
+    wsp, wsb = _ws(workspace, q8_0_workspace_bytes(Q8_OP_Q5K_GEMV, W.M, W.K, N), x.device)
+    _check("q5k_gemv", lib().q5k_gemv(ctypes.byref(W.desc), x.data_ptr(), y.data_ptr(), W.M,
                                       W.K, N, wsp, wsb, _stream(stream)))
     return y
 

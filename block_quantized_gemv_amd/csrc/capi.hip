@@ -332,6 +332,56 @@ int q4k_gemv(const q4k_weights* W, const float* x, float* y, int64_t M, int64_t 
   return Q8_OK;
 }
 
+// ---- Q5_K ----------------------------------------------------------------------
+int q5k_packed_size(int64_t M, int64_t K, size_t* qs_bytes, size_t* qh_bytes,
+                    size_t* meta_bytes) {
+  if (!qs_bytes || !qh_bytes || !meta_bytes) return Q8_ENULL;
+  if (!q4k_shape_ok(M, K)) return Q8_EINVAL;
+  const int64_t T = cdiv(M, kTile);
+  *qs_bytes = (size_t)(T * kTile * (K / 2));
+  *qh_bytes = (size_t)(T * kTile * (K / 8));
+  *meta_bytes = (size_t)(T * kTile * (K / 256) * 16);
+  return Q8_OK;
+}
+
+int q5k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* qh, void* meta,
+               void* stream) {
+  if (!q4k_shape_ok(M, K)) return Q8_EINVAL;
+  if (!blocks || !qs || !qh || !meta) return Q8_ENULL;
+  if (M == 0) return Q8_OK;
+  int rc;
+  if ((rc = check_dev_aligned(blocks, 4)) || (rc = check_dev_aligned(qs, 16)) ||
+      (rc = check_dev_aligned(qh, 16)) || (rc = check_dev_aligned(meta, 16)))
+    return rc;
+  return launch_q5k_repack(blocks, M, K, qs, qh, meta, static_cast<hipStream_t>(stream));
+}
+
+int q5k_gemv(const q5k_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
+             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!W) return Q8_ENULL;
+  if (W->M != M || W->K != K || !q4k_shape_ok(M, K) || N < 1 || N > Q8_MAX_N) return Q8_EINVAL;
+  if (!x || !y || !W->qs || !W->qh || !W->meta) return Q8_ENULL;
+  if (M == 0) return Q8_OK;
+  int rc;
+  if ((rc = check_dev_aligned(W->qs, 16)) || (rc = check_dev_aligned(W->qh, 16)) ||
+      (rc = check_dev_aligned(W->meta, 16)) || (rc = check_dev_aligned(x, 4)) ||
+      (rc = check_dev_aligned(y, 4)))
+    return rc;
+  if (workspace && (rc = check_dev(workspace))) return rc;
+  const q8_0_weights w8 = {W->qs, W->meta, M, K, 1, 0, 0, Q8_LAYOUT_ROWS, 0};
+  for (int64_t n0 = 0; n0 < N; n0 += kMaxQ4kN) {
+    const int64_t n = N - n0 < kMaxQ4kN ? N - n0 : kMaxQ4kN;
+    ProbDesc pd;
+    if ((rc = build_gemv(&w8, x + n0 * K, y + n0 * M, M, K, n, nullptr, &pd))) return rc;
+    pd.seg[0].fmt = FMT_Q5K;
+    pd.seg[0].qh = W->qh;
+    if ((rc = launch_problems(&pd, 1, (int)n, workspace, workspace_bytes,
+                              static_cast<hipStream_t>(stream))))
+      return rc;
+  }
+  return Q8_OK;
+}
+
 // ---- Q6_K ----------------------------------------------------------------------
 int q6k_packed_size(int64_t M, int64_t K, size_t* ql_bytes, size_t* qh_bytes,
                     size_t* meta_bytes) {
@@ -474,8 +524,8 @@ size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t
                             int32_t flags) {
   Plan plan;
   if (op == Q8_OP_ARGMAX) return argmax_ws_bytes(M);
-  if (op == Q8_OP_Q4K_GEMV || op == Q8_OP_Q6K_GEMV) {
-    // the largest need of the launches q4k_gemv / q6k_gemv make: columns in
+  if (op == Q8_OP_Q4K_GEMV || op == Q8_OP_Q5K_GEMV || op == Q8_OP_Q6K_GEMV) {
+    // the largest need of the launches q4k/q5k/q6k_gemv make: columns in
     // groups of kMaxQ4kN, each planned for its own format
     if (!shape_ok(M, K) || M == 0 || K % 256 || N < 1 || N > Q8_MAX_N) return 0;
     size_t need = 0;
@@ -485,7 +535,7 @@ size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t
       q8_0_weights W = {nullptr, nullptr, M, K, 1, 0, 0};
       ProbDesc pd;
       if (build_gemv(&W, nullptr, nullptr, M, K, n, nullptr, &pd)) return 0;
-      pd.seg[0].fmt = op == Q8_OP_Q6K_GEMV ? FMT_Q6K : FMT_Q4K;
+      pd.seg[0].fmt = op == Q8_OP_Q6K_GEMV ? FMT_Q6K : op == Q8_OP_Q5K_GEMV ? FMT_Q5K : FMT_Q4K;
       if (plan_problems(&pd, 1, (int)n, &plan)) return 0;
       if (plan.ws_bytes > need) need = plan.ws_bytes;
     }

@@ -203,25 +203,32 @@ __device__ __forceinline__ void dot_range(const uint8_t* qs_tile, const uint8_t*
   }
 }
 
-// ---- Q4_K weights ------------------------------------------------------------
+// ---- Q4_K and Q5_K weights ---------------------------------------------------
 // A quad is half of a 256-weight block: 4 sub-blocks of 32.  Sub-block j of
 // a row is 16 bytes whose byte i holds weights i (low nibble) and i + 16 (high
 // nibble), matching the activations' lanes (lanes 0..15 of a row hold x[i]
 // and x[i + 16]), so weight i and i + 16 both read lane i through the row
 // broadcast.  Per sub-block and column: y += d s * sum(q x) - dmin m * sum(x),
 // the sum of the 32 activations taken by DPP rotations within the row.
+// Q5_K adds a dword of fifth bits per sub-block and row, arranged so that the
+// 4 fifth bits of each half of a nibble dword reach bit 4 of its bytes with
+// one shift and one masked OR: bit 8b + I is that of weight 4I + b and bit
+// 8b + 4 + I that of weight 16 + 4I + b.
 
-template <int N>
+template <int N, bool Q5>
 struct QuadQ4 {
   u32x4 q[4];
   u32x4 meta;  // d, dmin (binary16), 12 bytes of 6-bit scales and mins
+  u32x4 f;     // Q5_K: fifth bits of the 4 sub-blocks
   XBlock<N> x[4];
 };
 
-template <int N>
-__device__ __forceinline__ void q4_load(QuadQ4<N>& B, const u32x4* qp, const u32x4* mp, int g,
-                                        const float* x, int64_t xs, int xl) {
+template <int N, bool Q5>
+__device__ __forceinline__ void q4_load(QuadQ4<N, Q5>& B, const u32x4* qp, const u32x4* mp,
+                                        const u32x4* fp, int g, const float* x, int64_t xs,
+                                        int xl) {
   B.meta = __builtin_nontemporal_load(mp + (g >> 1) * 64);
+  if constexpr (Q5) B.f = __builtin_nontemporal_load(fp + g * 64);
 #pragma unroll
   for (int i = 0; i < 4; ++i) B.q[i] = __builtin_nontemporal_load(qp + (4 * g + i) * 64);
 #pragma unroll
@@ -245,18 +252,16 @@ __device__ __forceinline__ void q4_scale_min(u32x4 meta, int h, int i, float& s,
   }
 }
 
+// p[n] += the 8 codes held in the bytes of cl (weights 4I .. 4I + 3 of the
+// sub-block) and ch (weights 16 + 4I ..) times their activations.  Byte b of a
+// dword to fp32 is one v_cvt_f32_ubyteN.
 template <int N, int I>
-__device__ __forceinline__ void q4_dword(uint32_t w, const XBlock<N>& X, float (&p)[N]) {
-  // Byte b of a dword to fp32 is one v_cvt_f32_ubyteN; the nibble masks are
-  // written as opaque VALU ops so the compiler keeps that form instead of
-  // folding each mask into a per-weight bit-field extract (two ops a weight).
-  uint32_t lo, hi;
-  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w));
-  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w >> 4));
-  const float l0 = (float)(lo & 255u), l1 = (float)((lo >> 8) & 255u);
-  const float l2 = (float)((lo >> 16) & 255u), l3 = (float)(lo >> 24);
-  const float h0 = (float)(hi & 255u), h1 = (float)((hi >> 8) & 255u);
-  const float h2 = (float)((hi >> 16) & 255u), h3 = (float)(hi >> 24);
+__device__ __forceinline__ void codes_fma(uint32_t cl, uint32_t ch, const XBlock<N>& X,
+                                          float (&p)[N]) {
+  const float l0 = (float)(cl & 255u), l1 = (float)((cl >> 8) & 255u);
+  const float l2 = (float)((cl >> 16) & 255u), l3 = (float)(cl >> 24);
+  const float h0 = (float)(ch & 255u), h1 = (float)((ch >> 8) & 255u);
+  const float h2 = (float)((ch >> 16) & 255u), h3 = (float)(ch >> 24);
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     fmac_row_bcast<4 * I + 0>(p[n], X.a[n], l0);
@@ -270,8 +275,25 @@ __device__ __forceinline__ void q4_dword(uint32_t w, const XBlock<N>& X, float (
   }
 }
 
-template <int N>
-__device__ __forceinline__ void q4_fma(const QuadQ4<N>& B, int h, float (&acc)[N]) {
+template <int N, bool Q5, int I>
+__device__ __forceinline__ void q4_dword(uint32_t w, uint32_t f, const XBlock<N>& X,
+                                         float (&p)[N]) {
+  // The nibble masks are written as opaque VALU ops so the compiler keeps the
+  // byte conversions instead of folding each mask into a per-weight bit-field
+  // extract (two ops a weight).
+  uint32_t lo, hi;
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w));
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w >> 4));
+  if constexpr (Q5) {
+    lo |= (f << (4 - I)) & 0x10101010u;
+    hi |= (f >> I) & 0x10101010u;
+    asm("" : "+v"(lo), "+v"(hi));
+  }
+  codes_fma<N, I>(lo, hi, X, p);
+}
+
+template <int N, bool Q5>
+__device__ __forceinline__ void q4_fma(const QuadQ4<N, Q5>& B, int h, float (&acc)[N]) {
   const float d = f16_to_f32(B.meta.x & 0xffffu), dmin = f16_to_f32(B.meta.x >> 16);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -280,10 +302,11 @@ __device__ __forceinline__ void q4_fma(const QuadQ4<N>& B, int h, float (&acc)[N
     float p[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) p[n] = 0.f;
-    q4_dword<N, 0>(B.q[i].x, B.x[i], p);
-    q4_dword<N, 1>(B.q[i].y, B.x[i], p);
-    q4_dword<N, 2>(B.q[i].z, B.x[i], p);
-    q4_dword<N, 3>(B.q[i].w, B.x[i], p);
+    const uint32_t f = Q5 ? B.f[i] : 0u;
+    q4_dword<N, Q5, 0>(B.q[i].x, f, B.x[i], p);
+    q4_dword<N, Q5, 1>(B.q[i].y, f, B.x[i], p);
+    q4_dword<N, Q5, 2>(B.q[i].z, f, B.x[i], p);
+    q4_dword<N, Q5, 3>(B.q[i].w, f, B.x[i], p);
     const float ds = d * s, dm = dmin * m;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
@@ -300,27 +323,29 @@ __device__ __forceinline__ void q4_fma(const QuadQ4<N>& B, int h, float (&acc)[N
   }
 }
 
-// Q4_K dot products of the 64 rows of one tile over 32-weight blocks
-// [b0, b1) (multiples of 4: whole quads), quads double-buffered.
-template <int N>
+// Q4_K (Q5 false) or Q5_K dot products of the 64 rows of one tile over
+// 32-weight blocks [b0, b1) (multiples of 4: whole quads), quads
+// double-buffered.  f_tile: Q5_K fifth bits (16 bytes per quad and row).
+template <int N, bool Q5>
 __device__ __forceinline__ void dot_range_q4k(const uint8_t* qs_tile, const uint8_t* meta_tile,
-                                              int b0, int b1, int lane, const float* x,
-                                              int64_t xs, float (&acc)[N]) {
+                                              const uint8_t* f_tile, int b0, int b1, int lane,
+                                              const float* x, int64_t xs, float (&acc)[N]) {
   const u32x4* qp = reinterpret_cast<const u32x4*>(qs_tile) + lane;
   const u32x4* mp = reinterpret_cast<const u32x4*>(meta_tile) + lane;
+  const u32x4* fp = reinterpret_cast<const u32x4*>(f_tile) + lane;
   const int xl = lane & 15;
   const int g0 = b0 >> 2, nq = (b1 - b0) >> 2;
   if (nq <= 0) return;
-  QuadQ4<N> A, B;
-  q4_load<N>(A, qp, mp, g0, x, xs, xl);
+  QuadQ4<N, Q5> A, B;
+  q4_load<N, Q5>(A, qp, mp, fp, g0, x, xs, xl);
   int it = 0;
   for (; it + 1 < nq; it += 2) {
-    q4_load<N>(B, qp, mp, g0 + it + 1, x, xs, xl);
-    q4_fma<N>(A, (g0 + it) & 1, acc);
-    if (it + 2 < nq) q4_load<N>(A, qp, mp, g0 + it + 2, x, xs, xl);
-    q4_fma<N>(B, (g0 + it + 1) & 1, acc);
+    q4_load<N, Q5>(B, qp, mp, fp, g0 + it + 1, x, xs, xl);
+    q4_fma<N, Q5>(A, (g0 + it) & 1, acc);
+    if (it + 2 < nq) q4_load<N, Q5>(A, qp, mp, fp, g0 + it + 2, x, xs, xl);
+    q4_fma<N, Q5>(B, (g0 + it + 1) & 1, acc);
   }
-  if (it < nq) q4_fma<N>(A, (g0 + it) & 1, acc);
+  if (it < nq) q4_fma<N, Q5>(A, (g0 + it) & 1, acc);
 }
 
 // ---- Q6_K weights ------------------------------------------------------------
@@ -706,10 +731,10 @@ __device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, 
 
 // ONE: a single problem with a single segment (dense GEMVs and the decode
 // chain): every kernel argument sits at a fixed offset, so no search loops.
-// MODE: 0 Q8_0 weights and fp32 activations; 1 integer activations; 2 Q4_K
-// and 3 Q6_K weights with fp32 activations.
+// MODE: 0 Q8_0 weights and fp32 activations; 1 integer activations; 2 Q4_K,
+// 3 Q6_K and 4 Q5_K weights with fp32 activations.
 template <int N, bool ONE, int MODE>
-__global__ __launch_bounds__(64 * max_waves_for(N, MODE == 3)) void gemv_kernel(const GemvParams p) {
+__global__ __launch_bounds__(64 * max_waves_for(N, MODE >= 3)) void gemv_kernel(const GemvParams p) {
   extern __shared__ float lds_part[];  // [W][N][64]
   __shared__ int s_last;
 
@@ -774,7 +799,11 @@ __global__ __launch_bounds__(64 * max_waves_for(N, MODE == 3)) void gemv_kernel(
       if (MODE == 1)
         dot_range_i8<N>(qs_tile, d_tile, b0, b1, lane, s.qx, s.dx, s.K, s.nblk, acc);
       else if (MODE == 2)
-        dot_range_q4k<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, acc);
+        dot_range_q4k<N, false>(qs_tile, d_tile, nullptr, b0, b1, lane, s.x, s.x_stride, acc);
+      else if (MODE == 4)
+        // Q5_K: 4 bytes of fifth bits per sub-block and row
+        dot_range_q4k<N, true>(qs_tile, d_tile, s.qh + (int64_t)t * kTile * (s.K / 8), b0, b1,
+                               lane, s.x, s.x_stride, acc);
       else if (MODE == 3)
         // Q6_K: 8 bytes of high fields per sub-block and row, 16 bytes of
         // scales and d per quad and row
@@ -1049,7 +1078,8 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
   // plan needs costs more than it gains.
   const bool wide = N >= 2 && total_tout >= num_cus();
   const int64_t want_u = wide ? 4 : cdiv(target_waves(), total_tout);
-  const int wfmt = max_waves_for(N, probs[0].seg[0].fmt == FMT_Q6K);
+  const int f0 = probs[0].seg[0].fmt;
+  const int wfmt = max_waves_for(N, f0 == FMT_Q6K || f0 == FMT_Q5K);
   int wmax = max_waves() < wfmt ? max_waves() : wfmt;
   if (wide && wmax > 4) wmax = 4;
   // units per tile
@@ -1147,10 +1177,13 @@ static hipError_t launch_n(const GemvParams& gp, int wgs, hipStream_t stream) {
   const size_t lds = (size_t)gp.W * N * 64 * sizeof(float);
   if (gp.seg[0].qx)  // the integer-activation path: one plain problem
     hipLaunchKernelGGL((gemv_kernel<N, true, 1>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
-  else if (gp.seg[0].fmt == FMT_Q4K || gp.seg[0].fmt == FMT_Q6K) {  // one plain problem, N <= 4
+  else if (gp.seg[0].fmt != FMT_Q8_0) {  // K-quants: one plain problem, N <= 4
     if constexpr (N <= kMaxQ4kN) {
       if (gp.seg[0].fmt == FMT_Q4K)
         hipLaunchKernelGGL((gemv_kernel<N, true, 2>), dim3(wgs), dim3(64 * gp.W), lds, stream,
+                           gp);
+      else if (gp.seg[0].fmt == FMT_Q5K)
+        hipLaunchKernelGGL((gemv_kernel<N, true, 4>), dim3(wgs), dim3(64 * gp.W), lds, stream,
                            gp);
       else
         hipLaunchKernelGGL((gemv_kernel<N, true, 3>), dim3(wgs), dim3(64 * gp.W), lds, stream,

@@ -16,8 +16,11 @@ constexpr int kTile = Q8_TILE_ROWS;  // rows per packed tile, one per lane
 // activations of a double-buffered quad take 16 N of them).
 constexpr int kMaxWaves = 16;
 constexpr int kMaxThreads = 64 * kMaxWaves;
-// (Q6_K keeps more per column in flight: 16-wave workgroups only at N = 1.)
-constexpr int max_waves_for(int N, bool q6k = false) { return N <= (q6k ? 1 : 2) ? 16 : 8; }
+// (Q5_K and Q6_K keep more per column in flight: 16-wave workgroups only at
+// N = 1.)
+constexpr int max_waves_for(int N, bool wide_quads = false) {
+  return N <= (wide_quads ? 1 : 2) ? 16 : 8;
+}
 constexpr int kMaxSeg = 9;           // K-segments over all problems of one launch
 constexpr int kMaxProb = 9;          // problems (independent GEMVs) per launch
 // Every workspace starts with a fixed region of 32-bit counters that each
@@ -32,9 +35,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Problem flags (the epilogue/prologue work of one problem).
 enum : int32_t { F_RMSNORM = 1, F_RESIDUAL = 2, F_SWIGLU = 4, F_ARGMAX = 8, F_PAIRED = 16 };
-// Weight formats: Q8_0 (qs = quants, d = scales) or Q4_K (qs = nibbles of
-// 32-weight sub-blocks, d = 16-byte block headers: d, dmin, scales/mins).
-enum : int32_t { FMT_Q8_0 = 0, FMT_Q4K = 1, FMT_Q6K = 2 };
+// Weight formats: Q8_0 (qs = quants, d = scales); Q4_K and Q5_K (qs = nibbles
+// of 32-weight sub-blocks, d = 16-byte block headers: d, dmin, scales/mins;
+// Q5_K's fifth bits in qh); Q6_K (qs = low nibbles, qh = 2-bit fields, d =
+// scales and d).
+enum : int32_t { FMT_Q8_0 = 0, FMT_Q4K = 1, FMT_Q6K = 2, FMT_Q5K = 3 };
 // Columns per Q4_K / Q6_K launch (more would spill registers; callers split N).
 constexpr int kMaxQ4kN = 4;
 // How a segment's partial sum is weighted in the fold.
@@ -64,7 +69,7 @@ struct Seg {
   const int8_t* qx;      // integer activations [N][K] (opt-in path), or nullptr
   const uint16_t* dx;    // their binary16 block scales [N][K / 32]
   int32_t fmt;           // FMT_*: how qs / d are packed
-  const uint8_t* qh;     // Q6_K: packed high 2-bit fields
+  const uint8_t* qh;     // Q6_K: packed high 2-bit fields; Q5_K: fifth bits
 };
 
 // One problem: an output of Mout rows computed from R row-tiles per output
@@ -108,7 +113,7 @@ struct SegDesc {
   const int8_t* qx;      // integer activations (opt-in path), or nullptr
   const uint16_t* dx;
   int32_t fmt;           // FMT_*
-  const void* qh;        // Q6_K high bits
+  const void* qh;        // Q6_K high bits, Q5_K fifth bits
   const q8_0_weights* W;
   const int32_t* eid;
   int32_t slot;
@@ -159,6 +164,8 @@ int launch_argmax(const float* v, int64_t n, int32_t* out, void* ws, size_t ws_b
 int launch_route(const float* logits, int32_t E, int32_t k, int32_t* ids, float* w,
                  hipStream_t stream);
 int launch_q4k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* meta,
+                      hipStream_t stream);
+int launch_q5k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* qh, void* meta,
                       hipStream_t stream);
 int launch_q6k_repack(const void* blocks, int64_t M, int64_t K, void* ql, void* qh, void* meta,
                       hipStream_t stream);

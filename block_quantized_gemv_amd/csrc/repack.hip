@@ -158,6 +158,89 @@ int launch_q4k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* 
   return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
 }
 
+// ---- Q5_K ------------------------------------------------------------------
+// GGUF Q5_K blocks ("skuznetsov/cogni-ml" README, cuda_q5k_gemv_probe; 176
+// bytes per 256 weights of one row: the 16-byte header of Q4_K, qh[32] whose
+// bit j of byte l is the fifth bit of sub-block j's weight l, then the 128
+// nibble bytes placed as in Q4_K) move into:
+//   qs, meta: as for Q4_K (the nibbles start at byte 48 instead of 16)
+//   qh:       per 64-row tile, per 128-weight quad, 16 bytes of each of the
+//             64 rows: one dword per sub-block of the quad, whose bit 8b + i is
+//             the fifth bit of weight 4i + b and bit 8b + 4 + i that of weight
+//             16 + 4i + b (i, b < 4), the order in which the GEMV merges them
+//             into its code bytes.
+// Bit moves only; padding rows are zeros.
+__global__ __launch_bounds__(256) void q5k_repack_qs_kernel(const uint32_t* __restrict__ src,
+                                                            int64_t M, int64_t K,
+                                                            u32x4* __restrict__ qs,
+                                                            uint32_t* __restrict__ qh,
+                                                            int64_t total) {
+  const int64_t nsub = K / 32, nsb = K / 256;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lane = idx & 63;
+    const int64_t c = (idx >> 6) % nsub;
+    const int64_t t = (idx >> 6) / nsub;
+    const int64_t r = t * 64 + lane;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    uint32_t fb = 0u;
+    if (r < M) {
+      const int j = (int)(c & 7);
+      const uint32_t* blk = src + (r * nsb + c / 8) * 176 / 4;
+      const uint32_t* g = blk + (48 + 32 * (j >> 1)) / 4;
+      const int sh = (j & 1) * 4;
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = ((g[i] >> sh) & 0x0F0F0F0Fu) | (((g[4 + i] >> sh) & 0x0F0F0F0Fu) << 4);
+      out = u32x4{o[0], o[1], o[2], o[3]};
+      // qh bytes l = 0..31 at block bytes 16..47, bit j of each
+      for (int l = 0; l < 32; ++l) {
+        const uint32_t bit = (blk[4 + l / 4] >> (8 * (l & 3) + j)) & 1u;
+        const int w = l & 15, i = w >> 2, b = w & 3;
+        fb |= bit << (8 * b + i + (l >= 16 ? 4 : 0));
+      }
+    }
+    qs[idx] = out;
+    qh[((t * (nsub / 4) + c / 4) * 64 + lane) * 4 + (c & 3)] = fb;
+  }
+}
+
+__global__ __launch_bounds__(256) void q5k_repack_meta_kernel(const uint32_t* __restrict__ src,
+                                                              int64_t M, int64_t K,
+                                                              u32x4* __restrict__ meta,
+                                                              int64_t total) {
+  const int64_t nsb = K / 256;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lane = idx & 63;
+    const int64_t b = (idx >> 6) % nsb;
+    const int64_t t = (idx >> 6) / nsb;
+    const int64_t r = t * 64 + lane;
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (r < M) {
+      const uint32_t* h = src + (r * nsb + b) * 176 / 4;
+      out = u32x4{h[0], h[1], h[2], h[3]};
+    }
+    meta[idx] = out;
+  }
+}
+
+int launch_q5k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* qh, void* meta,
+                      hipStream_t stream) {
+  const int64_t T = cdiv(M, kTile);
+  const int64_t nq = T * 64 * (K / 32);
+  const int64_t nm = T * 64 * (K / 256);
+  const auto* s32 = static_cast<const uint32_t*>(blocks);
+  auto grid = [](int64_t n) { return (unsigned)(n / 256 + 1 < 65536 ? n / 256 + 1 : 65536); };
+  hipLaunchKernelGGL(q5k_repack_qs_kernel, dim3(grid(nq)), dim3(256), 0, stream, s32, M, K,
+                     static_cast<u32x4*>(qs), static_cast<uint32_t*>(qh), nq);
+  if (hipGetLastError() != hipSuccess) return Q8_ELAUNCH;
+  hipLaunchKernelGGL(q5k_repack_meta_kernel, dim3(grid(nm)), dim3(256), 0, stream, s32, M, K,
+                     static_cast<u32x4*>(meta), nm);
+  return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
+}
+
 // ---- Q6_K ------------------------------------------------------------------
 // GGUF Q6_K blocks ("skuznetsov/cogni-ml" README, cuda_q6k_gemv_probe: ql, qh,
 // signed scales, d; 210 bytes per 256 weights: ql[128], qh[64], int8

@@ -269,6 +269,49 @@ int q4k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* meta, v
 int q4k_gemv(const q4k_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Q5_K weights (NEXT-2) -------------------------------------------------------
+ * GGUF Q5_K ("skuznetsov/cogni-ml" README, cuda_q5k_gemv_probe).  Reading of
+ * the packing (the page names the format; the arrangement is GGUF's): a
+ * 176-byte block holds 256 weights of one row: bytes 0-15 the Q4_K header (d,
+ * dmin, 12 bytes of 6-bit scales and mins), 16-47 qh (bit j of byte l is the
+ * fifth bit of weight 32 j + l), 48-175 the low 4 bits placed as Q4_K's
+ * nibbles; w_k = d s_j (low + 16 fifth) - dmin m_j, j = k / 32.
+ *
+ * Packed layout (q5k_repack), T = ceil(M / 64) tiles of 64 rows, t = r / 64,
+ * i = r % 64, c = 32-weight sub-block:
+ *  qs:   T * (K/32) * 64 * 16 bytes, the low 4 bits as q4k_repack's qs.
+ *  qh:   T * (K/128) * 64 * 16 bytes; at ((t * (K/128) + c / 4) * 64 + i) * 16
+ *        + 4 (c % 4) a dword whose bit 8b + a is the fifth bit of the
+ *        sub-block's weight 4a + b and bit 8b + 4 + a that of weight
+ *        16 + 4a + b (a, b < 4).
+ *  meta: as q4k_repack's meta (the 16-byte header of every block).
+ *  Rows M .. 64T-1 are zero.  Alignment: 16 bytes each. */
+typedef struct {
+  const void* qs;    /* device, packed low 4 bits */
+  const void* qh;    /* device, packed fifth bits */
+  const void* meta;  /* device, packed block headers */
+  int64_t M, K;
+} q5k_weights;
+
+/* Bytes of the packed arrays of one M x K Q5_K matrix.
+ * Errors: Q8_ENULL, Q8_EINVAL (M < 0, K <= 0, K % 256, K > Q8_MAX_K). */
+int q5k_packed_size(int64_t M, int64_t K, size_t* qs_bytes, size_t* qh_bytes,
+                    size_t* meta_bytes);
+
+/* Load-time repack of GGUF Q5_K blocks (device, M * K/256 blocks of 176 bytes,
+ * row-major, 4-byte aligned) into qs, qh and meta (device, q5k_packed_size()
+ * bytes, 16-byte aligned; every byte written).  Bit moves only.
+ * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_ELAUNCH. */
+int q5k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* qh, void* meta,
+               void* stream);
+
+/* y[n][r] = sum_k w[r][k] * x[n][k] with Q5_K weights; x, y, N, K and the
+ * workspace (op Q8_OP_Q5K_GEMV) as q4k_gemv.  Each sub-block adds
+ * d s_j * sum_k code_k x_k - dmin m_j * sum_k x_k in fp32 (code = low + 16
+ * fifth); columns run 4 per launch.  Errors as q8_0_gemv. */
+int q5k_gemv(const q5k_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
+             void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- Q6_K weights (NEXT-2) -------------------------------------------------------
  * GGUF Q6_K ("skuznetsov/cogni-ml" README, cuda_q6k_gemv_probe: ql, qh, signed
  * scales, d).  Reading of the packing (the page lists the fields; the
@@ -477,6 +520,7 @@ int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
  * op Q8_OP_GEMV_ARGMAX: (M, K, N) of q8_0_gemv_argmax.
  * op Q8_OP_Q4K_GEMV: (M, K, N) of q4k_gemv.
  * op Q8_OP_Q6K_GEMV: (M, K, N) of q6k_gemv.
+ * op Q8_OP_Q5K_GEMV: (M, K, N) of q5k_gemv.
  * op Q8_OP_ARGMAX: (n, 0, 0).
  * op Q8_OP_MOE_SCATTER / Q8_OP_MOE_COMBINE: (M, K, n_slots) with the
  *   shared expert's shape in (M2, K2) (0, 0 for none) and mode flags in flags.
@@ -489,6 +533,7 @@ int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
 #define Q8_OP_GEMV_ARGMAX 6
 #define Q8_OP_Q4K_GEMV 7
 #define Q8_OP_Q6K_GEMV 8
+#define Q8_OP_Q5K_GEMV 9
 size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t M2, int64_t K2,
                             int32_t flags);
 

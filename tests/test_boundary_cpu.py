@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "q8gemv.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:q8_0|q4k|q6k)_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b((?:q8_0|q4k|q5k|q6k)_\w+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -253,7 +253,7 @@ def test_q4k_rejects_bad_arguments_on_host():
                 q.q8_0_workspace_bytes(q.Q8_OP_GEMV, M, K, N))
     assert (q.q8_0_workspace_bytes(q.Q8_OP_Q4K_GEMV, 4096, 12288, 8) ==
             q.q8_0_workspace_bytes(q.Q8_OP_Q4K_GEMV, 4096, 12288, 4))
-    for op in (q.Q8_OP_Q4K_GEMV, q.Q8_OP_Q6K_GEMV):
+    for op in (q.Q8_OP_Q4K_GEMV, q.Q8_OP_Q5K_GEMV, q.Q8_OP_Q6K_GEMV):
         assert q.q8_0_workspace_bytes(op, 4096, 4000, 1) == 0
         assert q.q8_0_workspace_bytes(op, 4096, 4096, 9) == 0
 
@@ -275,3 +275,32 @@ def test_q6k_rejects_bad_arguments_on_host():
     assert L.q6k_gemv(ctypes.byref(W), dummy, dummy, 64, 512, 1, None, 0, None) == q.Q8_EINVAL
     W2 = q.q6k_weights(16, None, 16, 64, 256)
     assert L.q6k_gemv(ctypes.byref(W2), dummy, dummy, 64, 256, 1, None, 0, None) == q.Q8_ENULL
+
+
+def test_q5k_rejects_bad_arguments_on_host():
+    L = q.lib()
+    dummy = ctypes.c_void_p(16)
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.q5k_packed_size(130, 512, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 0
+    assert (a.value, b.value, c.value) == (192 * 256, 192 * 64, 192 * 2 * 16)
+    for K in (0, 32, 288):
+        assert L.q5k_packed_size(64, K, ctypes.byref(a), ctypes.byref(b),
+                                 ctypes.byref(c)) == q.Q8_EINVAL
+        assert L.q5k_repack(dummy, 64, K, dummy, dummy, dummy, None) == q.Q8_EINVAL
+    assert L.q5k_repack(dummy, 64, 256, dummy, None, dummy, None) == q.Q8_ENULL
+    assert L.q5k_packed_size(64, 256, None, ctypes.byref(b), ctypes.byref(c)) == q.Q8_ENULL
+    W = q.q5k_weights(16, 16, 16, 64, 256)
+    for N in (0, 9):
+        assert L.q5k_gemv(ctypes.byref(W), dummy, dummy, 64, 256, N, None, 0, None) == q.Q8_EINVAL
+    assert L.q5k_gemv(ctypes.byref(W), dummy, dummy, 64, 512, 1, None, 0, None) == q.Q8_EINVAL
+    assert L.q5k_gemv(None, dummy, dummy, 64, 256, 1, None, 0, None) == q.Q8_ENULL
+    W2 = q.q5k_weights(16, None, 16, 64, 256)
+    assert L.q5k_gemv(ctypes.byref(W2), dummy, dummy, 64, 256, 1, None, 0, None) == q.Q8_ENULL
+    # M = 0: nothing to do, nothing touched
+    W0 = q.q5k_weights(16, 16, 16, 0, 256)
+    assert L.q5k_gemv(ctypes.byref(W0), dummy, dummy, 0, 256, 1, None, 0, None) == q.Q8_OK
+    assert L.q5k_repack(dummy, 0, 256, dummy, dummy, dummy, None) == q.Q8_OK
+    # at N = 1 the plan is the Q4_K one (same quads, same wave count)
+    for (M, K) in [(151936, 1024), (4096, 12288), (64, 256)]:
+        assert (q.q8_0_workspace_bytes(q.Q8_OP_Q5K_GEMV, M, K, 1) ==
+                q.q8_0_workspace_bytes(q.Q8_OP_Q4K_GEMV, M, K, 1))

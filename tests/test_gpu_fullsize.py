@@ -104,3 +104,21 @@ def test_q6k_9b_shapes_sampled(mat):
         y = host(q.q6k_gemv(p, to_dev(x)))
         yr, _ = oracle.q6k_gemv(sub.blocks(), x)
         check(y[:, rows], yr, s2_bound(sub, x), f"Q6_K {M}x{K} N={N}")
+
+
+@pytest.mark.parametrize("mat", [W.MAT_GATE_UP, W.MAT_DOWN])
+def test_q5k_9b_shapes_sampled(mat):
+    """Q5_K weights (NEXT-2) at the 9B-class shapes the benchmark times, N = 1
+    and 8, sampled rows against the oracle; tolerance as in test_gpu_q5k."""
+    from test_gpu_q5k import check, pack5, s2_bound
+    M, K = W.C4_SHAPES[mat]
+    m = W.draw_q5k(W.rng(94, mat), M, K)
+    p = pack5(m)
+    g = np.random.default_rng(95 + mat)
+    rows = np.unique(np.concatenate([g.integers(0, M, 256), [0, 63, 64, M - 1]]))
+    sub = W.Q5KMatrix(m.code[rows], m.s[rows], m.m[rows], m.d[rows], m.dmin[rows])
+    for N in (1, 8):
+        x = W.activations(94, N, K, layer=N)
+        y = host(q.q5k_gemv(p, to_dev(x)))
+        yr, _ = oracle.q5k_gemv(sub.blocks(), x)
+        check(y[:, rows], yr, s2_bound(sub, x), f"Q5_K {M}x{K} N={N}")
