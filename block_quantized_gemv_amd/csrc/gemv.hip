@@ -1071,13 +1071,20 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
     segc += pd.nseg;
   }
   if (segc > kMaxSeg || nprob > kMaxProb || total_tout <= 0) return Q8_EINVAL;
-  // Several columns with at least one tile per compute unit: one workgroup
-  // of 4 waves per tile (4 K-units, longer-lived waves, more workgroups
-  // resident) measured best for every N >= 2 (C4 gate_up 24576x4096: N=2
-  // 28.3 -> 25.4 us, N=8 69 -> 52 us); with fewer tiles the K split such a
-  // plan needs costs more than it gains.
+  // Several columns with at least one tile per compute unit: workgroups of
+  // 4 waves (4 K-units each, longer-lived waves, more workgroups resident)
+  // measured best for every N >= 2 (C4 gate_up 24576x4096: N=2 28.3 -> 25.4
+  // us, N=8 69 -> 52 us); with fewer tiles the K split such a plan needs
+  // costs more than it gains.  One plain problem with fewer than two tiles
+  // per compute unit takes 8 units in two workgroups per tile instead: one
+  // workgroup per tile would leave half the compute units with twice the
+  // work of the others (the same gate_up shape at N = 4 and 8, Q8_0: 33.1 ->
+  // 29.6 and 52.5 -> 47.3 us; Q6_K at N = 8: 83.3 -> 71.8 us).  Not for the
+  // integer-activation path, which measured slower so (N = 8: 30.0 -> 35.4).
   const bool wide = N >= 2 && total_tout >= num_cus();
-  const int64_t want_u = wide ? 4 : cdiv(target_waves(), total_tout);
+  const bool wide_split = wide && nprob == 1 && probs[0].nseg == 1 && probs[0].R == 1 &&
+                          !probs[0].seg[0].qx && total_tout < 2 * (int64_t)num_cus();
+  const int64_t want_u = wide ? (wide_split ? 8 : 4) : cdiv(target_waves(), total_tout);
   const int f0 = probs[0].seg[0].fmt;
   const int wfmt = max_waves_for(N, f0 == FMT_Q6K || f0 == FMT_Q5K);
   int wmax = max_waves() < wfmt ? max_waves() : wfmt;
