@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import block_quantized_gemv_amd as q
@@ -304,3 +305,28 @@ def test_q5k_rejects_bad_arguments_on_host():
     for (M, K) in [(151936, 1024), (4096, 12288), (64, 256)]:
         assert (q.q8_0_workspace_bytes(q.Q8_OP_Q5K_GEMV, M, K, 1) ==
                 q.q8_0_workspace_bytes(q.Q8_OP_Q4K_GEMV, M, K, 1))
+
+
+def test_plan_invariants_over_random_shapes():
+    """The planner's output is a valid launch for every shape: waves per
+    workgroup within the kernel's launch bound, units within the K range,
+    workgroups covering every unit of every tile with none empty, and a
+    workspace large enough for the cross-workgroup partials."""
+    g = np.random.default_rng(123)
+    shapes = [(int(g.integers(1, 200000)), 32 * int(g.integers(1, 600)), int(g.integers(1, 9)))
+              for _ in range(1500)]
+    shapes += [(24576, 4096, N) for N in range(1, 9)] + [(151936, 896, N) for N in range(1, 9)]
+    shapes += [(64 * t, 4096, N) for t in (255, 256, 257, 383, 384, 511, 512, 513) for N in (1, 2, 8)]
+    for (M, K, N) in shapes:
+        p = q.q8_0_gemv_plan(M, K, N)
+        T, quads = -(-M // 64), -(-K // 128)
+        W, U, P = p["waves_per_wg"], p["units_per_tile"], p["wgs_per_tile"]
+        assert 1 <= W <= (16 if N <= 2 else 8), (M, K, N, p)
+        assert 1 <= U <= quads, (M, K, N, p)
+        assert P == -(-U // W) and U > (P - 1) * W, (M, K, N, p)
+        assert p["workgroups"] == T * P, (M, K, N, p)
+        ws = q.q8_0_workspace_bytes(q.Q8_OP_GEMV, M, K, N)
+        if P > 1:
+            assert ws >= 65536 + T * U * N * 64 * 4, (M, K, N, p, ws)
+        else:
+            assert ws == 0, (M, K, N, p, ws)
