@@ -283,8 +283,31 @@ int q8_0_gemv_fused(const q8_0_weights* W, const float* x, float* y, int64_t M, 
   return gemv_common(W, x, y, M, K, 1, fusion, nullptr, workspace, workspace_bytes, stream);
 }
 
-// ---- Q4_K ----------------------------------------------------------------------
+// ---- K-quants (Q4_K, Q5_K, Q6_K) ---------------------------------------------
 static bool q4k_shape_ok(int64_t M, int64_t K) { return shape_ok(M, K) && K % 256 == 0; }
+
+// The GEMV over packed K-quant weights: the launch machinery sees the nibble
+// (or low-bit) stream as qs, the per-block headers as d and the extra bit
+// stream (Q5_K, Q6_K) as qh.  Columns go kMaxQ4kN at a time; each launch
+// reads the weights once.  Pointers and alignments are checked by the caller.
+static int kquant_gemv(int32_t fmt, const void* qs, const void* qh, const void* meta,
+                       const float* x, float* y, int64_t M, int64_t K, int64_t N,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int rc;
+  if (workspace && (rc = check_dev(workspace))) return rc;
+  const q8_0_weights w8 = {qs, meta, M, K, 1, 0, 0, Q8_LAYOUT_ROWS, 0};
+  for (int64_t n0 = 0; n0 < N; n0 += kMaxQ4kN) {
+    const int64_t n = N - n0 < kMaxQ4kN ? N - n0 : kMaxQ4kN;
+    ProbDesc pd;
+    if ((rc = build_gemv(&w8, x + n0 * K, y + n0 * M, M, K, n, nullptr, &pd))) return rc;
+    pd.seg[0].fmt = fmt;
+    pd.seg[0].qh = qh;
+    if ((rc = launch_problems(&pd, 1, (int)n, workspace, workspace_bytes,
+                              static_cast<hipStream_t>(stream))))
+      return rc;
+  }
+  return Q8_OK;
+}
 
 int q4k_packed_size(int64_t M, int64_t K, size_t* qs_bytes, size_t* meta_bytes) {
   if (!qs_bytes || !meta_bytes) return Q8_ENULL;
@@ -316,23 +339,10 @@ int q4k_gemv(const q4k_weights* W, const float* x, float* y, int64_t M, int64_t 
   if ((rc = check_dev_aligned(W->qs, 16)) || (rc = check_dev_aligned(W->meta, 16)) ||
       (rc = check_dev_aligned(x, 4)) || (rc = check_dev_aligned(y, 4)))
     return rc;
-  if (workspace && (rc = check_dev(workspace))) return rc;
-  // the launch machinery sees the nibbles as qs and the block headers as d;
-  // columns go kMaxQ4kN at a time (each launch reads the weights once)
-  const q8_0_weights w8 = {W->qs, W->meta, M, K, 1, 0, 0, Q8_LAYOUT_ROWS, 0};
-  for (int64_t n0 = 0; n0 < N; n0 += kMaxQ4kN) {
-    const int64_t n = N - n0 < kMaxQ4kN ? N - n0 : kMaxQ4kN;
-    ProbDesc pd;
-    if ((rc = build_gemv(&w8, x + n0 * K, y + n0 * M, M, K, n, nullptr, &pd))) return rc;
-    pd.seg[0].fmt = FMT_Q4K;
-    if ((rc = launch_problems(&pd, 1, (int)n, workspace, workspace_bytes,
-                              static_cast<hipStream_t>(stream))))
-      return rc;
-  }
-  return Q8_OK;
+  return kquant_gemv(FMT_Q4K, W->qs, nullptr, W->meta, x, y, M, K, N, workspace, workspace_bytes,
+                     stream);
 }
 
-// ---- Q5_K ----------------------------------------------------------------------
 int q5k_packed_size(int64_t M, int64_t K, size_t* qs_bytes, size_t* qh_bytes,
                     size_t* meta_bytes) {
   if (!qs_bytes || !qh_bytes || !meta_bytes) return Q8_ENULL;
@@ -367,22 +377,10 @@ int q5k_gemv(const q5k_weights* W, const float* x, float* y, int64_t M, int64_t 
       (rc = check_dev_aligned(W->meta, 16)) || (rc = check_dev_aligned(x, 4)) ||
       (rc = check_dev_aligned(y, 4)))
     return rc;
-  if (workspace && (rc = check_dev(workspace))) return rc;
-  const q8_0_weights w8 = {W->qs, W->meta, M, K, 1, 0, 0, Q8_LAYOUT_ROWS, 0};
-  for (int64_t n0 = 0; n0 < N; n0 += kMaxQ4kN) {
-    const int64_t n = N - n0 < kMaxQ4kN ? N - n0 : kMaxQ4kN;
-    ProbDesc pd;
-    if ((rc = build_gemv(&w8, x + n0 * K, y + n0 * M, M, K, n, nullptr, &pd))) return rc;
-    pd.seg[0].fmt = FMT_Q5K;
-    pd.seg[0].qh = W->qh;
-    if ((rc = launch_problems(&pd, 1, (int)n, workspace, workspace_bytes,
-                              static_cast<hipStream_t>(stream))))
-      return rc;
-  }
-  return Q8_OK;
+  return kquant_gemv(FMT_Q5K, W->qs, W->qh, W->meta, x, y, M, K, N, workspace, workspace_bytes,
+                     stream);
 }
 
-// ---- Q6_K ----------------------------------------------------------------------
 int q6k_packed_size(int64_t M, int64_t K, size_t* ql_bytes, size_t* qh_bytes,
                     size_t* meta_bytes) {
   if (!ql_bytes || !qh_bytes || !meta_bytes) return Q8_ENULL;
@@ -417,19 +415,8 @@ int q6k_gemv(const q6k_weights* W, const float* x, float* y, int64_t M, int64_t 
       (rc = check_dev_aligned(W->meta, 16)) || (rc = check_dev_aligned(x, 4)) ||
       (rc = check_dev_aligned(y, 4)))
     return rc;
-  if (workspace && (rc = check_dev(workspace))) return rc;
-  const q8_0_weights w8 = {W->ql, W->meta, M, K, 1, 0, 0, Q8_LAYOUT_ROWS, 0};
-  for (int64_t n0 = 0; n0 < N; n0 += kMaxQ4kN) {
-    const int64_t n = N - n0 < kMaxQ4kN ? N - n0 : kMaxQ4kN;
-    ProbDesc pd;
-    if ((rc = build_gemv(&w8, x + n0 * K, y + n0 * M, M, K, n, nullptr, &pd))) return rc;
-    pd.seg[0].fmt = FMT_Q6K;
-    pd.seg[0].qh = W->qh;
-    if ((rc = launch_problems(&pd, 1, (int)n, workspace, workspace_bytes,
-                              static_cast<hipStream_t>(stream))))
-      return rc;
-  }
-  return Q8_OK;
+  return kquant_gemv(FMT_Q6K, W->ql, W->qh, W->meta, x, y, M, K, N, workspace, workspace_bytes,
+                     stream);
 }
 
 int q8_0_quantize_act(const float* x, int64_t K, int64_t N, int8_t* qx, uint16_t* dx,
