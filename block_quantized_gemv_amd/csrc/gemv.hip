@@ -1081,14 +1081,21 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
   // work of the others (the same gate_up shape at N = 4 and 8, Q8_0: 33.1 ->
   // 29.6 and 52.5 -> 47.3 us; Q6_K at N = 8: 83.3 -> 71.8 us).  Not for the
   // integer-activation path, which measured slower so (N = 8: 30.0 -> 35.4).
-  const bool wide = N >= 2 && total_tout >= num_cus();
+  // K-quant weights (a quad is 4-7 KB instead of 8.5) take the same 4-wave
+  // plans at N = 1, with half the waves per launch when the tiles are few:
+  // longer units amortise each wave's first load (N = 1, Q5_K / Q6_K gate_up
+  // 24576x4096: 21.0 -> 20.6, 26.2 -> 24.6 us; down 4096x12288: 15.5 -> 14.3,
+  // 17.2 -> 16.8 us).
+  const int f0 = probs[0].seg[0].fmt;
+  const bool kq = f0 != FMT_Q8_0 && N == 1;
+  const bool wide = (N >= 2 || kq) && total_tout >= num_cus();
   const bool wide_split = wide && nprob == 1 && probs[0].nseg == 1 && probs[0].R == 1 &&
                           !probs[0].seg[0].qx && total_tout < 2 * (int64_t)num_cus();
-  const int64_t want_u = wide ? (wide_split ? 8 : 4) : cdiv(target_waves(), total_tout);
-  const int f0 = probs[0].seg[0].fmt;
+  const int64_t want_u = wide ? (wide_split ? 8 : 4)
+                              : cdiv(kq ? target_waves() / 2 : target_waves(), total_tout);
   const int wfmt = max_waves_for(N, f0 == FMT_Q6K || f0 == FMT_Q5K);
   int wmax = max_waves() < wfmt ? max_waves() : wfmt;
-  if (wide && wmax > 4) wmax = 4;
+  if ((wide || kq) && wmax > 4) wmax = 4;
   // units per tile
   int sbase = 0;
   int64_t U[kMaxProb];

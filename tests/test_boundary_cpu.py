@@ -247,13 +247,13 @@ def test_q4k_rejects_bad_arguments_on_host():
     assert L.q4k_gemv(ctypes.byref(W), dummy, dummy, 64, 512, 1, None, 0, None) == q.Q8_EINVAL
     assert L.q4k_gemv(None, dummy, dummy, 64, 256, 1, None, 0, None) == q.Q8_ENULL
     assert L.q4k_gemv(ctypes.byref(W), None, dummy, 64, 256, 1, None, 0, None) == q.Q8_ENULL
-    # up to 4 columns a Q4_K GEMV plans like a Q8_0 GEMV of the same shape;
-    # beyond, it runs 4 columns at a time and needs the larger group's
-    for (M, K, N) in [(151936, 1024, 1), (4096, 12288, 2), (64, 256, 4)]:
-        assert (q.q8_0_workspace_bytes(q.Q8_OP_Q4K_GEMV, M, K, N) ==
-                q.q8_0_workspace_bytes(q.Q8_OP_GEMV, M, K, N))
-    assert (q.q8_0_workspace_bytes(q.Q8_OP_Q4K_GEMV, 4096, 12288, 8) ==
-            q.q8_0_workspace_bytes(q.Q8_OP_Q4K_GEMV, 4096, 12288, 4))
+    # beyond 4 columns a K-quant GEMV runs 4 columns at a time and needs the
+    # larger group's workspace; a split plan needs the counters and partials
+    for op in (q.Q8_OP_Q4K_GEMV, q.Q8_OP_Q5K_GEMV, q.Q8_OP_Q6K_GEMV):
+        ws = {N: q.q8_0_workspace_bytes(op, 4096, 12288, N) for N in range(1, 9)}
+        assert ws[8] == ws[4] and ws[5] == max(ws[4], ws[1]), ws
+        assert all(v >= 65536 + 64 * 64 * 4 for v in ws.values()), ws  # 64 tiles, split K
+        assert q.q8_0_workspace_bytes(op, 64, 256, 1) == 0  # one quad: one unit
     for op in (q.Q8_OP_Q4K_GEMV, q.Q8_OP_Q5K_GEMV, q.Q8_OP_Q6K_GEMV):
         assert q.q8_0_workspace_bytes(op, 4096, 4000, 1) == 0
         assert q.q8_0_workspace_bytes(op, 4096, 4096, 9) == 0
