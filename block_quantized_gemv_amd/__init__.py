@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libq8gemv.so")
 
 Q8_OK, Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_EWORKSPACE, Q8_ELAUNCH = 0, -1, -2, -3, -4, -5, -6
 Q8_MAX_N = 8
+Q8_MAX_K = 1 << 20
 Q8_MAX_SLOTS = 8
 Q8_TILE_ROWS = 64
 Q8_PRO_NONE, Q8_PRO_RMSNORM, Q8_PRO_GQA = 0, 1, 2

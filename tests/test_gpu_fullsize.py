@@ -122,3 +122,31 @@ def test_q5k_9b_shapes_sampled(mat):
         y = host(q.q5k_gemv(p, to_dev(x)))
         yr, _ = oracle.q5k_gemv(sub.blocks(), x)
         check(y[:, rows], yr, s2_bound(sub, x), f"Q5_K {M}x{K} N={N}")
+
+
+@pytest.mark.parametrize("N", [1, 5])
+def test_gemv_at_the_largest_k(N):
+    """K = Q8_MAX_K (2^20, the largest the boundary accepts) with a ragged
+    row count: every output against the oracle.  The longest units and the
+    largest in-kernel offsets of the Q8_0 path."""
+    M, K = 130, q.Q8_MAX_K
+    g = W.rng(97, N, K)
+    m = W.draw_matrix(g, M, K)
+    x = W.draw_x(g, N, K)
+    y = host(q.q8_0_gemv(pack(m), to_dev(x)))
+    yr, S = oracle.gemv(m.aos(), x)
+    q8tol.check(y, yr, S, f"gemv {M}x{K} N={N}")
+
+
+def test_q4k_gemv_at_the_largest_k():
+    """The same for Q4_K weights (K = 2^20, ragged M, N = 1 and 5)."""
+    from test_gpu_q4k import check, pack4, s2_bound
+    M, K = 65, q.Q8_MAX_K
+    g = W.rng(98, M, K)
+    m = W.draw_q4k(g, M, K)
+    p = pack4(m)
+    for N in (1, 5):
+        x = W.draw_x(g, N, K)
+        y = host(q.q4k_gemv(p, to_dev(x)))
+        yr, _ = oracle.q4k_gemv(m.blocks(), x)
+        check(y, yr, s2_bound(m, x), f"Q4_K {M}x{K} N={N}")
