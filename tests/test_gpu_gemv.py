@@ -297,3 +297,40 @@ def test_gemv_argmax_rejects_bad_arguments():
                                 host_am.ctypes.data, wsp, wsb, None) == q.Q8_EHOSTPTR
     assert lib.q8_0_gemv_argmax(p.desc, x.data_ptr(), y.data_ptr(), M, K, 2, am.data_ptr() + 2,
                                 wsp, wsb, None) == q.Q8_EALIGN
+
+
+def test_split_plans_replay_bitwise_in_a_graph():
+    """GEMVs whose tiles span several workgroups (ticketed cross-workgroup
+    fold, counters the kernel itself returns to zero) captured in a HIP graph:
+    every replay, with eager calls on the same workspace between replays,
+    equals the eager result bitwise.  Q8_0 at N = 1 and 8 and Q6_K at N = 1."""
+    from test_gpu_q6k import pack6
+    g = W.rng(21)
+    cases = []
+    m = W.draw_matrix(g, 896, 4864)
+    p = pack(m)
+    for N in (1, 8):
+        x = to_dev(W.draw_x(g, N, 4864))
+        assert q.q8_0_gemv_plan(896, 4864, N)["wgs_per_tile"] > 1
+        cases.append(lambda y, ws, p=p, x=x: q.q8_0_gemv(p, x, y, ws))
+    m6 = W.draw_q6k(g, 256, 12288)
+    p6 = pack6(m6)
+    x6 = to_dev(W.draw_x(g, 1, 12288))
+    cases.append(lambda y, ws: q.q6k_gemv(p6, x6, y, ws))
+    ws = q.Workspace(1 << 22)
+    for run in cases:
+        eager = run(None, ws).clone()
+        torch.cuda.synchronize()
+        y = torch.empty_like(eager)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            run(y, ws)
+        for _ in range(4):
+            y.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, eager)
+            assert torch.equal(run(None, ws), eager)  # eager call between replays
+            torch.cuda.synchronize()
