@@ -12,7 +12,7 @@ covers 32 consecutive weights of one row and is 34 bytes: a little-endian
 IEEE binary16 scale d followed by 32 signed 8-bit quants.  Blocks of a row are
 consecutive, rows are consecutive.
 
-Value distributions (the workloads this build measures):
+Value distributions (of the benchmarked and tested workloads):
   quants  discrete uniform in [-127, 127], both ends inclusive
   scales  |N(0,1)| * 0.01, rounded to binary16 (round-to-nearest-even)
   x       N(0,1) in float32, shape [N][K]
