@@ -1117,6 +1117,9 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
     const int64_t us_min = cdiv(min_units(), pd.R);
     if (us < us_min) us = us_min;
     if (us > us_max) us = us_max;
+    // (few tiles, long K: at least 2 quads a unit; C2 down 896x4864 with 38
+    // units of 1 quad 8.2 us, 19 units of 2 quads 7.2 us)
+    if (few && us > blocks / 2) us = blocks / 2 > 0 ? blocks / 2 : 1;
     if (us < pd.nseg) us = pd.nseg;
     if (us > blocks) us = blocks;
     // With few tiles per compute unit the slowest wave sets the pace: prefer
