@@ -1091,13 +1091,15 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
   const bool wide = (N >= 2 || kq) && total_tout >= num_cus();
   const bool wide_split = wide && nprob == 1 && probs[0].nseg == 1 && probs[0].R == 1 &&
                           !probs[0].seg[0].qx && total_tout < 2 * (int64_t)num_cus();
-  // Q8_0 with few tiles and a long K (one plain problem, N <= 4) takes the
-  // same shape: C4 down 4096x12288 went from 32 units of 3 quads in 8-wave
-  // workgroups to 16 units of 6 quads in 4-wave ones, N = 1 / 2 / 4: 15.8 ->
-  // 14.6, 17.8 -> 16.3, 21.7 -> 19.9 us.
-  const bool few = !wide && f0 == FMT_Q8_0 && N <= 4 && nprob == 1 && probs[0].nseg == 1 &&
-                   probs[0].R == 1 && !probs[0].seg[0].qx && total_tout < num_cus() &&
-                   probs[0].seg[0].W->K >= 4096;
+  // Q8_0 with few tiles and a long K (one problem, N <= 4; K summed over its
+  // segments) takes the same shape: C4 down 4096x12288 went from 32 units of
+  // 3 quads in 8-wave workgroups to 16 units of 6 quads in 4-wave ones, N = 1
+  // / 2 / 4: 15.8 -> 14.6, 17.8 -> 16.3, 21.7 -> 19.9 us; the MoE combine
+  // (five segments, K = 11264) 13.6 -> 13.0 us.
+  int64_t k_total = 0;
+  for (int s = 0; s < probs[0].nseg; ++s) k_total += probs[0].seg[s].W->K;
+  const bool few = !wide && f0 == FMT_Q8_0 && N <= 4 && nprob == 1 && probs[0].R == 1 &&
+                   !probs[0].seg[0].qx && total_tout < num_cus() && k_total >= 4096;
   const int64_t want_u =
       wide ? (wide_split ? 8 : 4)
            : cdiv((kq || few) ? target_waves() / 2 : target_waves(), total_tout);
