@@ -354,8 +354,7 @@ def measure_rows(log, cold_bytes=1.2e9):
             y = torch.empty(N, M, device=dev)
             ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_Q4K_GEMV, M, K, N))
             sec = graph_time(lambda i: q.q4k_gemv(views[i % n], x, y, ws), n)
-            launches = "" if N <= 4 else " (2 launches)"
-            rec("n2", f"C4-shaped {M}x{K} Q4_K N={N}{launches}", sec,
+            rec("n2", f"C4-shaped {M}x{K} Q4_K N={N}", sec,
                 0.5625 * M * K + 4 * K * N + 4 * M * N)
             del views, qs, meta
             torch.cuda.empty_cache()
@@ -370,8 +369,7 @@ def measure_rows(log, cold_bytes=1.2e9):
             y = torch.empty(N, M, device=dev)
             ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_Q5K_GEMV, M, K, N))
             sec = graph_time(lambda i: q.q5k_gemv(views[i % n], x, y, ws), n)
-            launches = "" if N <= 4 else " (2 launches)"
-            rec("n2", f"C4-shaped {M}x{K} Q5_K N={N}{launches}", sec,
+            rec("n2", f"C4-shaped {M}x{K} Q5_K N={N}", sec,
                 176 / 256 * M * K + 4 * K * N + 4 * M * N)
             del views, qs, qh, meta
             torch.cuda.empty_cache()
@@ -386,8 +384,7 @@ def measure_rows(log, cold_bytes=1.2e9):
             y = torch.empty(N, M, device=dev)
             ws = q.Workspace(q.q8_0_workspace_bytes(q.Q8_OP_Q6K_GEMV, M, K, N))
             sec = graph_time(lambda i: q.q6k_gemv(views[i % n], x, y, ws), n)
-            launches = "" if N <= 4 else " (2 launches)"
-            rec("n2", f"C4-shaped {M}x{K} Q6_K N={N}{launches}", sec,
+            rec("n2", f"C4-shaped {M}x{K} Q6_K N={N}", sec,
                 210 / 256 * M * K + 4 * K * N + 4 * M * N)
             del views, ql, qh, meta
             torch.cuda.empty_cache()

@@ -477,6 +477,151 @@ __device__ __forceinline__ void dot_range_q6k(const uint8_t* qs_tile, const uint
   if (it < nq) q6_fma<N>(A, acc);
 }
 
+// Several columns (N > 4): a ring of single sub-block buffers, so that the
+// activations of only RING sub-blocks are live and all N columns fit one
+// launch (the weights are read once; N = 8, Q4_K 24576x4096: two launches of
+// 4 columns 61.6 us, one launch with a ring of 2 48.1 us).
+template <int N>
+struct SubQ4 {
+  u32x4 q;
+  u32x4 meta;
+  uint32_t f;
+  XBlock<N> x;
+};
+
+template <int N, bool Q5>
+__device__ __forceinline__ void sub_load_q4(SubQ4<N>& B, const u32x4* qp, const u32x4* mp,
+                                            const uint32_t* fp, int sb, const float* x,
+                                            int64_t xs, int xl) {
+  B.q = __builtin_nontemporal_load(qp + sb * 64);
+  B.meta = __builtin_nontemporal_load(mp + (sb >> 3) * 64);
+  if constexpr (Q5) B.f = __builtin_nontemporal_load(fp + (sb >> 2) * 256 + (sb & 3));
+  load_xblock<N>(x + 32 * sb, xs, xl, B.x);
+}
+
+template <int N, bool Q5>
+__device__ __forceinline__ void sub_fma_q4(const SubQ4<N>& B, int sb, float (&acc)[N]) {
+  const float d = f16_to_f32(B.meta.x & 0xffffu), dmin = f16_to_f32(B.meta.x >> 16);
+  float s, m;
+  q4_scale_min(B.meta, (sb >> 2) & 1, sb & 3, s, m);
+  float p[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) p[n] = 0.f;
+  const uint32_t f = Q5 ? B.f : 0u;
+  q4_dword<N, Q5, 0>(B.q.x, f, B.x, p);
+  q4_dword<N, Q5, 1>(B.q.y, f, B.x, p);
+  q4_dword<N, Q5, 2>(B.q.z, f, B.x, p);
+  q4_dword<N, Q5, 3>(B.q.w, f, B.x, p);
+  const float ds = d * s, dm = dmin * m;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    float sx = B.x.a[n] + B.x.b[n];
+    sx = dpp_add<0x128>(sx);
+    sx = dpp_add<0x124>(sx);
+    sx = dpp_add<0x122>(sx);
+    sx = dpp_add<0x121>(sx);
+    acc[n] = fmaf(ds, p[n], acc[n]);
+    acc[n] = fmaf(-dm, sx, acc[n]);
+  }
+}
+
+template <int N, bool Q5, int RING>
+__device__ __forceinline__ void dot_range_q4k_ring(const uint8_t* qs_tile, const uint8_t* meta_tile,
+                                                   const uint8_t* f_tile, int b0, int b1, int lane,
+                                                   const float* x, int64_t xs, float (&acc)[N]) {
+  const u32x4* qp = reinterpret_cast<const u32x4*>(qs_tile) + lane;
+  const u32x4* mp = reinterpret_cast<const u32x4*>(meta_tile) + lane;
+  const uint32_t* fp = reinterpret_cast<const uint32_t*>(f_tile) + 4 * lane;
+  const int xl = lane & 15;
+  SubQ4<N> S[RING];
+#pragma unroll
+  for (int r = 0; r < RING; ++r)
+    if (b0 + r < b1) sub_load_q4<N, Q5>(S[r], qp, mp, fp, b0 + r, x, xs, xl);
+  for (int b = b0; b < b1; b += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      if (b + r < b1) {
+        sub_fma_q4<N, Q5>(S[r], b + r, acc);
+        if (b + r + RING < b1) sub_load_q4<N, Q5>(S[r], qp, mp, fp, b + r + RING, x, xs, xl);
+      }
+    }
+  }
+}
+
+template <int N>
+struct SubQ6 {
+  u32x4 q;
+  u32x2 h;
+  u32x4 meta;
+  XBlock<N> x;
+};
+
+template <int N>
+__device__ __forceinline__ void sub_load_q6(SubQ6<N>& B, const u32x4* qp, const u32x2* hp,
+                                            const u32x4* mp, int sb, const float* x, int64_t xs,
+                                            int xl) {
+  B.q = __builtin_nontemporal_load(qp + sb * 64);
+  B.h = __builtin_nontemporal_load(hp + sb * 64);
+  B.meta = __builtin_nontemporal_load(mp + (sb >> 2) * 64);
+  load_xblock<N>(x + 32 * sb, xs, xl, B.x);
+}
+
+template <int N>
+__device__ __forceinline__ void sub_fma_q6(const SubQ6<N>& B, int sb, float (&acc)[N]) {
+  const float d = f16_to_f32(B.meta.z & 0xffffu);
+  const int i = sb & 3;
+  const uint32_t sw = i < 2 ? B.meta.x : B.meta.y;
+  const float sl = d * (float)(int8_t)(sw >> (16 * (i & 1)));
+  const float sh = d * (float)(int8_t)(sw >> (16 * (i & 1) + 8));
+  float pl[N], ph[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) pl[n] = ph[n] = 0.f;
+  q6_dword<N, 0>(B.q.x, B.h.x, B.h.y, B.x, pl, ph);
+  q6_dword<N, 1>(B.q.y, B.h.x, B.h.y, B.x, pl, ph);
+  q6_dword<N, 2>(B.q.z, B.h.x, B.h.y, B.x, pl, ph);
+  q6_dword<N, 3>(B.q.w, B.h.x, B.h.y, B.x, pl, ph);
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    float sa = B.x.a[n], sbx = B.x.b[n];
+    sa = dpp_add<0x128>(sa);
+    sbx = dpp_add<0x128>(sbx);
+    sa = dpp_add<0x124>(sa);
+    sbx = dpp_add<0x124>(sbx);
+    sa = dpp_add<0x122>(sa);
+    sbx = dpp_add<0x122>(sbx);
+    sa = dpp_add<0x121>(sa);
+    sbx = dpp_add<0x121>(sbx);
+    acc[n] = fmaf(sl, pl[n], acc[n]);
+    acc[n] = fmaf(-32.0f * sl, sa, acc[n]);
+    acc[n] = fmaf(sh, ph[n], acc[n]);
+    acc[n] = fmaf(-32.0f * sh, sbx, acc[n]);
+  }
+}
+
+template <int N, int RING>
+__device__ __forceinline__ void dot_range_q6k_ring(const uint8_t* qs_tile, const uint8_t* qh_tile,
+                                                   const uint8_t* meta_tile, int b0, int b1,
+                                                   int lane, const float* x, int64_t xs,
+                                                   float (&acc)[N]) {
+  const u32x4* qp = reinterpret_cast<const u32x4*>(qs_tile) + lane;
+  const u32x2* hp = reinterpret_cast<const u32x2*>(qh_tile) + lane;
+  const u32x4* mp = reinterpret_cast<const u32x4*>(meta_tile) + lane;
+  const int xl = lane & 15;
+  SubQ6<N> S[RING];
+#pragma unroll
+  for (int r = 0; r < RING; ++r)
+    if (b0 + r < b1) sub_load_q6<N>(S[r], qp, hp, mp, b0 + r, x, xs, xl);
+  for (int b = b0; b < b1; b += RING) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      if (b + r < b1) {
+        sub_fma_q6<N>(S[r], b + r, acc);
+        if (b + r + RING < b1) sub_load_q6<N>(S[r], qp, hp, mp, b + r + RING, x, xs, xl);
+      }
+    }
+  }
+}
+
 // ---- integer activations (opt-in variant) ------------------------------------
 // Activations quantized per 32-entry block to int8 with a binary16 scale
 // (q8_0_quantize_act).  Per block and column the 32 int8 x int8 products are
@@ -798,17 +943,32 @@ __global__ __launch_bounds__(64 * max_waves_for(N, MODE >= 3)) void gemv_kernel(
       const int b1 = b1e < s.nblk ? b1e : s.nblk;
       if (MODE == 1)
         dot_range_i8<N>(qs_tile, d_tile, b0, b1, lane, s.qx, s.dx, s.K, s.nblk, acc);
-      else if (MODE == 2)
-        dot_range_q4k<N, false>(qs_tile, d_tile, nullptr, b0, b1, lane, s.x, s.x_stride, acc);
-      else if (MODE == 4)
+      else if (MODE == 2) {
+        if constexpr (N > 4)
+          dot_range_q4k_ring<N, false, 2>(qs_tile, d_tile, nullptr, b0, b1, lane, s.x,
+                                              s.x_stride, acc);
+        else
+          dot_range_q4k<N, false>(qs_tile, d_tile, nullptr, b0, b1, lane, s.x, s.x_stride, acc);
+      } else if (MODE == 4) {
         // Q5_K: 4 bytes of fifth bits per sub-block and row
-        dot_range_q4k<N, true>(qs_tile, d_tile, s.qh + (int64_t)t * kTile * (s.K / 8), b0, b1,
-                               lane, s.x, s.x_stride, acc);
-      else if (MODE == 3)
+        if constexpr (N > 4)
+          dot_range_q4k_ring<N, true, 2>(qs_tile, d_tile,
+                                             s.qh + (int64_t)t * kTile * (s.K / 8), b0, b1, lane,
+                                             s.x, s.x_stride, acc);
+        else
+          dot_range_q4k<N, true>(qs_tile, d_tile, s.qh + (int64_t)t * kTile * (s.K / 8), b0, b1,
+                                 lane, s.x, s.x_stride, acc);
+      } else if (MODE == 3) {
         // Q6_K: 8 bytes of high fields per sub-block and row, 16 bytes of
         // scales and d per quad and row
-        dot_range_q6k<N>(qs_tile, s.qh + (int64_t)t * kTile * (s.K / 4),
-                         s.d + (int64_t)t * s.G * 1024, b0, b1, lane, s.x, s.x_stride, acc);
+        if constexpr (N > 4)
+          dot_range_q6k_ring<N, 2>(qs_tile, s.qh + (int64_t)t * kTile * (s.K / 4),
+                                       s.d + (int64_t)t * s.G * 1024, b0, b1, lane, s.x,
+                                       s.x_stride, acc);
+        else
+          dot_range_q6k<N>(qs_tile, s.qh + (int64_t)t * kTile * (s.K / 4),
+                           s.d + (int64_t)t * s.G * 1024, b0, b1, lane, s.x, s.x_stride, acc);
+      }
       else
         dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
                      s.gqa_off, acc);

@@ -40,8 +40,9 @@ enum : int32_t { F_RMSNORM = 1, F_RESIDUAL = 2, F_SWIGLU = 4, F_ARGMAX = 8, F_PA
 // Q5_K's fifth bits in qh); Q6_K (qs = low nibbles, qh = 2-bit fields, d =
 // scales and d).
 enum : int32_t { FMT_Q8_0 = 0, FMT_Q4K = 1, FMT_Q6K = 2, FMT_Q5K = 3 };
-// Columns per Q4_K / Q6_K launch (more would spill registers; callers split N).
-constexpr int kMaxQ4kN = 4;
+// Columns per K-quant launch (all of them: N > 4 uses a ring of sub-block
+// buffers whose registers fit every N).
+constexpr int kMaxQ4kN = 8;
 // How a segment's partial sum is weighted in the fold.
 enum : int32_t { A_ONE = 0, A_PTR = 1, A_SIGMOID = 2 };
 

@@ -263,7 +263,7 @@ int q4k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* meta, v
 /* y[n][r] = sum_k w[r][k] * x[n][k] with Q4_K weights, x fp32 [N][K] and y
  * fp32 [N][M] (device, 4-byte aligned), 1 <= N <= Q8_MAX_N, K % 256 == 0.
  * Each sub-block adds d s_j * sum_k q_k x_k - dmin m_j * sum_k x_k in fp32.
- * Columns are processed 4 per launch (N > 4 reads the weights twice).
+ * All N columns run in one launch (the weights are read once).
  * Workspace: q8_0_workspace_bytes(Q8_OP_Q4K_GEMV, M, K, N, 0, 0, 0) bytes
  * (device; NULL when 0), as for q8_0_gemv.  Errors as q8_0_gemv. */
 int q4k_gemv(const q4k_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
@@ -308,7 +308,7 @@ int q5k_repack(const void* blocks, int64_t M, int64_t K, void* qs, void* qh, voi
 /* y[n][r] = sum_k w[r][k] * x[n][k] with Q5_K weights; x, y, N, K and the
  * workspace (op Q8_OP_Q5K_GEMV) as q4k_gemv.  Each sub-block adds
  * d s_j * sum_k code_k x_k - dmin m_j * sum_k x_k in fp32 (code = low + 16
- * fifth); columns run 4 per launch.  Errors as q8_0_gemv. */
+ * fifth); all columns run in one launch.  Errors as q8_0_gemv. */
 int q5k_gemv(const q5k_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
              void* workspace, size_t workspace_bytes, void* stream);
 
@@ -354,7 +354,7 @@ int q6k_repack(const void* blocks, int64_t M, int64_t K, void* ql, void* qh, voi
 
 /* y[n][r] = sum_k w[r][k] * x[n][k] with Q6_K weights; x, y, N, K and the
  * workspace (op Q8_OP_Q6K_GEMV) as q4k_gemv.  Each 16-weight group adds
- * d s * (sum(code x) - 32 sum(x)) in fp32; columns run 4 per launch.
+ * d s * (sum(code x) - 32 sum(x)) in fp32; all columns run in one launch.
  * Errors as q8_0_gemv. */
 int q6k_gemv(const q6k_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
              void* workspace, size_t workspace_bytes, void* stream);
