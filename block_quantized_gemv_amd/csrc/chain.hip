@@ -283,30 +283,39 @@ __device__ __forceinline__ float row_sum(float v) {
 // Wait (bounded) until entries [0, n) of the tagged record at byte offset off
 // carry the current step; put(k, value) for each, then return the sum of
 // squares accumulated in a fixed order.  Poll lanes (pl < kPL) only; n even.
-template <typename Put>
-__device__ __forceinline__ float poll_tagged(__amdgpu_buffer_rsrc_t rs, int64_t off, int n,
-                                             uint32_t step, int pl, uint32_t* status, Put put) {
+// Each lane owns NSL 16-byte slots (the last one repeated when it owns
+// fewer) and loads all of them every round, unconditionally: a load under a
+// lane-dependent branch would make the compiler wait for every earlier load
+// before issuing it (the register may still be the target of the previous
+// round's load), turning one round into NSL serial memory round trips.
+template <int NSL, typename Put>
+__device__ __forceinline__ float poll_tagged_n(__amdgpu_buffer_rsrc_t rs, int64_t off, int n,
+                                               uint32_t step, int pl, uint32_t* status, Put put) {
   // recompute the per-lane offsets here rather than keep them live (and
   // spilled) across the whole step
   __asm__ volatile("" : "+v"(pl));
   const int nsl = n >> 1;
   uint32_t todo = 0;
+  int own = 0;
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j)
-    if (pl + kPL * j < nsl) todo |= 1u << j;
+  for (int j = 0; j < NSL; ++j)
+    if (pl + kPL * j < nsl) {
+      todo |= 1u << j;
+      own = j;
+    }
   const uint32_t all = todo;
-  u32x4 v[kSlots];
+  u32x4 v[NSL];
   int spins = 0;
   int base = (int)(off + (int64_t)pl * 16);
   while (todo) {
     // an opaque offset each round, so the loads are issued again
     __asm__ volatile("" : "+v"(base));
 #pragma unroll
-    for (int j = 0; j < kSlots; ++j)
-      if ((todo >> j) & 1u)
-        v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + kPL * 16 * j, 0, kPollAux);
+    for (int j = 0; j < NSL; ++j)
+      v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + kPL * 16 * (j < own ? j : own), 0,
+                                                   kPollAux);
 #pragma unroll
-    for (int j = 0; j < kSlots; ++j)
+    for (int j = 0; j < NSL; ++j)
       if (((todo >> j) & 1u) && (v[j].x ^ v[j].y) == step && (v[j].z ^ v[j].w) == step)
         todo &= ~(1u << j);
     if (todo && ++spins > kSpinMax) {
@@ -316,7 +325,7 @@ __device__ __forceinline__ float poll_tagged(__amdgpu_buffer_rsrc_t rs, int64_t 
   }
   float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
+  for (int j = 0; j < NSL; ++j) {
     if ((all >> j) & 1u) {
       const int k = 2 * (pl + kPL * j);
       const float a = __uint_as_float(v[j].x), b = __uint_as_float(v[j].z);
@@ -327,6 +336,21 @@ __device__ __forceinline__ float poll_tagged(__amdgpu_buffer_rsrc_t rs, int64_t 
     }
   }
   return ss;
+}
+
+template <typename Put>
+__device__ __forceinline__ float poll_tagged(__amdgpu_buffer_rsrc_t rs, int64_t off, int n,
+                                             uint32_t step, int pl, uint32_t* status, Put put) {
+  const int nsl = (n >> 1) > 0 ? (n >> 1) : 1;
+  switch ((nsl + kPL - 1) / kPL) {
+    case 1: return poll_tagged_n<1>(rs, off, n, step, pl, status, put);
+    case 2: return poll_tagged_n<2>(rs, off, n, step, pl, status, put);
+    case 3: return poll_tagged_n<3>(rs, off, n, step, pl, status, put);
+    case 4: return poll_tagged_n<4>(rs, off, n, step, pl, status, put);
+    case 5: return poll_tagged_n<5>(rs, off, n, step, pl, status, put);
+    case 6: return poll_tagged_n<6>(rs, off, n, step, pl, status, put);
+    default: return poll_tagged_n<kSlots>(rs, off, n, step, pl, status, put);
+  }
 }
 
 // 1 / sqrt(mean of squares + eps) from the poll waves' partial sums, added in
