@@ -31,6 +31,7 @@ Q8_OP_Q6K_GEMV = 8
 Q8_OP_Q5K_GEMV = 9
 
 Q8_LAYOUT_ROWS, Q8_LAYOUT_GATE_UP_PAIRS = 0, 1
+Q8_CHAIN_COHERENT = 1
 Q8_CHAIN_QKV, Q8_CHAIN_H_ATTN, Q8_CHAIN_SWIGLU, Q8_CHAIN_H_OUT = 0, 1, 2, 3
 
 EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv", "q8_0_gemv_fused",
@@ -79,11 +80,14 @@ class q8_0_chain_plan(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("intermediate", ctypes.c_int32), ("vocab", ctypes.c_int32),
-                ("eps", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("flags", ctypes.c_uint32),
                 ("ws_bytes", ctypes.c_int64), ("off", ctypes.c_int64 * 4),
                 ("layer_stride", ctypes.c_int64), ("am_off", ctypes.c_int64),
                 ("lm_qs", ctypes.c_void_p), ("lm_d", ctypes.c_void_p),
-                ("len", ctypes.c_int32 * 4)]
+                ("len", ctypes.c_int32 * 4), ("spin_limit", ctypes.c_uint32),
+                ("groups", ctypes.c_int32), ("off_v", ctypes.c_int64),
+                ("off_p", ctypes.c_int64), ("group_words_v", ctypes.c_int32),
+                ("group_words_h", ctypes.c_int32)]
 
 
 _lib = None
@@ -150,6 +154,22 @@ def _check(fn: str, rc: int) -> None:
 def _stream(stream=None) -> int:
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+def _ncols(x: torch.Tensor, K: int, name: str = "x") -> int:
+    """Columns N of an activation tensor holding N vectors of K entries ([K]
+    or [N, K]); raises ValueError before anything reaches the library."""
+    N = 1 if x.dim() == 1 else x.shape[0]
+    if x.dim() > 2 or x.numel() != N * K:
+        raise ValueError(f"{name} has shape {tuple(x.shape)}; expected [{K}] or [N, {K}]")
+    if not 1 <= N <= Q8_MAX_N:
+        raise ValueError(f"{name} has {N} columns; 1..{Q8_MAX_N} are supported")
+    return N
+
+
+def _room(t: torch.Tensor, n: int, name: str) -> None:
+    if t.numel() < n:
+        raise ValueError(f"{name} has {t.numel()} entries; the call writes {n}")
 
 
 def _need(t: torch.Tensor, dtype, name: str) -> None:
@@ -249,8 +269,10 @@ def q4k_packed_size(M: int, K: int) -> tuple[int, int]:
 def q4k_gemv(W: PackedQ4K, x: torch.Tensor, y: torch.Tensor | None = None, workspace=None,
              stream=None) -> torch.Tensor:
     """y[N][M] = x[N][K] @ W^T for packed Q4_K weights W (x float32)."""
+    N = _ncols(x, W.K)
+    if y is not None:
+        _room(y, N * W.M, "y")
     _need(x, torch.float32, "x")
-    N = 1 if x.dim() == 1 else x.shape[0]
     if y is None:
         y = torch.empty((W.M,) if x.dim() == 1 else (N, W.M), dtype=torch.float32,
                         device=x.device)
@@ -298,8 +320,10 @@ def q5k_packed_size(M: int, K: int) -> tuple[int, int, int]:
 def q5k_gemv(W: PackedQ5K, x: torch.Tensor, y: torch.Tensor | None = None, workspace=None,
              stream=None) -> torch.Tensor:
     """y[N][M] = x[N][K] @ W^T for packed Q5_K weights W (x float32)."""
+    N = _ncols(x, W.K)
+    if y is not None:
+        _room(y, N * W.M, "y")
     _need(x, torch.float32, "x")
-    N = 1 if x.dim() == 1 else x.shape[0]
     if y is None:
         y = torch.empty((W.M,) if x.dim() == 1 else (N, W.M), dtype=torch.float32,
                         device=x.device)
@@ -347,8 +371,10 @@ def q6k_packed_size(M: int, K: int) -> tuple[int, int, int]:
 def q6k_gemv(W: PackedQ6K, x: torch.Tensor, y: torch.Tensor | None = None, workspace=None,
              stream=None) -> torch.Tensor:
     """y[N][M] = x[N][K] @ W^T for packed Q6_K weights W (x float32)."""
+    N = _ncols(x, W.K)
+    if y is not None:
+        _room(y, N * W.M, "y")
     _need(x, torch.float32, "x")
-    N = 1 if x.dim() == 1 else x.shape[0]
     if y is None:
         y = torch.empty((W.M,) if x.dim() == 1 else (N, W.M), dtype=torch.float32,
                         device=x.device)
@@ -401,6 +427,11 @@ class PackedQ8:
 
 def q8_0_repack(aos: torch.Tensor, M: int, K: int, qs: torch.Tensor, d: torch.Tensor,
                 stream=None, layout: int = Q8_LAYOUT_ROWS) -> None:
+    if aos.numel() != M * (K // 32) * 34:
+        raise ValueError(f"aos has {aos.numel()} bytes, expected {M * (K // 32) * 34}")
+    qb, db = q8_0_packed_size(M, K)
+    _room(qs, qb, "qs")
+    _room(d, db, "d")
     _need(aos, torch.uint8, "aos")
     if layout == Q8_LAYOUT_ROWS:
         rc = lib().q8_0_repack(aos.data_ptr(), M, K, qs.data_ptr(), d.data_ptr(), _stream(stream))
@@ -427,8 +458,10 @@ def _ws(ws, nbytes: int, device) -> tuple[int, int]:
 def q8_0_gemv(W: PackedQ8, x: torch.Tensor, y: torch.Tensor | None = None, workspace=None,
               stream=None) -> torch.Tensor:
     """y[N][M] = x[N][K] @ W^T for packed Q8_0 weights W (x float32)."""
+    N = _ncols(x, W.K)
+    if y is not None:
+        _room(y, N * W.M, "y")
     _need(x, torch.float32, "x")
-    N = 1 if x.dim() == 1 else x.shape[0]
     if y is None:
         y = torch.empty((W.M,) if x.dim() == 1 else (N, W.M), dtype=torch.float32,
                         device=x.device)
@@ -443,13 +476,33 @@ def make_fusion(prologue: int = Q8_PRO_NONE, epilogue: int = 0, eps: float = 0.0
                 n_heads: int = 0, n_kv_heads: int = 0, head_dim: int = 0, gqa_offset: int = 0,
                 residual: torch.Tensor | None = None,
                 argmax_out: torch.Tensor | None = None) -> q8_0_fusion:
-    return q8_0_fusion(prologue, epilogue, eps, n_heads, n_kv_heads, head_dim, gqa_offset,
-                       residual.data_ptr() if residual is not None else None,
-                       argmax_out.data_ptr() if argmax_out is not None else None)
+    f = q8_0_fusion(prologue, epilogue, eps, n_heads, n_kv_heads, head_dim, gqa_offset,
+                    residual.data_ptr() if residual is not None else None,
+                    argmax_out.data_ptr() if argmax_out is not None else None)
+    # sizes of the tensors behind the raw pointers, checked by q8_0_gemv_fused
+    f.residual_numel = residual.numel() if residual is not None else None
+    f.argmax_numel = argmax_out.numel() if argmax_out is not None else None
+    return f
 
 
 def q8_0_gemv_fused(W: PackedQ8, x: torch.Tensor, y: torch.Tensor, fusion: q8_0_fusion,
                     workspace=None, stream=None) -> torch.Tensor:
+    if fusion.prologue == Q8_PRO_GQA:
+        need = fusion.gqa_offset + fusion.n_kv_heads * fusion.head_dim
+        if fusion.n_heads * fusion.head_dim != W.K or x.numel() < need:
+            raise ValueError(f"GQA prologue reads x[{fusion.gqa_offset}:{need}] of a vector "
+                             f"of {x.numel()}, with n_heads*head_dim == K ({W.K})")
+    elif x.numel() != W.K:
+        raise ValueError(f"x has {x.numel()} entries, expected K = {W.K}")
+    _room(y, W.M // 2 if fusion.epilogue & Q8_EPI_SWIGLU else W.M, "y")
+    if fusion.epilogue & Q8_EPI_RESIDUAL and fusion.residual:
+        n = getattr(fusion, "residual_numel", None)
+        if n is not None and n < W.M:
+            raise ValueError(f"residual has {n} entries, expected {W.M}")
+    if fusion.epilogue & Q8_EPI_ARGMAX and fusion.argmax_out:
+        n = getattr(fusion, "argmax_numel", None)
+        if n is not None and n < 1:
+            raise ValueError("argmax_out needs one entry")
     _need(x, torch.float32, "x")
     _need(y, torch.float32, "y")
     wsp, wsb = _ws(workspace,
@@ -464,8 +517,12 @@ def q8_0_gemv_argmax(W: PackedQ8, x: torch.Tensor, y: torch.Tensor | None = None
                      argmax_out: torch.Tensor | None = None, workspace=None, stream=None):
     """y[N][M] = x[N][K] @ W^T and argmax_out[n] = lowest index of the largest
     y[n][*], one pick per column; returns (y, argmax_out)."""
+    N = _ncols(x, W.K)
+    if y is not None:
+        _room(y, N * W.M, "y")
+    if argmax_out is not None:
+        _room(argmax_out, N, "argmax_out")
     _need(x, torch.float32, "x")
-    N = 1 if x.dim() == 1 else x.shape[0]
     if y is None:
         y = torch.empty((W.M,) if x.dim() == 1 else (N, W.M), dtype=torch.float32,
                         device=x.device)
@@ -506,9 +563,13 @@ def q8_0_quantize_act(x: torch.Tensor, qx: torch.Tensor | None = None,
 def q8_0_gemv_q8act(W: PackedQ8, qx: torch.Tensor, dx: torch.Tensor,
                     y: torch.Tensor | None = None, workspace=None, stream=None) -> torch.Tensor:
     """y[N][M] from packed weights and integer activations (q8_0_quantize_act)."""
+    N = _ncols(qx, W.K, "qx")
+    if dx.numel() != N * (W.K // 32):
+        raise ValueError(f"dx has {dx.numel()} scales, expected {N * (W.K // 32)}")
+    if y is not None:
+        _room(y, N * W.M, "y")
     _need(qx, torch.int8, "qx")
     _need(dx, torch.int16, "dx")
-    N = qx.shape[0]
     if y is None:
         y = torch.empty((N, W.M), dtype=torch.float32, device=qx.device)
     _need(y, torch.float32, "y")
@@ -521,6 +582,8 @@ def q8_0_gemv_q8act(W: PackedQ8, qx: torch.Tensor, dx: torch.Tensor,
 
 def q8_0_argmax(v: torch.Tensor, out: torch.Tensor | None = None, workspace=None,
                 stream=None) -> torch.Tensor:
+    if out is not None:
+        _room(out, 1, "out")
     _need(v, torch.float32, "v")
     if out is None:
         out = torch.empty(1, dtype=torch.int32, device=v.device)
@@ -533,6 +596,10 @@ def q8_0_argmax(v: torch.Tensor, out: torch.Tensor | None = None, workspace=None
 
 def q8_0_route_topk(logits: torch.Tensor, k: int, expert_ids: torch.Tensor | None = None,
                     slot_weights: torch.Tensor | None = None, stream=None):
+    if expert_ids is not None:
+        _room(expert_ids, k, "expert_ids")
+    if slot_weights is not None:
+        _room(slot_weights, k, "slot_weights")
     _need(logits, torch.float32, "logits")
     if expert_ids is None:
         expert_ids = torch.empty(k, dtype=torch.int32, device=logits.device)
@@ -552,11 +619,28 @@ def q8_0_moe_gemv(W_experts: PackedQ8, expert_ids: torch.Tensor, slot_weights, x
                   stream=None) -> torch.Tensor:
     """All routed-expert slots (and the shared expert) in one launch; see
     q8_0_moe_gemv in include/q8gemv.h for the modes."""
+    S = expert_ids.numel()
+    base = mode & ~Q8_MOE_SWIGLU
+    half = 2 if mode & Q8_MOE_SWIGLU else 1
+    if base == Q8_MOE_SCATTER:
+        if x.numel() != W_experts.K or (shared is not None and shared.K != W_experts.K):
+            raise ValueError(f"scatter reads one x of K = {W_experts.K} entries "
+                             f"(x has {x.numel()})")
+        _room(y, S * W_experts.M // half + (shared.M // half if shared is not None else 0), "y")
+    else:
+        want = S * W_experts.K + (shared.K if shared is not None else 0)
+        if x.numel() != want:
+            raise ValueError(f"combine reads x of {want} entries (x has {x.numel()})")
+        _room(y, W_experts.M, "y")
+        if slot_weights is not None:
+            _room(slot_weights, S, "slot_weights")
+        if shared is not None and shared_gate is not None:
+            _room(shared_gate, 1, "shared_gate")
+    if dev_status is not None:
+        _room(dev_status, 1, "dev_status")
     _need(expert_ids, torch.int32, "expert_ids")
     _need(x, torch.float32, "x")
     _need(y, torch.float32, "y")
-    S = expert_ids.numel()
-    base = mode & ~Q8_MOE_SWIGLU
     if shared is not None:
         M2, K2 = shared.M, shared.K
     else:
@@ -578,6 +662,10 @@ def q8_0_moe_gemv(W_experts: PackedQ8, expert_ids: torch.Tensor, slot_weights, x
 # ---------------------------------------------------------------------------
 # Persistent decode chain: one launch per decode step
 # ---------------------------------------------------------------------------
+class ChainStepError(RuntimeError):
+    """A persistent decode step whose outputs are invalid (next_token == -1)."""
+
+
 class PersistentChain:
     """A whole decode step (n_layers Qwen2-style layers + LM head + argmax) in
     one kernel launch; see q8_0_chain_prepare in include/q8gemv.h.  `layers`
@@ -609,8 +697,22 @@ class PersistentChain:
 
     def run(self, h_in: torch.Tensor, logits: torch.Tensor | None = None,
             next_token: torch.Tensor | None = None, h_out: torch.Tensor | None = None,
-            stream=None) -> None:
+            stream=None, check: bool = False) -> None:
+        """One decode step.  With check=True the call waits for the step and
+        raises ChainStepError if it was marked invalid (next_token == -1: a
+        wait for another workgroup's data expired)."""
         _need(h_in, torch.float32, "h_in")
+        if h_in.numel() != self.hidden:
+            raise ValueError(f"h_in has {h_in.numel()} entries, expected {self.hidden}")
+        if h_out is not None and h_out.numel() != self.hidden:
+            raise ValueError(f"h_out has {h_out.numel()} entries, expected {self.hidden}")
+        if self.vocab:
+            if logits is None or next_token is None:
+                raise ValueError("a chain with an LM head needs logits and next_token")
+            if logits.numel() < self.vocab or next_token.numel() < 1:
+                raise ValueError("logits needs vocab entries and next_token one")
+        if check and next_token is None:
+            raise ValueError("check=True needs next_token")
         for t, name, dt in ((logits, "logits", torch.float32),
                             (next_token, "next_token", torch.int32),
                             (h_out, "h_out", torch.float32)):
@@ -620,6 +722,12 @@ class PersistentChain:
         _check("q8_0_chain_run",
                lib().q8_0_chain_run(ctypes.byref(self.plan), self.ws.data_ptr(), h_in.data_ptr(),
                                     ptr(h_out), ptr(logits), ptr(next_token), _stream(stream)))
+        if check:
+            s = stream if stream is not None else torch.cuda.current_stream()
+            s.synchronize()
+            if int(next_token.cpu()[0]) == -1:
+                raise ChainStepError(f"decode step invalid: a wait expired "
+                                     f"(status {self.status(stream)})")
 
     def read(self, layer: int, which: int, stream=None) -> torch.Tensor:
         out = torch.empty(self.plan.len[which], dtype=torch.float32, device=self.ws.device)

@@ -7,40 +7,62 @@
 // hand-off latency rather than bandwidth (the pages' graph and slot-fusion
 // results: a per-layer task graph of fixed launches; capturing it gains about
 // a third, fusing slots cuts launches).  Here one workgroup per compute unit
-// stays resident for the whole step; only the activations between projections
-// are dependent, so each workgroup streams the next projection's weights into
-// registers while it waits for the current one's inputs.
+// stays resident for the whole step and streams each projection's weights
+// into registers well before its input arrives.
 //
-// Hand-off between workgroups.  Every activation vector of the step has its
-// own buffer in the workspace (no reuse within a step, so no write-after-read
-// hazards).  Each entry is one 8-byte word: the fp32 bits and, in the upper
-// half, those bits XOR the step number.  A consumer polls the words it needs
-// with device-coherent 16-byte loads until every word decodes to the current
-// step: the data itself is the signal, so there are no flags, fences or
-// barriers between workgroups, and a read that raced a write can never be
-// taken for current data (a torn word fails the XOR check).  The step number
-// lives in the workspace; the last workgroup to finish advances it.
+// The MI355X has 8 XCDs of 32 compute units, each XCD with its own L2.  A
+// hand-off inside one XCD goes through that L2: a plain store, then a load
+// that skips the compute unit's L1 (device-scope policy), about 0.23 us per
+// hop.  Between XCDs the store must be written through to memory (device
+// scope as well), about 0.45 us per hop, and when every workgroup reads the
+// same few lines the memory side serialises them.  So the step is organised
+// so that each layer needs one exchange across XCDs, with 8 readers per line,
+// and four inside an XCD (workgroup b runs on XCD b % 8 and belongs to group
+// x = b % 8 as member j = b / 8; the kernel checks its XCD on entry):
 //
-// Work split.  A layer projection is cut into items of 4 output rows (gate
-// and up pairs: 2 gate + the 2 matching up rows) over the full K, spread
-// round-robin over the workgroups, so no K-split partials cross workgroups.
-// Inside a workgroup a wave task is (item, 16 consecutive 16-weight chunks):
-// lane 4m + r holds the 16 quants of row r in chunk m of the task and its
-// scale, so the four lanes of a chunk read the item's 64 contiguous packed
-// bytes of that chunk (16 cache lines per load instruction, not 64) and share
-// one broadcast 16-float slice of the input from LDS (laid out with 4 floats
-// of padding after every 16, so the 16 slices a wave reads fall in distinct
-// banks).  The 16 lanes of a row are summed by DPP/permlane rotations, and
-// the tasks of one item are added in task order by whichever of them
-// finishes last, which also runs the epilogue (RMS scale, residual, SwiGLU,
-// tagged store).  Small tasks spread even the smallest projections over many
-// waves.  Each weight wave keeps its first kPre tasks of the next projection
-// with work for it in registers.  Waves 0-5 poll the inputs into LDS; waves
-// 6-15 hold the weights.  The LM head is streamed: one 64-row tile per wave,
-// lane = row, input broadcast from LDS.
+//   A  v = Wv rmsnorm(h)      every XCD computes all value rows (its members
+//                             split them), exchanged inside the XCD;
+//                             the query/key rows, which nothing downstream
+//                             reads at position 0, are computed once over
+//                             the whole grid
+//   B  h1 = h + Wo gqa(v)     every XCD computes all of h1 (wo is read by
+//                             each XCD), exchanged inside the XCD
+//   C  s = swiglu(Wgu rmsnorm(h1)) XCD x computes its own slice of s,
+//                             exchanged inside the XCD
+//   D  P_x = Wdown[:, slice x] s[slice x]  (a split of down's K over XCDs)
+//                             sent across XCDs: member j of every XCD reads
+//                             the rows it owns from all 8 partials
+//   E  h2 = h1 + sum_x P_x    (x ascending), member j's rows, exchanged
+//                             inside the XCD as the next layer's h
 //
-// Every spin is bounded; on expiry bit 1 of the status word is set and the
-// kernel runs to completion with whatever it read.
+// Hand-off records.  Every activation vector of the step has its own record
+// in the workspace (no reuse within a step).  Each entry is one 8-byte word:
+// the fp32 bits and, in the upper half, those bits XOR the step number.  A
+// consumer polls the words it needs until every word decodes to the current
+// step: the data itself is the signal, so there are no flags or fences
+// between workgroups, and a read that raced a write can never be taken for
+// current data (a torn word fails the check).  The step number lives in the
+// workspace; the last workgroup to finish advances it.
+//
+// Inside a workgroup, waves 0-3 poll: they wait for the next stage's input
+// and stage it in LDS while waves 4-15 compute the current stage.  A task is
+// 4 output rows over a K range of at most 1024 (4 rounds of 16 chunks of 16
+// weights): lane 4m + r holds row r's chunks 16k + m, so a task ends with
+// whole dot products after a reduction over the 16 lanes of each row.  A
+// weight wave owns at most one task per stage, in one of three register
+// slots, and reloads a slot with the next layer's weights at the start of the
+// stage after its use, so every load has a whole layer to arrive and the
+// bursts overlap compute rather than the latency-critical polls.
+//
+// Every wait is bounded.  An expired wait sets bit 1 of the step's error
+// word; the step then writes next_token = -1, the bit is added to the sticky
+// status word, and the kernel runs to completion.  The hand-offs inside an
+// XCD need every member of a group on one XCD (which one does not matter);
+// q8_0_chain_prepare checks that with a probe launch of the same shape and
+// otherwise sets Q8_CHAIN_COHERENT (every store device-scope).  A member that
+// still lands elsewhere cannot make a consumer take wrong data (each word
+// carries its step); at worst its hand-offs wait until its L2 writes the line
+// back, or the wait expires.
 #include <math.h>
 #include <string.h>
 
@@ -52,23 +74,20 @@
 namespace q8 {
 namespace {
 
-constexpr int kCT = 1024;       // threads per workgroup
-constexpr int kCW = kCT / 64;   // waves per workgroup
-constexpr int kPW = 6;          // poll/epilogue waves
-constexpr int kPL = 64 * kPW;   // poll lanes
-constexpr int kXW = kCW - kPW;  // waves holding prefetched weights
-constexpr int kSlots = 7;       // 16-byte poll slots per poll lane
-constexpr int kMaxIn = 2 * kPL * kSlots;  // longest polled vector (5376 entries)
-constexpr int kMaxTasks = 1024; // wave tasks of one workgroup in one projection
-constexpr int kRounds = 4;      // rounds of 16 chunks (4 lanes each) per wave task
-constexpr int kTaskChunks = 16 * kRounds;  // 16-weight chunks per wave task
-constexpr int kPre = 1;         // tasks of the next projection a wave holds in registers
-constexpr int kSpinMax = 1 << 18;
-// Cache policy of the polling loads: sc1 (device scope: coherent across the
-// XCDs' separate L2s).
-constexpr int kPollAux = 16;
-constexpr int kHdrBytes = 256;
+constexpr int kCT = 1024;          // threads per workgroup
+constexpr int kCW = kCT / 64;      // waves per workgroup
+constexpr int kPW = 4;             // poll waves
+constexpr int kPL = 64 * kPW;      // poll lanes
+constexpr int kXW = kCW - kPW;     // weight waves
+constexpr int kRounds = 4;         // rounds of 16 chunks per task
+constexpr int kTaskChunks = 16 * kRounds;
+constexpr int kMaxK = 16 * kTaskChunks;  // longest K a task covers (1024)
+constexpr int kNX = 8;             // XCD groups
 constexpr int kMaxGrid = 1024;
+constexpr int kHdrBytes = 256;
+constexpr uint32_t kDefaultSpin = 1u << 16;
+constexpr int kAuxDev = 16;        // cache policy sc1: device scope
+constexpr int kMaxTw = 12;         // wo/down tasks of one workgroup (<= kXW)
 
 enum { ST_QKV = 0, ST_WO = 1, ST_GU = 2, ST_DN = 3 };
 
@@ -79,21 +98,23 @@ struct ChainMat {
 
 // Kernel arguments: everything the step needs except the per-layer weight
 // table, which lives in the workspace after the 256-byte header (ChainMat
-// [L][4]: qkv, wo, gate_up, down) and is copied to LDS at the start.  Kernel
-// arguments sit in constant memory, so reading them never waits on the
-// wave's outstanding vector memory traffic.
+// [L][4]: qkv, wo, gate_up, down) and is copied to LDS at the start.
 struct ChainArgs {
   uint8_t* ws;
   const float* h_in;
   float* h_out;
   float* logits;
   int32_t* next_token;
-  int32_t L, H, NH, NKV, HD, I, V, G;
-  int32_t Mq;
+  int32_t L, H, NH, NKV, HD, I, V;
+  int32_t G, GS;          // grid, members per XCD group (G = kNX * GS)
+  int32_t Mq, KV, NHD;    // qkv rows, value rows, attention width
   float eps;
-  int64_t off_qkv, off_h1, off_s, off_h2;  // byte offsets of layer 0's records
-  int64_t layer_stride;  // bytes between layers' record sets
-  int64_t am_off;        // argmax partials: [kMaxGrid] (fp32 value, int32 index)
+  uint32_t flags;         // Q8_CHAIN_COHERENT
+  uint32_t spin;          // polling rounds before a wait gives up
+  int64_t o_qkv, o_v, o_h1, o_s, o_p, o_h2;  // byte offsets of layer 0's records
+  int32_t gv, gh;         // words between the group copies of v- / h-sized records
+  int64_t layer_stride;   // bytes between layers' record sets
+  int64_t am_off;         // argmax partials: [kMaxGrid] (fp32 value, int32 index)
   int64_t ws_bytes;
   ChainMat lm;
 };
@@ -103,20 +124,23 @@ struct Hdr {  // first 256 bytes of the workspace
   uint32_t pad0[15];
   uint32_t ticket;
   uint32_t pad1[15];
-  uint32_t status;
-  uint32_t pad2[31];
+  uint32_t status;  // sticky: every error bit of every run since prepare
+  uint32_t pad2[15];
+  uint32_t err;     // error bits of the current step (cleared at its end)
+  uint32_t pad3[15];
 };
+
+__device__ __forceinline__ unsigned xcc_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 15u;
+}
 
 __device__ __forceinline__ float q_at(uint32_t w, int k) {
   return (float)(int32_t)(int8_t)(w >> (8 * k));
 }
 __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
 }
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 #pragma unroll
@@ -130,11 +154,6 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
-__device__ __forceinline__ void st_tag(uint64_t* p, float v, uint32_t step) {
-  const uint32_t b = __float_as_uint(v);
-  st_dev(p, (uint64_t)b | ((uint64_t)(b ^ step) << 32));
-}
-
 // Weight pointers come from a table in memory, so the compiler cannot prove
 // they are global; flat loads would also count against lgkmcnt and make every
 // LDS wait (and so every barrier) wait for the prefetched weights.
@@ -144,88 +163,66 @@ __device__ __forceinline__ T ld_w(const void* p) {
       reinterpret_cast<uintptr_t>(p)));
 }
 
-// Per-kind constants of one workgroup's share of a projection, computed once
-// per launch (integer divisions kept off the per-stage path).
-struct KindInfo {
-  int K, C, tpi, ntask;
-  int tpi_mul;  // ceil(2^20 / tpi): tau / tpi == (tau * tpi_mul) >> 20 for tau < 1024
-};
-
-__device__ __forceinline__ KindInfo kind_info(const ChainArgs& P, int kind, int vwg) {
-  int M, K;
-  switch (kind) {
-    case ST_QKV: M = P.Mq; K = P.H; break;
-    case ST_WO: M = P.H; K = P.NH * P.HD; break;
-    case ST_GU: M = 2 * P.I; K = P.H; break;
-    default: M = P.H; K = P.I; break;
-  }
-  KindInfo ki;
-  ki.K = K;
-  ki.C = K >> 4;
-  ki.tpi = (ki.C + kTaskChunks - 1) / kTaskChunks;
-  const int n_items = M >> 2;
-  const int n_it = n_items > vwg ? (n_items - 1 - vwg) / P.G + 1 : 0;
-  ki.ntask = n_it * ki.tpi;
-  ki.tpi_mul = ((1 << 20) + ki.tpi - 1) / ki.tpi;
-  return ki;
+// One tagged word: the fp32 bits, and those bits XOR the step.  AUX is the
+// cache policy of the store: 0 inside an XCD (the L2 is shared), kAuxDev
+// across XCDs (written through to memory).
+template <int AUX>
+__device__ __forceinline__ void st_tag(__amdgpu_buffer_rsrc_t rs, int64_t off, float v,
+                                       uint32_t step) {
+  const uint32_t b = __float_as_uint(v);
+  const u32x2 w = {b, b ^ step};
+  __builtin_amdgcn_raw_buffer_store_b64(w, rs, (int)off, 0, AUX);
 }
-
-// One projection of the step as seen by one workgroup.
-struct Stage {
-  ChainMat W;
-  int kind, layer;
-  int K, C, tpi, ntask, tpi_mul;
-  bool pairs;
-};
-
-__device__ __forceinline__ Stage stage_of(const KindInfo* ki, const ChainMat* wt, int s) {
-  Stage st;
-  st.layer = s >> 2;
-  st.kind = s & 3;
-  st.W = wt[s];
-  st.pairs = st.kind == ST_GU;
-  const KindInfo k = ki[st.kind];
-  st.K = k.K;
-  st.C = k.C;
-  st.tpi = k.tpi;
-  st.ntask = k.ntask;
-  st.tpi_mul = k.tpi_mul;
-  return st;
+__device__ __forceinline__ void st_tag_local(__amdgpu_buffer_rsrc_t rs, int64_t off, float v,
+                                             uint32_t step, bool coherent) {
+  if (coherent)
+    st_tag<kAuxDev>(rs, off, v, step);
+  else
+    st_tag<0>(rs, off, v, step);
 }
-
-// item (within this workgroup) and chunk block of wave task tau
-__device__ __forceinline__ int task_item(const Stage& st, int tau) {
-  return (tau * st.tpi_mul) >> 20;
-}
-
-// Packed-tile position of row r (0..3) of item j (0..15) of a tile.
-__device__ __forceinline__ int item_pos(bool pairs, int j, int r) {
-  return pairs ? (r < 2 ? 2 * j + r : 30 + 2 * j + r) : 4 * j + r;
-}
-
-// Chunk of this lane in round k of wave task tau (may be >= C: no work).
-__device__ __forceinline__ int task_chunk(const Stage& st, int tau, int k, int lane) {
-  return (tau - task_item(st, tau) * st.tpi) * kTaskChunks + 16 * k + (lane >> 2);
-}
-
-// The weights of one lane for one wave task: kRounds x (16 quants + scale).
-struct TaskRegs {
-  u32x4 q[kRounds];
-  uint32_t d[kRounds];
-};
 
 // LDS position of input entry k: 4 floats of padding after every 16, so the
 // 16 chunks that the lanes of a wave read at once fall in distinct banks.
 __device__ __forceinline__ int xpad(int k) { return k + ((k >> 4) << 2); }
 
-// The 16 quants of row (lane & 3) in chunk c of item `item`, and its scale.
-__device__ __forceinline__ void load_lane(const Stage& st, int item, int c, int lane, u32x4& q,
-                                          uint32_t& d) {
-  const int Gq = (st.K + 127) >> 7;
-  const int t = item >> 4;
-  const int p = item_pos(st.pairs, item & 15, lane & 3);
-  q = ld_w<u32x4>(st.W.qs + ((int64_t)t * st.C + c) * 1024 + p * 16);
-  d = ld_w<uint16_t>(st.W.d + ((int64_t)t * Gq + (c >> 3)) * 512 + p * 8 + ((c >> 1) & 3) * 2);
+// ---- tasks -----------------------------------------------------------------
+// Tile and position (within the 64-row packed tile) of row r of a task.
+struct RowPos {
+  int tile, pos;
+};
+// rows layout: item `it` is rows 4 it .. 4 it + 3
+__device__ __forceinline__ RowPos rows_item(int it, int r) { return {it >> 4, 4 * (it & 15) + r}; }
+// gate/up pairs layout: pair item p is gate rows 2p, 2p + 1 (positions
+// 2 (p % 16) + r) and the matching up rows (positions 32 + 2 (p % 16) + r - 2)
+__device__ __forceinline__ RowPos rows_pair(int p, int r) {
+  return {p >> 4, r < 2 ? 2 * (p & 15) + r : 30 + 2 * (p & 15) + r};
+}
+
+// A lane's share of one task: kRounds x (16 quants of its row in chunk
+// 16 k + lane / 4, and that chunk's binary16 scale).
+struct TaskW {
+  u32x4 q[kRounds];
+  uint32_t d[kRounds];
+};
+
+// Issue the loads of one task: chunks [c0, c0 + nc) of the row at rp of a
+// matrix whose rows are Kfull long.
+__device__ __forceinline__ void load_task(const ChainMat& W, int Kfull, int c0, int nc, RowPos rp,
+                                          int lane, TaskW& w) {
+  __asm__ volatile("" : "+v"(lane), "+v"(rp.tile), "+v"(rp.pos));
+  const int Cf = Kfull >> 4, Gq = (Kfull + 127) >> 7;
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    const int c = 16 * k + (lane >> 2);
+    w.q[k] = u32x4{0, 0, 0, 0};
+    w.d[k] = 0;
+    if (16 * k < nc && c < nc) {
+      const int cg = c0 + c;
+      w.q[k] = ld_w<u32x4>(W.qs + ((int64_t)rp.tile * Cf + cg) * 1024 + rp.pos * 16);
+      w.d[k] = ld_w<uint16_t>(W.d + ((int64_t)rp.tile * Gq + (cg >> 3)) * 512 + rp.pos * 8 +
+                              ((cg >> 1) & 3) * 2);
+    }
+  }
 }
 
 // d * sum_k q[k] * x[xo + k]
@@ -261,7 +258,7 @@ __device__ __forceinline__ float sum_rows(float v) {
   __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c), "+v"(d));
   return c + d;
 }
-// Sum over all 64 lanes (lane 0's value is used).
+// Sum over all 64 lanes (every lane gets the same bits).
 __device__ __forceinline__ float wave_sum_dpp(float v) {
   v += dpp_f<0x121>(v);  // row_ror:1
   v += dpp_f<0x122>(v);  // row_ror:2
@@ -269,88 +266,94 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   v += dpp_f<0x128>(v);  // row_ror:8
   return sum_rows(v);
 }
-
 // Sum over the 16 lanes that hold the same row (lane & 3); every lane ends
-// with the sum for its row, in the same order in every lane.  Rotations
-// within 16-lane rows (DPP) and swaps of row pairs and wave halves
-// (v_permlane16/32_swap): VALU operations only, no LDS round trips.
+// with the sum for its row, in the same order in every lane.
 __device__ __forceinline__ float row_sum(float v) {
   v += dpp_f<0x124>(v);  // row_ror:4
   v += dpp_f<0x128>(v);  // row_ror:8
   return sum_rows(v);
 }
 
-// Wait (bounded) until entries [0, n) of the tagged record at byte offset off
-// carry the current step; put(k, value) for each, then return the sum of
-// squares accumulated in a fixed order.  Poll lanes (pl < kPL) only; n even.
-// Each lane owns NSL 16-byte slots (the last one repeated when it owns
-// fewer) and loads all of them every round, unconditionally: a load under a
-// lane-dependent branch would make the compiler wait for every earlier load
-// before issuing it (the register may still be the target of the previous
-// round's load), turning one round into NSL serial memory round trips.
-template <int NSL, typename Put>
-__device__ __forceinline__ float poll_tagged_n(__amdgpu_buffer_rsrc_t rs, int64_t off, int n,
-                                               uint32_t step, int pl, uint32_t* status, Put put) {
-  // recompute the per-lane offsets here rather than keep them live (and
-  // spilled) across the whole step
+// The 4 row sums of one task (lane r < 4 holds row r), over nc chunks of the
+// input staged in LDS (padded layout, chunk c at 20 c).
+__device__ __forceinline__ float task_dot(const TaskW& w, int nc, const float* xs, int lane) {
+  float v = 0.f;
+#pragma unroll
+  for (int k = 0; k < kRounds; ++k) {
+    if (16 * k < nc) {
+      const int c = 16 * k + (lane >> 2);
+      const float t = lane_dot(w.q[k], w.d[k], xs, 20 * (c < nc ? c : 0));
+      v += c < nc ? t : 0.f;
+    }
+  }
+  return row_sum(v);
+}
+
+// ---- polling ----------------------------------------------------------------
+// Wait (bounded) until slots [0, nslots) of a record carry the current step.
+// Slot sl (16 bytes, two entries) lives at byte offset addr(sl); lane pl of
+// `stride` polling lanes owns slots pl + stride * q (q < NSL) and loads all
+// of them every round, unconditionally: a load under a lane-dependent branch
+// makes the compiler wait for every earlier load before issuing it (the
+// register may still be the target of the previous round's load), which
+// turns one round into NSL serial memory round trips.  put(sl, a, b) receives
+// each owned slot's two values.  On expiry the lane sets bit 1 of the status
+// word and `failed`, and later polls of that lane return at once.
+template <int NSL, typename Addr, typename Put>
+__device__ __forceinline__ void poll_rec(__amdgpu_buffer_rsrc_t rs, int nslots, int stride,
+                                         uint32_t step, int pl, uint32_t spin, bool& failed,
+                                         uint32_t* status, Addr addr, Put put) {
+  // recompute the per-lane offsets at each poll rather than let the compiler
+  // keep them live (and spilled) across the whole step
   __asm__ volatile("" : "+v"(pl));
-  const int nsl = n >> 1;
   uint32_t todo = 0;
   int own = 0;
 #pragma unroll
-  for (int j = 0; j < NSL; ++j)
-    if (pl + kPL * j < nsl) {
-      todo |= 1u << j;
-      own = j;
+  for (int q = 0; q < NSL; ++q)
+    if (pl + stride * q < nslots) {
+      todo |= 1u << q;
+      own = q;
     }
   const uint32_t all = todo;
+  int off[NSL];
+#pragma unroll
+  for (int q = 0; q < NSL; ++q) off[q] = addr(pl + stride * (q < own ? q : own));
   u32x4 v[NSL];
-  int spins = 0;
-  int base = (int)(off + (int64_t)pl * 16);
+  uint32_t spins = 0;
+  if (failed) todo = 0;
   while (todo) {
-    // an opaque offset each round, so the loads are issued again
-    __asm__ volatile("" : "+v"(base));
 #pragma unroll
-    for (int j = 0; j < NSL; ++j)
-      v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + kPL * 16 * (j < own ? j : own), 0,
-                                                   kPollAux);
+    for (int q = 0; q < NSL; ++q) {
+      // an opaque offset each round, so the loads are issued again
+      __asm__ volatile("" : "+v"(off[q]));
+      v[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[q], 0, kAuxDev);
+    }
 #pragma unroll
-    for (int j = 0; j < NSL; ++j)
-      if (((todo >> j) & 1u) && (v[j].x ^ v[j].y) == step && (v[j].z ^ v[j].w) == step)
-        todo &= ~(1u << j);
-    if (todo && ++spins > kSpinMax) {
+    for (int q = 0; q < NSL; ++q)
+      if (((todo >> q) & 1u) && (v[q].x ^ v[q].y) == step && (v[q].z ^ v[q].w) == step)
+        todo &= ~(1u << q);
+    if (todo && ++spins > spin) {
       atomicOr(status, 2u);
+      failed = true;
       break;
     }
   }
-  float ss = 0.f;
+  if (failed) return;
 #pragma unroll
-  for (int j = 0; j < NSL; ++j) {
-    if ((all >> j) & 1u) {
-      const int k = 2 * (pl + kPL * j);
-      const float a = __uint_as_float(v[j].x), b = __uint_as_float(v[j].z);
-      put(k, a);
-      put(k + 1, b);
-      ss = fmaf(a, a, ss);
-      ss = fmaf(b, b, ss);
-    }
-  }
-  return ss;
+  for (int q = 0; q < NSL; ++q)
+    if ((all >> q) & 1u) put(pl + stride * q, __uint_as_float(v[q].x), __uint_as_float(v[q].z));
 }
 
-template <typename Put>
-__device__ __forceinline__ float poll_tagged(__amdgpu_buffer_rsrc_t rs, int64_t off, int n,
-                                             uint32_t step, int pl, uint32_t* status, Put put) {
-  const int nsl = (n >> 1) > 0 ? (n >> 1) : 1;
-  switch ((nsl + kPL - 1) / kPL) {
-    case 1: return poll_tagged_n<1>(rs, off, n, step, pl, status, put);
-    case 2: return poll_tagged_n<2>(rs, off, n, step, pl, status, put);
-    case 3: return poll_tagged_n<3>(rs, off, n, step, pl, status, put);
-    case 4: return poll_tagged_n<4>(rs, off, n, step, pl, status, put);
-    case 5: return poll_tagged_n<5>(rs, off, n, step, pl, status, put);
-    case 6: return poll_tagged_n<6>(rs, off, n, step, pl, status, put);
-    default: return poll_tagged_n<kSlots>(rs, off, n, step, pl, status, put);
-  }
+// The record poll of the staging waves (kPL lanes): at most 2 slots a lane
+// (records of at most 1024 entries).
+template <typename Addr, typename Put>
+__device__ __forceinline__ void poll_stage_rec(__amdgpu_buffer_rsrc_t rs, int nslots, uint32_t step,
+                                               int pl, uint32_t spin, bool& failed,
+                                               uint32_t* status, Addr addr, Put put) {
+  if (nslots <= kPL)
+    poll_rec<1>(rs, nslots, kPL, step, pl, spin, failed, status, addr, put);
+  else
+    poll_rec<2>(rs, nslots, kPL, step, pl, spin, failed, status, addr, put);
 }
 
 // 1 / sqrt(mean of squares + eps) from the poll waves' partial sums, added in
@@ -401,242 +404,258 @@ __device__ __forceinline__ float lm_tile_dot(const ChainMat& W, int K, int tile,
   return acc;
 }
 
+// [lo, hi): part i of n items split into `parts` contiguous near-equal parts
+__device__ __forceinline__ void span(int n, int parts, int i, int& lo, int& hi) {
+  lo = (int)((int64_t)n * i / parts);
+  hi = (int)((int64_t)n * (i + 1) / parts);
+}
+
 __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
-  __shared__ float s_ss[2][kPW];     // poll waves' sums of squares, by stage parity
-  __shared__ int s_cnt[kMaxTasks];   // per-item arrivals of wave tasks
-  __shared__ KindInfo s_ki[4];
+  __shared__ float s_ss[2][kPW];  // poll waves' sums of squares: [0] h (stage A), [1] h1 (stage C)
   __shared__ float s_cv[kCW];
   __shared__ int s_ci[kCW];
   __shared__ int s_last;
 
   uint8_t* const ws = P.ws;
   Hdr* hdr = reinterpret_cast<Hdr*>(ws);
-  const int G = P.G, L = P.L, H = P.H;
-  const int bid = blockIdx.x;
-  const int vwg = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int G = P.G, GS = P.GS, L = P.L, H = P.H;
+  const int b = blockIdx.x;
+  const int x = b % kNX, j = b / kNX;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const bool poller = wave < kPW;
   const int cw = wave - kPW;
   const int pl = threadIdx.x;  // poll lane (poll waves only)
-  const int NS = 4 * L;
+  const bool coherent = (P.flags & Q8_CHAIN_COHERENT) != 0;
+  uint32_t* const status = &hdr->err;
+  bool failed = false;
 
   uint32_t step = ld_dev(&hdr->step) + 1u;
   if (step == 0u) step = 1u;
 
-  // LDS: stage inputs and residual copies are double-buffered so that the
-  // poll waves can stage projection s+1 while the weight waves work on s
-  const int XS = P.I > H ? (P.I > P.NH * P.HD ? P.I : P.NH * P.HD)
-                        : (H > P.NH * P.HD ? H : P.NH * P.HD);
+  // ---- this workgroup's tasks ------------------------------------------------
+  int v0, v1, q0, q1, w0, w1, g0, g1, cs0, cs1;
+  span(P.KV / 4, GS, j, v0, v1);                       // value items of member j
+  span((P.Mq - P.KV) / 4, G, b, q0, q1);               // query/key items of workgroup b
+  span(H / 4, GS, j, w0, w1);                          // wo / down items of member j
+  span(P.I / 16, kNX, x, cs0, cs1);                    // s chunks of XCD x
+  span(8 * (cs1 - cs0), GS, j, g0, g1);                // gate/up pair items of member j
+  g0 += 8 * cs0;
+  g1 += 8 * cs0;
+  const int tv = v1 - v0, tq = q1 - q0, tw = w1 - w0, tc = g1 - g0;
+  // wave assignment: A and gate/up tasks from the top weight wave down,
+  // wo/down tasks from the bottom
+  const int ta = kXW - 1 - cw;                         // top-down index of this wave
+  const bool hasA = !poller && ta < tv + tq;
+  const bool hasB = !poller && cw < tw;
+  const bool hasC = !poller && ta < tc;
+  const bool hasD = hasB;
+  const int cslice = cs1 - cs0;                        // down's K chunks on this XCD
+
+  // LDS: stage inputs (A and C in xb0, B and D in xb1), the layer input h
+  // (residual of wo), this member's h1 rows (for E), E's partials, the table
+  const int XS = max(max(H, P.NHD), 16 * cslice);
   const int XSa = (xpad(XS) + 3) & ~3, Ha = (H + 3) & ~3;
-  float* const xsb = lds;                    // [2][XSa] inputs by stage parity
-  float* const hres = xsb + 2 * XSa;         // [2][Ha]: before attention, before MLP
-  float* const red = hres + 2 * Ha;          // [task][4] row partial sums
-  ChainMat* const wt = reinterpret_cast<ChainMat*>(red + kMaxTasks * 4);
+  float* const xb0 = lds;
+  float* const xb1 = xb0 + XSa;
+  float* const hres = xb1 + XSa;
+  float* const h1s = hres + Ha;             // [4 kMaxTw]
+  float* const pbuf = h1s + 4 * kMaxTw;     // [kNX][4 kMaxTw]
+  ChainMat* const wt = reinterpret_cast<ChainMat*>(pbuf + kNX * 4 * kMaxTw);
   {
     const ChainMat* wg = reinterpret_cast<const ChainMat*>(ws + kHdrBytes);
     for (int i = threadIdx.x; i < 4 * L; i += kCT) wt[i] = wg[i];
-    for (int i = threadIdx.x; i < kMaxTasks; i += kCT) s_cnt[i] = 0;
-    if (threadIdx.x < 4) s_ki[threadIdx.x] = kind_info(P, threadIdx.x, vwg);
   }
-  __syncthreads();
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       ws, 0, (int)(P.ws_bytes > 0x7fffffff ? 0x7fffffff : P.ws_bytes), 0x00020000);
-  auto rec = [&](int layer, int kind) -> int64_t {
-    const int64_t o = kind == ST_QKV ? P.off_qkv
-                      : kind == ST_WO  ? P.off_h1
-                      : kind == ST_GU  ? P.off_s
-                                       : P.off_h2;
-    return o + (int64_t)layer * P.layer_stride;
-  };
-  auto recp = [&](int layer, int kind) -> uint64_t* {
-    return reinterpret_cast<uint64_t*>(ws + rec(layer, kind));
-  };
+  auto lrec = [&](int64_t o0, int l) -> int64_t { return o0 + (int64_t)l * P.layer_stride; };
+  __syncthreads();
 
-  // ---- poll waves: stage the input of projection s (s == NS: LM head) ------
-  auto poll_stage = [&](int s) {
-    float* xs = xsb + (s & 1) * XSa;
-    const int kind = s & 3, l = s >> 2;
-    float ss = 0.f;
-    if (s == NS || kind == ST_QKV || kind == ST_GU) {
-      float* hr = hres + (kind == ST_GU && s < NS ? Ha : 0);
-      if (s == 0) {
-        for (int k = pl; k < H; k += kPL) {
-          const float v = P.h_in[k];
-          xs[xpad(k)] = v;
-          hr[k] = v;
-          ss = fmaf(v, v, ss);
-        }
-      } else {
-        const int64_t off = kind == ST_GU && s < NS ? rec(l, ST_WO) : rec(l - 1, ST_DN);
-        ss = poll_tagged(rs, off, H, step, pl, &hdr->status, [&](int k, float v) {
-          xs[xpad(k)] = v;
-          hr[k] = v;
-        });
-      }
-      ss = wave_sum_dpp(ss);
-      if (lane == 0) s_ss[s & 1][wave] = ss;
-    } else if (kind == ST_WO) {
-      // the position-0 attention output: query head h returns the value
-      // vector of key/value head h / (n_heads / n_kv_heads), so value entry
-      // k goes to every query head of its group
-      const int64_t off = rec(l, ST_QKV) + (int64_t)(P.NH + P.NKV) * P.HD * 8;
-      const int grp = P.NH / P.NKV;
-      poll_tagged(rs, off, P.NKV * P.HD, step, pl, &hdr->status, [&](int k, float v) {
-        const int g = k / P.HD, j = k - g * P.HD;
-        for (int h = g * grp; h < (g + 1) * grp; ++h) xs[xpad(h * P.HD + j)] = v;
-      });
-    } else {
-      poll_tagged(rs, rec(l, ST_GU), P.I, step, pl, &hdr->status,
-                  [&](int k, float v) { xs[xpad(k)] = v; });
-    }
+  // ---- weight slots: 0 = A (top waves) or D (bottom waves), 1 = B, 2 = C ----
+  TaskW s0, s1, s2;
+  const int KA = H, KB = P.NHD, KC = H;
+  auto loadA = [&](int l) {
+    // value items first, then query/key items
+    const int it = ta < tv ? P.Mq / 4 - P.KV / 4 + v0 + ta : q0 + ta - tv;
+    load_task(wt[4 * l + ST_QKV], KA, 0, KA >> 4, rows_item(it, lane & 3), lane, s0);
   };
-
-  // ---- weight waves: which wave takes which task ----------------------------
-  // Tasks of the small projections go to different waves (down from wave 0,
-  // qkv after it, wo after that; gate_up spreads over all), so that most
-  // waves' next task is one or more projections away and its weights can be
-  // loaded that early.
-  int nt[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) nt[k] = NS > 0 ? s_ki[k].ntask : 0;
-  const int cap_dn = nt[ST_DN] < kXW ? nt[ST_DN] : kXW;
-  const int cap_qkv = nt[ST_QKV] < kXW ? nt[ST_QKV] : kXW;
-  auto base_of = [&](int kind) {
-    return kind == ST_QKV ? cap_dn % kXW : kind == ST_WO ? (cap_dn + cap_qkv) % kXW : 0;
+  auto loadB = [&](int l) {
+    load_task(wt[4 * l + ST_WO], KB, 0, KB >> 4, rows_item(w0 + cw, lane & 3), lane, s1);
   };
-  auto first_task = [&](int kind) { return (cw - base_of(kind) + kXW) % kXW; };
-  // next projection (from s on, within one layer's worth) with a task for
-  // this wave, or -1
-  auto next_work = [&](int s) {
-    const int end = s + 4 < NS ? s + 4 : NS;
-    for (int s2 = s; s2 < end; ++s2)
-      if (first_task(s2 & 3) < nt[s2 & 3]) return s2;
-    return -1;
+  auto loadC = [&](int l) {
+    load_task(wt[4 * l + ST_GU], KC, 0, KC >> 4, rows_pair(g0 + ta, lane & 3), lane, s2);
   };
-  TaskRegs pf[kPre];
-  int pf_s = -1;
-  // the weights of this wave's first kPre tasks of projection s
-  auto prefetch = [&](int s) {
-    pf_s = s;
-    if (s < 0) return;
-    const Stage nx = stage_of(s_ki, wt, s);
-    const int tau0 = first_task(nx.kind);
-#pragma unroll
-    for (int j = 0; j < kPre; ++j) {
-      const int tau = tau0 + j * kXW;
-      if (tau < nx.ntask) {
-        const int item = vwg + task_item(nx, tau) * G;
-#pragma unroll
-        for (int k = 0; k < kRounds; ++k) {
-          const int c = task_chunk(nx, tau, k, lane);
-          pf[j].q[k] = u32x4{0, 0, 0, 0};
-          pf[j].d[k] = 0;
-          if (c < nx.C) load_lane(nx, item, c, lane, pf[j].q[k], pf[j].d[k]);
-        }
-      }
-    }
+  auto loadD = [&](int l) {
+    load_task(wt[4 * l + ST_DN], P.I, cs0, cslice, rows_item(w0 + cw, lane & 3), lane, s0);
   };
-
-  if (poller) {
-    poll_stage(0);
-  } else if (NS > 0) {
-    prefetch(next_work(0));
+  if (L > 0) {
+    if (hasA) loadA(0);
+    if (hasB) loadB(0);
+    if (hasC) loadC(0);
+    if (hasD) loadD(0);
   }
 
-  for (int s = 0; s < NS; ++s) {
-    __syncthreads();  // A(s): input of s staged; every wave done with s - 1
-    if (poller) {
-      // start polling once this workgroup's own outputs of s are written:
-      // the others' finish at about the same time, so one round usually
-      // finds everything, and idle rounds would only add memory traffic
-      __syncthreads();  // B(s)
-      if (s + 1 < NS || P.V > 0) poll_stage(s + 1);
-      continue;
+  // ---- poll waves: stage the input h of layer 0 --------------------------------
+  if (poller) {
+    float ss = 0.f;
+    for (int k = pl; k < H; k += kPL) {
+      const float v = P.h_in[k];
+      xb0[xpad(k)] = v;
+      hres[k] = v;
+      ss = fmaf(v, v, ss);
     }
-    const Stage st = stage_of(s_ki, wt, s);
-    const int l = st.layer;
-    const float* xs = xsb + (s & 1) * XSa;
-    auto x_off = [&](int c) { return 20 * c; };
-    // one wave task: 16 chunks of one item (4 rows); the last task of an item
-    // to finish folds the item's partials in task order and writes its outputs
-    auto run_task = [&](int tau, const TaskRegs& w) {
-      float v = 0.f;
-#pragma unroll
-      for (int k = 0; k < kRounds; ++k) {
-        // every round reads a valid chunk (its own, else chunk 0), with no
-        // branch, so that the rounds' LDS reads can be issued together; the
-        // weights of a chunk past the row end are zero and its sum is dropped
-        const int c = task_chunk(st, tau, k, lane);
-        const float t = lane_dot(w.q[k], w.d[k], xs, x_off(c < st.C ? c : 0));
-        v += c < st.C ? t : 0.f;
-      }
-      v = row_sum(v);
-      const int it = task_item(st, tau);
-      float y = v;
-      if (st.tpi > 1) {
-        if (lane < 4) red[tau * 4 + lane] = v;
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): partials written
-        int arrived = 0;
-        if (lane == 0) arrived = atomicAdd(&s_cnt[it], 1);
-        arrived = __builtin_amdgcn_readfirstlane(arrived);
-        if (arrived != st.tpi - 1) return;
-        if (lane == 0) s_cnt[it] = 0;
-        y = 0.f;
+    ss = wave_sum_dpp(ss);
+    if (lane == 0) s_ss[0][wave] = ss;
+  }
+
+  const int grp = P.NH / P.NKV;
+  for (int l = 0; l < L; ++l) {
+    // ================= stage A: value rows (and query/key rows) ===============
+    __syncthreads();
+    if (!poller) {
+      if (hasD && l > 0) loadD(l);  // slot 0 of the bottom waves is free since D(l - 1)
+      if (hasA) {
+        const float c = rms_scale(s_ss[0], H, P.eps);
+        const float y = task_dot(s0, KA >> 4, xb0, lane) * c;
         if (lane < 4) {
-          const float* rp = red + it * st.tpi * 4 + lane;
-          for (int cb = 0; cb < st.tpi; ++cb) y += rp[cb * 4];
+          if (ta < tv) {
+            const int row = 4 * (v0 + ta) + lane;  // value row
+            st_tag_local(rs, lrec(P.o_v, l) + ((int64_t)x * P.gv + row) * 8, y, step, coherent);
+            if (x == 0)
+              st_tag<0>(rs, lrec(P.o_qkv, l) + (int64_t)(P.Mq - P.KV + row) * 8, y, step);
+          } else {
+            const int row = 4 * (q0 + ta - tv) + lane;
+            st_tag<0>(rs, lrec(P.o_qkv, l) + (int64_t)row * 8, y, step);
+          }
         }
       }
-      const int item = vwg + it * G;
-      const int t = item >> 4, j = item & 15;
-      if (st.kind == ST_QKV || st.kind == ST_GU) y *= rms_scale(s_ss[s & 1], H, P.eps);
-      if (st.kind == ST_GU) {
+    } else {
+      // the value vector of this XCD -> the position-0 attention output: query
+      // head h returns value head h / (n_heads / n_kv_heads)
+      poll_stage_rec(
+          rs, P.KV / 2, step, pl, P.spin, failed, status,
+          [&](int sl) { return (int)(lrec(P.o_v, l) + ((int64_t)x * P.gv + 2 * sl) * 8); },
+          [&](int sl, float a, float c2) {
+            const int k = 2 * sl, g = k / P.HD, jj = k - g * P.HD;
+            for (int hh = g * grp; hh < (g + 1) * grp; ++hh) {
+              xb1[xpad(hh * P.HD + jj)] = a;
+              xb1[xpad(hh * P.HD + jj + 1)] = c2;
+            }
+          });
+    }
+    // ================= stage B: h1 = h + Wo attn (all of h1 on every XCD) =====
+    __syncthreads();
+    if (!poller) {
+      if (hasA && l + 1 < L) loadA(l + 1);
+      if (hasB) {
+        const float y = task_dot(s1, KB >> 4, xb1, lane);
+        if (lane < 4) {
+          const int row = 4 * (w0 + cw) + lane;
+          const float h1 = hres[row] + y;
+          h1s[4 * cw + lane] = h1;
+          st_tag_local(rs, lrec(P.o_h1, l) + ((int64_t)x * P.gh + row) * 8, h1, step, coherent);
+        }
+      }
+    } else {
+      float ss = 0.f;
+      poll_stage_rec(
+          rs, H / 2, step, pl, P.spin, failed, status,
+          [&](int sl) { return (int)(lrec(P.o_h1, l) + ((int64_t)x * P.gh + 2 * sl) * 8); },
+          [&](int sl, float a, float c2) {
+            xb0[xpad(2 * sl)] = a;
+            xb0[xpad(2 * sl + 1)] = c2;
+            ss = fmaf(a, a, ss);
+            ss = fmaf(c2, c2, ss);
+          });
+      ss = wave_sum_dpp(ss);
+      if (lane == 0) s_ss[1][wave] = ss;
+    }
+    // ================= stage C: this XCD's slice of s = swiglu(gate, up) ======
+    __syncthreads();
+    if (!poller) {
+      if (hasB && l + 1 < L) loadB(l + 1);
+      if (hasC) {
+        const float c = rms_scale(s_ss[1], H, P.eps);
+        const float y = task_dot(s2, KC >> 4, xb0, lane) * c;
         // lanes 0, 1: gate rows; 2, 3: the matching up rows (quad_perm [2,3,2,3])
         const float up = dpp_f<0xEE>(y);
-        if (lane < 2) st_tag(recp(l, ST_GU) + 32 * t + 2 * j + lane, y / (1.0f + expf(-y)) * up, step);
-      } else if (lane < 4) {
-        const int row = 64 * t + 4 * j + lane;
-        if (st.kind == ST_QKV) {
-          st_tag(recp(l, ST_QKV) + row, y, step);
-        } else {
-          const float out = hres[(st.kind == ST_DN ? Ha : 0) + row] + y;
-          st_tag(recp(l, st.kind) + row, out, step);
-          if (st.kind == ST_DN && l == L - 1 && P.h_out) P.h_out[row] = out;
+        if (lane < 2) {
+          const int o = 2 * (g0 + ta) + lane;
+          st_tag_local(rs, lrec(P.o_s, l) + (int64_t)o * 8, y / (1.0f + expf(-y)) * up, step,
+                       coherent);
         }
       }
-    };
-    int tau = first_task(st.kind);
-    if (pf_s == s) {
-#pragma unroll
-      for (int j = 0; j < kPre; ++j) {
-        if (tau < st.ntask) {
-          TaskRegs w = pf[j];
-          // keep arithmetic on the prefetched registers after barrier A
-#pragma unroll
-          for (int k = 0; k < kRounds; ++k) __asm__ volatile("" : "+v"(w.q[k]), "+v"(w.d[k]));
-          run_task(tau, w);
+    } else {
+      const int base = 16 * cs0;
+      poll_stage_rec(
+          rs, 8 * cslice, step, pl, P.spin, failed, status,
+          [&](int sl) { return (int)(lrec(P.o_s, l) + (int64_t)(base + 2 * sl) * 8); },
+          [&](int sl, float a, float c2) {
+            xb1[xpad(2 * sl)] = a;
+            xb1[xpad(2 * sl + 1)] = c2;
+          });
+    }
+    // ================= stage D: this XCD's split-K partial of down ============
+    __syncthreads();
+    if (!poller) {
+      if (hasC && l + 1 < L) loadC(l + 1);
+      if (hasD) {
+        const float y = task_dot(s0, cslice, xb1, lane);
+        if (lane < 4) {
+          const int row = 4 * (w0 + cw) + lane;
+          st_tag<kAuxDev>(rs, lrec(P.o_p, l) + ((int64_t)x * P.gh + row) * 8, y, step);
         }
-        tau += kXW;
       }
-    }
-    for (; tau < st.ntask; tau += kXW) {
-      TaskRegs w;
-      const int item = vwg + task_item(st, tau) * G;
+    } else {
+      // ---- stage E (wave 0): this member's rows of h2 = h1 + the XCDs'
+      // partials in XCD order; then every poll wave stages the next h
+      if (wave == 0) {
+        const int nr = 4 * tw;   // rows owned, from row 4 w0
+        const int per = 2 * tw;  // slots per partial
+        auto addr = [&](int sl) {
+          const int xs = sl / per, k = sl - xs * per;
+          return (int)(lrec(P.o_p, l) + ((int64_t)xs * P.gh + 4 * w0 + 2 * k) * 8);
+        };
+        auto put = [&](int sl, float a, float c2) {
+          const int xs = sl / per, k = sl - xs * per;
+          pbuf[xs * 4 * kMaxTw + 2 * k] = a;
+          pbuf[xs * 4 * kMaxTw + 2 * k + 1] = c2;
+        };
+        const int nsl = kNX * per;
+        if (nsl > 0) {
+          if (nsl <= 64)
+            poll_rec<1>(rs, nsl, 64, step, lane, P.spin, failed, status, addr, put);
+          else if (nsl <= 128)
+            poll_rec<2>(rs, nsl, 64, step, lane, P.spin, failed, status, addr, put);
+          else
+            poll_rec<3>(rs, nsl, 64, step, lane, P.spin, failed, status, addr, put);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's partials are in LDS
+        if (lane < nr) {
+          float h2 = h1s[lane];
 #pragma unroll
-      for (int k = 0; k < kRounds; ++k) {
-        const int c = task_chunk(st, tau, k, lane);
-        w.q[k] = u32x4{0, 0, 0, 0};
-        w.d[k] = 0;
-        if (c < st.C) load_lane(st, item, c, lane, w.q[k], w.d[k]);
+          for (int xs = 0; xs < kNX; ++xs) h2 += pbuf[xs * 4 * kMaxTw + lane];
+          const int row = 4 * w0 + lane;
+          st_tag_local(rs, lrec(P.o_h2, l) + ((int64_t)x * P.gh + row) * 8, h2, step, coherent);
+          if (x == 0 && l == L - 1 && P.h_out) P.h_out[row] = h2;
+        }
       }
-      run_task(tau, w);
+      float ss = 0.f;
+      poll_stage_rec(
+          rs, H / 2, step, pl, P.spin, failed, status,
+          [&](int sl) { return (int)(lrec(P.o_h2, l) + ((int64_t)x * P.gh + 2 * sl) * 8); },
+          [&](int sl, float a, float c2) {
+            xb0[xpad(2 * sl)] = a;
+            xb0[xpad(2 * sl + 1)] = c2;
+            hres[2 * sl] = a;
+            hres[2 * sl + 1] = c2;
+            ss = fmaf(a, a, ss);
+            ss = fmaf(c2, c2, ss);
+          });
+      ss = wave_sum_dpp(ss);
+      if (lane == 0) s_ss[0][wave] = ss;
     }
-    __syncthreads();  // B(s)
-    // the next projection with work for this wave streams in from now on
-    // (issued after B: a full memory pipeline stalls the issuing wave)
-    if (pf_s <= s) prefetch(next_work(s + 1));
   }
 
   // ---- LM head + argmax ---------------------------------------------------
@@ -644,12 +663,11 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   if (V > 0) {
-    __syncthreads();  // A(LM)
-    const float* xs = xsb + (NS & 1) * XSa;
-    const float c = rms_scale(s_ss[NS & 1], H, P.eps);
+    __syncthreads();  // the final h is staged in xb0
+    const float c = rms_scale(s_ss[0], H, P.eps);
     const int T = (V + 63) >> 6;
-    for (int tile = wave * G + vwg; tile < T; tile += kCW * G) {
-      const float y = lm_tile_dot(P.lm, H, tile, lane, xs) * c;
+    for (int tile = wave * G + b; tile < T; tile += kCW * G) {
+      const float y = lm_tile_dot(P.lm, H, tile, lane, xb0) * c;
       const int row = tile * 64 + lane;
       if (row < V) {
         P.logits[row] = y;
@@ -671,32 +689,42 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
           bv = s_cv[w];
           bi = s_ci[w];
         }
-      st_dev(reinterpret_cast<float*>(ws + P.am_off) + 2 * vwg, bv);
-      st_dev(reinterpret_cast<int32_t*>(ws + P.am_off) + 2 * vwg + 1, bi);
+      st_dev(reinterpret_cast<float*>(ws + P.am_off) + 2 * b, bv);
+      st_dev(reinterpret_cast<int32_t*>(ws + P.am_off) + 2 * b + 1, bi);
     }
   }
 
-  // ---- end of step: the last workgroup folds the argmax and advances the step
+  // ---- end of step: the last workgroup folds the argmax and advances the step.
+  // The partials above are device-scope stores; each wave waits for its stores
+  // to complete before the barrier, and the ticket is taken after it, so the
+  // last arriver's device-scope loads see every partial.
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) s_last = ticket_add(&hdr->ticket) == (unsigned)(G - 1);
   __syncthreads();
   if (!s_last || wave != 0) return;
+  __asm__ volatile("" ::: "memory");
   if (V > 0) {
     float v = -INFINITY;
     int i = 0x7fffffff;
     for (int g = lane; g < G; g += 64) {
-      const float tv = ld_dev(reinterpret_cast<const float*>(ws + P.am_off) + 2 * g);
+      const float tv2 = ld_dev(reinterpret_cast<const float*>(ws + P.am_off) + 2 * g);
       const int ti = ld_dev(reinterpret_cast<const int32_t*>(ws + P.am_off) + 2 * g + 1);
-      if (tv > v || (tv == v && ti < i)) {
-        v = tv;
+      if (tv2 > v || (tv2 == v && ti < i)) {
+        v = tv2;
         i = ti;
       }
     }
     wave_argmax(v, i);
-    if (lane == 0) *P.next_token = i;
+    // an expired wait anywhere in this step makes its outputs invalid: say so
+    // in the token itself
+    const uint32_t st = ld_dev(status);
+    if (lane == 0) *P.next_token = st ? -1 : i;
   }
   if (lane == 0) {
+    const uint32_t st = ld_dev(status);
+    if (st) atomicOr(&hdr->status, st);
+    st_dev(status, 0u);
     st_dev(&hdr->ticket, 0u);
     st_dev(&hdr->step, step);
   }
@@ -710,49 +738,84 @@ __global__ void chain_unpack_kernel(const uint64_t* src, int n, float* dst) {
 
 __global__ void chain_status_kernel(const uint32_t* st, int32_t* out) { *out = (int32_t)*st; }
 
+// Records the XCD of every workgroup of a grid shaped like the chain's.
+__global__ __launch_bounds__(kCT) void chain_place_kernel(int32_t* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = (int32_t)xcc_id();
+}
+
 // ---- host side ---------------------------------------------------------------
 struct Layout {
-  int32_t Mq, XS;
-  int64_t par_bytes, off[4], layer_stride, am_off, total;
+  int32_t Mq, KV, NHD, XS, gv, gh;
+  int64_t par_bytes, o_qkv, o_v, o_h1, o_s, o_p, o_h2, layer_stride, am_off, total;
   int32_t lds_bytes;
 };
+
+int64_t a256(int64_t v) { return (v + 255) / 256 * 256; }
 
 int layout_of(const q8_0_chain_desc* c, Layout* lo) {
   if (!c) return Q8_ENULL;
   const int64_t L = c->n_layers, H = c->hidden, NH = c->n_heads, NKV = c->n_kv_heads,
                 HD = c->head_dim, I = c->intermediate;
   if (L < 0 || L > 1024 || H <= 0 || NH <= 0 || NKV <= 0 || HD <= 0 || I <= 0) return Q8_EINVAL;
-  if (NH % NKV || H % 32 || (NH * HD) % 32 || I % 32 || HD % 16) return Q8_EINVAL;
+  if (NH % NKV || H % 32 || (NH * HD) % 32 || I % 32 || HD % 2) return Q8_EINVAL;
   if (!(c->eps >= 0.f)) return Q8_EINVAL;
-  const int64_t Mq = (NH + 2 * NKV) * HD;
-  if (Mq % 4) return Q8_EINVAL;
-  if (H > kMaxIn || NH * HD > kMaxIn || I > kMaxIn || NKV * HD > kMaxIn) return Q8_EINVAL;
+  const int64_t KV = NKV * HD, Mq = (NH + 2 * NKV) * HD;
+  if (KV % 4 || Mq % 4) return Q8_EINVAL;
+  // a task covers a whole row of at most kMaxK weights
+  if (H > kMaxK || NH * HD > kMaxK || KV > kMaxK) return Q8_EINVAL;
+  if ((I / 16 + kNX - 1) / kNX * 16 > kMaxK) return Q8_EINVAL;
   if (c->vocab < 0 || c->vocab > 0x7fffffff - 64) return Q8_EINVAL;
-  // wave tasks per workgroup must fit the partial-sum area (checked for one
-  // workgroup per compute unit at launch; 64 is the smallest grid accepted)
-  const int64_t shapes[4][2] = {{Mq, H}, {H, NH * HD}, {2 * I, H}, {H, I}};
-  for (auto& sh : shapes) {
-    const int64_t items = sh[0] / 4, tpi = (sh[1] / 16 + kTaskChunks - 1) / kTaskChunks;
-    if (((items + 63) / 64) * tpi > kMaxTasks) return Q8_EINVAL;
-  }
   lo->Mq = (int32_t)Mq;
-  lo->XS = (int32_t)std::max(std::max(H, NH * HD), I);
-  lo->par_bytes = (int64_t)align_up(sizeof(ChainMat) * (4 * L + 1), 256);
+  lo->KV = (int32_t)KV;
+  lo->NHD = (int32_t)(NH * HD);
+  lo->XS = (int32_t)std::max(std::max(H, NH * HD), (I / 16 + kNX - 1) / kNX * 16);
+  lo->gv = (int32_t)(a256(KV * 8) / 8);
+  lo->gh = (int32_t)(a256(H * 8) / 8);
+  lo->par_bytes = a256((int64_t)sizeof(ChainMat) * (4 * L + 1));
   int64_t o = kHdrBytes + lo->par_bytes;
-  const int64_t len[4] = {Mq, H, I, H};
-  for (int k = 0; k < 4; ++k) {
-    lo->off[k] = o;
-    o += (int64_t)align_up(len[k] * 8, 256);
-  }
-  lo->layer_stride = o - lo->off[0];
-  o = lo->off[0] + lo->layer_stride * L;
+  lo->o_qkv = o;
+  o += a256(Mq * 8);
+  lo->o_v = o;
+  o += kNX * (int64_t)lo->gv * 8;
+  lo->o_h1 = o;
+  o += kNX * (int64_t)lo->gh * 8;
+  lo->o_s = o;
+  o += a256(I * 8);
+  lo->o_p = o;
+  o += kNX * (int64_t)lo->gh * 8;
+  lo->o_h2 = o;
+  o += kNX * (int64_t)lo->gh * 8;
+  lo->layer_stride = o - lo->o_qkv;
+  o = lo->o_qkv + lo->layer_stride * L;
   lo->am_off = o;
   o += kMaxGrid * 8;
   lo->total = o;
   const int64_t XSp = lo->XS + (lo->XS >> 4) * 4;  // padded input length
-  const int64_t lds = 4 * (2 * ((XSp + 3) & ~3) + 2 * ((H + 3) & ~3) + kMaxTasks * 4) +
+  const int64_t lds = 4 * (2 * ((XSp + 3) & ~3) + ((H + 3) & ~3) + 4 * kMaxTw +
+                           kNX * 4 * kMaxTw) +
                       (int64_t)sizeof(ChainMat) * 4 * L;
   lo->lds_bytes = (int32_t)lds;
+  return Q8_OK;
+}
+
+// Every workgroup's tasks fit the weight waves: value + query/key tasks on
+// the top waves and wo/down tasks on the bottom ones without overlap, gate/up
+// tasks within the weight waves.
+int tasks_fit(const q8_0_chain_desc* c, const Layout& lo, int G) {
+  if (G % kNX || G / kNX < 1) return Q8_EINVAL;
+  const int GS = G / kNX;
+  const int64_t I = c->intermediate;
+  auto cnt = [](int64_t n, int64_t parts, int64_t i) {
+    return (int)(n * (i + 1) / parts - n * i / parts);
+  };
+  for (int b = 0; b < G; ++b) {
+    const int x = b % kNX, jm = b / kNX;
+    const int tv = cnt(lo.KV / 4, GS, jm), tq = cnt((lo.Mq - lo.KV) / 4, G, b);
+    const int tw = cnt(c->hidden / 4, GS, jm);
+    const int64_t cs0 = I / 16 * x / kNX, cs1 = I / 16 * (x + 1) / kNX;
+    const int tc = cnt(8 * (cs1 - cs0), GS, jm);
+    if (tw > kMaxTw || tv + tq + tw > kXW || tc > kXW) return Q8_EINVAL;
+  }
   return Q8_OK;
 }
 
@@ -774,14 +837,8 @@ int chain_prepare(const q8_0_chain_desc* c, void* ws, size_t ws_bytes, q8_0_chai
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return Q8_ELAUNCH;
-  if (cus < 64 || cus > kMaxGrid) return Q8_EINVAL;
-  // the partial-sum area must hold every workgroup's wave tasks at this grid
-  const int64_t H = c->hidden, I = c->intermediate, NHD = (int64_t)c->n_heads * c->head_dim;
-  const int64_t shapes[4][2] = {{lo.Mq, H}, {H, NHD}, {2 * I, H}, {H, I}};
-  for (auto& sh : shapes) {
-    const int64_t items = sh[0] / 4, tpi = (sh[1] / 16 + kTaskChunks - 1) / kTaskChunks;
-    if (((items + cus - 1) / cus) * tpi > kMaxTasks) return Q8_EINVAL;
-  }
+  if (cus < kNX || cus > kMaxGrid) return Q8_EINVAL;
+  if ((rc = tasks_fit(c, lo, cus))) return rc;
   int maxlds = 0;
   if (hipDeviceGetAttribute(&maxlds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
       hipSuccess)
@@ -791,11 +848,13 @@ int chain_prepare(const q8_0_chain_desc* c, void* ws, size_t ws_bytes, q8_0_chai
   int lds = lo.lds_bytes;
   if (maxlds >= 96 * 1024 && lds < 84 * 1024) lds = 84 * 1024;
   if (lds > maxlds) return Q8_EINVAL;
-  if (lds > 64 * 1024 &&
-      hipFuncSetAttribute((const void*)chain_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          lds) != hipSuccess) {
-    (void)hipGetLastError();
-    return Q8_ELAUNCH;
+  const void* kernels[2] = {(const void*)chain_kernel, (const void*)chain_place_kernel};
+  for (const void* k : kernels) {
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
+      (void)hipGetLastError();
+      return Q8_ELAUNCH;
+    }
   }
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel, kCT, lds) !=
@@ -815,13 +874,29 @@ int chain_prepare(const q8_0_chain_desc* c, void* ws, size_t ws_bytes, q8_0_chai
     }
   }
   uint8_t* w8 = static_cast<uint8_t*>(ws);
-  if (hipMemsetAsync(ws, 0, (size_t)lo.total, stream) != hipSuccess ||
+  // Where the workgroups of a chain-shaped grid run: the hand-offs inside an
+  // XCD rely on the members b, b + 8, b + 16, ... of a group sharing one XCD
+  // (the dispatcher deals workgroups to the XCDs in turn); if a grid of this
+  // shape does not, every hand-off goes through device-scope stores instead.
+  std::vector<int32_t> place(cus, -1);
+  int32_t* dplace = reinterpret_cast<int32_t*>(w8 + lo.am_off);
+  if (hipMemsetAsync(ws, 0, (size_t)lo.total, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return Q8_ELAUNCH;
+  }
+  hipLaunchKernelGGL(chain_place_kernel, dim3(cus), dim3(kCT), lds, stream, dplace);
+  if (hipGetLastError() != hipSuccess ||
+      hipMemcpyAsync(place.data(), dplace, (size_t)cus * 4, hipMemcpyDeviceToHost, stream) !=
+          hipSuccess ||
+      hipMemsetAsync(dplace, 0, (size_t)cus * 4, stream) != hipSuccess ||
       hipMemcpyAsync(w8 + kHdrBytes, host.data(), host.size() * sizeof(ChainMat),
                      hipMemcpyHostToDevice, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess) {
     (void)hipGetLastError();
     return Q8_ELAUNCH;
   }
+  bool placed = true;
+  for (int i = 0; i < cus; ++i) placed &= place[i] == place[i % kNX] && place[i] >= 0;
   memset(plan, 0, sizeof(*plan));
   plan->grid = cus;
   plan->threads = kCT;
@@ -834,8 +909,12 @@ int chain_prepare(const q8_0_chain_desc* c, void* ws, size_t ws_bytes, q8_0_chai
   plan->intermediate = c->intermediate;
   plan->vocab = c->vocab;
   plan->eps = c->eps;
+  plan->flags = placed ? 0u : (uint32_t)Q8_CHAIN_COHERENT;
   plan->ws_bytes = lo.total;
-  for (int k = 0; k < 4; ++k) plan->off[k] = lo.off[k];
+  plan->off[Q8_CHAIN_QKV] = lo.o_qkv;
+  plan->off[Q8_CHAIN_H_ATTN] = lo.o_h1;  // the copy of XCD group 0
+  plan->off[Q8_CHAIN_SWIGLU] = lo.o_s;
+  plan->off[Q8_CHAIN_H_OUT] = lo.o_h2;   // the copy of XCD group 0
   plan->layer_stride = lo.layer_stride;
   plan->am_off = lo.am_off;
   if (c->vocab > 0) {
@@ -846,11 +925,18 @@ int chain_prepare(const q8_0_chain_desc* c, void* ws, size_t ws_bytes, q8_0_chai
   plan->len[1] = c->hidden;
   plan->len[2] = c->intermediate;
   plan->len[3] = c->hidden;
+  plan->spin_limit = 0;
+  plan->groups = kNX;
+  plan->off_v = lo.o_v;
+  plan->off_p = lo.o_p;
+  plan->group_words_v = lo.gv;
+  plan->group_words_h = lo.gh;
   return Q8_OK;
 }
 
 int chain_run(const q8_0_chain_plan* plan, void* ws, const float* h_in, float* h_out,
               float* logits, int32_t* next_token, hipStream_t stream) {
+  if (plan->groups != kNX || plan->grid % kNX) return Q8_EINVAL;
   ChainArgs a;
   memset(&a, 0, sizeof(a));
   a.ws = static_cast<uint8_t*>(ws);
@@ -866,12 +952,21 @@ int chain_run(const q8_0_chain_plan* plan, void* ws, const float* h_in, float* h
   a.I = plan->intermediate;
   a.V = plan->vocab;
   a.G = plan->grid;
+  a.GS = plan->grid / kNX;
   a.Mq = plan->len[0];
+  a.KV = plan->n_kv_heads * plan->head_dim;
+  a.NHD = plan->n_heads * plan->head_dim;
   a.eps = plan->eps;
-  a.off_qkv = plan->off[0];
-  a.off_h1 = plan->off[1];
-  a.off_s = plan->off[2];
-  a.off_h2 = plan->off[3];
+  a.flags = plan->flags;
+  a.spin = plan->spin_limit ? plan->spin_limit : kDefaultSpin;
+  a.o_qkv = plan->off[Q8_CHAIN_QKV];
+  a.o_h1 = plan->off[Q8_CHAIN_H_ATTN];
+  a.o_s = plan->off[Q8_CHAIN_SWIGLU];
+  a.o_h2 = plan->off[Q8_CHAIN_H_OUT];
+  a.o_v = plan->off_v;
+  a.o_p = plan->off_p;
+  a.gv = plan->group_words_v;
+  a.gh = plan->group_words_h;
   a.layer_stride = plan->layer_stride;
   a.am_off = plan->am_off;
   a.ws_bytes = plan->ws_bytes;

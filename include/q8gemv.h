@@ -423,13 +423,26 @@ int q8_0_moe_gemv(const q8_0_weights* W_experts, const int32_t* expert_ids,
  * of the RMS scale); repeated runs are bitwise identical.
  *
  * The launch keeps one workgroup resident on every compute unit for the whole
- * step and hands activations between projections through the workspace, so
- * the caller must not run other work that occupies the whole device
- * concurrently with it (it would only be slower; every wait in the kernel is
- * bounded and an expired wait sets bit 1 of the status word).
+ * step and hands activations between workgroups through the workspace; all of
+ * them must be resident at once, so nothing else may occupy the device while
+ * a step runs.  Most hand-offs stay inside one XCD (its L2 is shared); that
+ * needs the members b, b + 8, b + 16, ... of each of the 8 groups on one XCD,
+ * which q8_0_chain_prepare checks with a probe launch of the same shape
+ * (otherwise it sets Q8_CHAIN_COHERENT in the plan: every hand-off then goes
+ * through device-scope stores, slower but independent of placement).
  *
- * Limits: hidden, n_heads*head_dim and intermediate are multiples of 32 and
- * at most 5376; n_heads % n_kv_heads == 0; head_dim % 16 == 0.  Weights: qkv_l
+ * Every wait in the kernel is bounded (plan.spin_limit polling rounds).  A
+ * wait that expires marks the step invalid: *next_token is set to -1 (never
+ * a valid index) and bit 1 of the status word is set; the kernel still runs
+ * to completion.  A step with no expired wait writes a valid token, whatever
+ * earlier steps did.  Concurrent work that keeps workgroups from being
+ * resident therefore shows up as -1 tokens, never as plausible wrong ones.
+ *
+ * Limits: hidden, n_heads*head_dim and n_kv_heads*head_dim at most 1024;
+ * hidden, n_heads*head_dim and intermediate multiples of 32; intermediate/8
+ * rounded up to 16 at most 1024; n_heads % n_kv_heads == 0; head_dim even;
+ * the grid (one workgroup per compute unit) a multiple of 8 whose per-
+ * workgroup shares fit its 12 computing waves.  Weights: qkv_l
  * ((n_heads + 2 n_kv_heads) head_dim x hidden), wo_l (hidden x
  * n_heads*head_dim) and down_l (hidden x intermediate) in Q8_LAYOUT_ROWS;
  * gate_up_l (2 intermediate x hidden, gate rows first) in
@@ -452,7 +465,9 @@ typedef struct {
 } q8_0_chain_desc;
 
 /* Filled by q8_0_chain_prepare; passed unchanged to the other chain calls
- * (it holds the launch configuration, so a run needs no device reads). */
+ * (it holds the launch configuration, so a run needs no device reads).  The
+ * caller may set `flags` and `spin_limit` between prepare and run. */
+#define Q8_CHAIN_COHERENT 1u  /* flags: every hand-off through device-scope stores */
 typedef struct {
   int32_t grid;          /* workgroups of the launch (one per compute unit) */
   int32_t threads;       /* threads per workgroup */
@@ -465,7 +480,8 @@ typedef struct {
   int32_t intermediate;
   int32_t vocab;
   float eps;
-  int32_t reserved;
+  uint32_t flags;        /* Q8_CHAIN_COHERENT, set by prepare when workgroup b of a
+                            chain-shaped grid does not run on XCD b % groups */
   int64_t ws_bytes;      /* workspace bytes in use */
   int64_t off[4];        /* workspace offsets of layer 0's four activation records */
   int64_t layer_stride;  /* bytes between layers' records */
@@ -473,6 +489,12 @@ typedef struct {
   const void* lm_qs;     /* LM head weights (NULL without LM head) */
   const void* lm_d;
   int32_t len[4];        /* entries of the four records */
+  uint32_t spin_limit;   /* polling rounds before a wait gives up (0: 65536) */
+  int32_t groups;        /* XCD groups the workgroups are split into (8) */
+  int64_t off_v;         /* workspace offset of layer 0's per-group value records */
+  int64_t off_p;         /* workspace offset of layer 0's down-projection partials */
+  int32_t group_words_v; /* entries between the group copies of a value record */
+  int32_t group_words_h; /* entries between the group copies of a hidden-sized record */
 } q8_0_chain_plan;
 
 /* Workspace bytes for a chain (0 if the description is invalid). */
@@ -510,7 +532,8 @@ int q8_0_chain_read(const q8_0_chain_plan* plan, const void* workspace, int32_t 
                     int32_t which, float* dst, void* stream);
 
 /* Copies the chain's status word to *dev_status (device int32): 0, or bit 1
- * if a wait for another workgroup's data expired in some run since prepare.
+ * if a wait for another workgroup's data expired in some run since prepare
+ * (sticky; each step's own validity is in its next_token).
  * Errors: Q8_ENULL, Q8_EHOSTPTR, Q8_ELAUNCH. */
 int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
 

@@ -158,7 +158,8 @@ def test_chain_workspace_bytes_and_host_validation():
     assert nbytes >= 256 + 2 * 8 * (1152 + 896 + 4864 + 896)
     bad = [dict(gu_layout=q.Q8_LAYOUT_ROWS),   # gate_up must use the pairs layout
            dict(hidden=900), dict(inter=4870), dict(n_kv=3), dict(hd=40),
-           dict(inter=6144),                   # polled vectors longer than the kernel's limit
+           dict(hidden=1056),                  # rows longer than one task covers (1024)
+           dict(inter=8224),                   # down's K slice per XCD longer than 1024
            dict(eps=-1.0), dict(n_layers=-1)]
     for kw in bad:
         d, keep = _chain(**kw)

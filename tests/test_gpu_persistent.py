@@ -196,3 +196,50 @@ def test_persistent_repeatable_and_graph_replay():
     torch.cuda.synchronize()
     assert torch.equal(logits, new)
     assert pc.status() == 0
+
+
+def test_persistent_expired_wait_marks_step_invalid():
+    """A host-set spin limit of one round makes the kernel's own bounded waits
+    give up (the data of other workgroups is not there yet): the step must say
+    so (next_token == -1, sticky status bit 1) and exit normally; the next step
+    with the default limit is valid again and bitwise equal to a clean run."""
+    cfg = ChainConfig(vocab=4096)
+    aos, lm, pc, h0 = build(cfg, 2, 72)
+    logits, tok, h_out = outputs(pc, cfg)
+    x = to_dev(h0)
+    pc.run(x, logits, tok, h_out, check=True)
+    torch.cuda.synchronize()
+    ref_tok, ref_logits = int(host(tok)[0]), logits.clone()
+    assert ref_tok >= 0 and pc.status() == 0
+    pc.plan.spin_limit = 1
+    pc.run(x, logits, tok, h_out)
+    torch.cuda.synchronize()
+    assert int(host(tok)[0]) == -1
+    assert pc.status() & 2
+    with pytest.raises(q.ChainStepError):
+        pc.run(x, logits, tok, h_out, check=True)
+    pc.plan.spin_limit = 0
+    pc.run(x, logits, tok, h_out, check=True)
+    torch.cuda.synchronize()
+    assert int(host(tok)[0]) == ref_tok
+    assert torch.equal(logits, ref_logits)
+
+
+def test_persistent_coherent_mode_bitwise_equal():
+    """Q8_CHAIN_COHERENT (every hand-off through device-scope stores) changes
+    only where the hand-offs are visible, never the arithmetic."""
+    cfg = ChainConfig(vocab=4096)
+    aos, lm, pc, h0 = build(cfg, 3, 73)
+    logits, tok, h_out = outputs(pc, cfg)
+    x = to_dev(h0)
+    pc.run(x, logits, tok, h_out, check=True)
+    torch.cuda.synchronize()
+    ref = (logits.clone(), tok.clone(), h_out.clone(), pc.read(2, q.Q8_CHAIN_SWIGLU).clone())
+    flags = pc.plan.flags
+    pc.plan.flags = flags | q.Q8_CHAIN_COHERENT
+    pc.run(x, logits, tok, h_out, check=True)
+    torch.cuda.synchronize()
+    pc.plan.flags = flags
+    assert torch.equal(logits, ref[0]) and torch.equal(tok, ref[1])
+    assert torch.equal(h_out, ref[2]) and torch.equal(pc.read(2, q.Q8_CHAIN_SWIGLU), ref[3])
+    check_stagewise(aos, lm, pc, h0, cfg, logits, tok, h_out)

@@ -2,6 +2,7 @@
 quantizer bit-exact against the oracle (codes and binary16 scales), and the
 int8 x int8 GEMV within the fp32 tolerance of the oracle's fp64 result on
 the same codes."""
+import ctypes
 import numpy as np
 import pytest
 import torch
@@ -90,8 +91,18 @@ def test_gemv_q8act_rejects_bad_arguments():
     shifted = torch.zeros(97, dtype=torch.int8, device=DEV)[1:].view(1, 96)  # misaligned
     with pytest.raises(q.Q8Error):
         q.q8_0_gemv_q8act(p, shifted, dx)
-    with pytest.raises(q.Q8Error):
+    # 9 columns: the binding refuses before the call, and the C entry point
+    # itself refuses too
+    with pytest.raises(ValueError):
         q.q8_0_gemv_q8act(p, qx.repeat(9, 1), dx.repeat(9, 1))
+    q9, d9 = qx.repeat(9, 1), dx.repeat(9, 1)
+    y9 = torch.zeros(9 * 64, device=DEV)
+    ws = q.Workspace(1 << 20)
+    wp, wb = ws.get(1 << 20)
+    rc = q.lib().q8_0_gemv_q8act(ctypes.byref(p.desc), q9.data_ptr(), d9.data_ptr(),
+                                 y9.data_ptr(), 64, 96, 9, wp, wb,
+                                 torch.cuda.current_stream().cuda_stream)
+    assert rc == q.Q8_EINVAL
     with pytest.raises(q.Q8Error):
         q.q8_0_quantize_act(torch.zeros((1, 100), device=DEV))
     with pytest.raises(q.Q8Error):
