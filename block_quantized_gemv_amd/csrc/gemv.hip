@@ -826,9 +826,12 @@ __device__ __forceinline__ float seg_alpha(const Seg& s) {
 }
 
 // val[ts][n] = sum over segments (in order) of alpha_seg * (sum of the
-// segment's unit partials, in unit order), for each tile of a pair.  Partials
-// are fetched 8 units at a time so that global loads are in flight together;
-// the summation order does not depend on the batching.
+// segment's unit partials), for each tile of a pair.  The unit partials are
+// added in a fixed three-level order: batches of 8 consecutive units, groups
+// of 8 batches, then the groups in order, so the fold adds at most
+// 8 + 8 + ceil(units / 64) roundings to an output's chain (bitwise the same
+// on every call).  Each batch's 8 partials are fetched before any is added,
+// so their global loads are in flight together.
 template <int N, typename Get>
 __device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, int us, Get get,
                                            float (&val)[2][N]) {
@@ -843,24 +846,37 @@ __device__ __forceinline__ void fold_units(const GemvParams& p, const Prob& pr, 
       float ssum[N];
 #pragma unroll
       for (int n = 0; n < N; ++n) ssum[n] = 0.f;
-      for (int i0 = 0; i0 < s.units; i0 += 8) {
-        const int cnt = s.units - i0 < 8 ? s.units - i0 : 8;
-        float buf[8][N];
+      for (int g0 = 0; g0 < s.units; g0 += 64) {
+        float gsum[N];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (j < cnt) {
+        for (int n = 0; n < N; ++n) gsum[n] = 0.f;
+        const int gend = s.units - g0 < 64 ? s.units : g0 + 64;
+        for (int i0 = g0; i0 < gend; i0 += 8) {
+          const int cnt = gend - i0 < 8 ? gend - i0 : 8;
+          float buf[8][N];
 #pragma unroll
-            for (int n = 0; n < N; ++n) buf[j][n] = get(uu + j, n);
+          for (int j = 0; j < 8; ++j) {
+            if (j < cnt) {
+#pragma unroll
+              for (int n = 0; n < N; ++n) buf[j][n] = get(uu + j, n);
+            }
           }
+          float bsum[N];
+#pragma unroll
+          for (int n = 0; n < N; ++n) bsum[n] = buf[0][n];
+#pragma unroll
+          for (int j = 1; j < 8; ++j) {
+            if (j < cnt) {
+#pragma unroll
+              for (int n = 0; n < N; ++n) bsum[n] += buf[j][n];
+            }
+          }
+#pragma unroll
+          for (int n = 0; n < N; ++n) gsum[n] += bsum[n];
+          uu += cnt;
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (j < cnt) {
-#pragma unroll
-            for (int n = 0; n < N; ++n) ssum[n] += buf[j][n];
-          }
-        }
-        uu += cnt;
+        for (int n = 0; n < N; ++n) ssum[n] += gsum[n];
       }
       if (s.alpha_mode == A_ONE) {
 #pragma unroll
@@ -1283,6 +1299,9 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
     // units of 1 quad 8.2 us, 19 units of 2 quads 7.2 us)
     if (few && us > blocks / 2) us = blocks / 2 > 0 ? blocks / 2 : 1;
     if (us < pd.nseg) us = pd.nseg;
+    // a unit covers at most 16 scale quads (64 blocks), which with the
+    // three-level fold keeps every output's chain of roundings short
+    if (us < cdiv(blocks, 16)) us = cdiv(blocks, 16);
     if (us > blocks) us = blocks;
     // With few tiles per compute unit the slowest wave sets the pace: prefer
     // the nearest larger unit count that splits the quads evenly, while the

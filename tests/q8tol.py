@@ -1,10 +1,15 @@
 """Parity tolerance of the Q8_0 GEMV against the fp64 oracle.
 
 Per output: |y_gpu - y_ref| <= 2e-5 * S + 1e-6 with S = sum_k |w_k x_k| (the
-oracle's magnitude sum).  An fp32 schedule whose longest dependent
-accumulation chain plus reduction depth is D has error <= D * 2^-24 * S, so
-any schedule with D below ~335 passes by construction; the kernels' chains are
-at most 32 (one block) + K/32/units (block folds) + units (unit fold).
+oracle's magnitude sum).  An fp32 schedule in which every product passes
+through at most D roundings has error <= D * 2^-24 * S (to first order), so
+any schedule with D below ~335 passes by construction.  In the GEMV kernels a
+product passes through at most 32 (the FMAs of its block) + 1 (the block's
+scale) + 64 (the blocks of one unit: the planner gives a unit at most 16 scale
+quads) + 8 + 8 + ceil(units / 64) (the fixed three-level fold of a tile's unit
+partials) + 2 (segment weight and epilogue) roundings.  Units per tile never
+exceed K / 128, so D <= 115 + K / 8192, below 250 for every K the boundary
+accepts (K <= 2^20).
 """
 import numpy as np
 

@@ -70,7 +70,7 @@ SHAPES = [(1, 256), (64, 256), (65, 512), (130, 1024), (300, 2048), (64, 4096), 
 
 
 @pytest.mark.parametrize("M,K", SHAPES)
-@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_q4k_gemv_matches_oracle(M, K, N):
     g = W.rng(81, M * 7 + N, K)
     m = W.draw_q4k(g, M, K)
