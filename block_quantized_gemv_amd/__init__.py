@@ -40,7 +40,7 @@ EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv",
            "q8_0_strerror", "q8_0_version", "q8_0_chain_workspace_bytes", "q8_0_chain_prepare",
            "q8_0_chain_run", "q8_0_chain_read", "q8_0_chain_status", "q4k_packed_size",
            "q4k_repack", "q4k_gemv", "q5k_packed_size", "q5k_repack", "q5k_gemv",
-           "q6k_packed_size", "q6k_repack", "q6k_gemv")
+           "q6k_packed_size", "q6k_repack", "q6k_gemv", "q8_0_gemv_noalloc")
 
 
 class Q8Error(RuntimeError):
@@ -107,6 +107,7 @@ def lib() -> ctypes.CDLL:
         L.q8_0_repack.argtypes = [P, I64, I64, P, P, P]
         L.q8_0_repack_layout.argtypes = [P, I64, I64, I32, P, P, P]
         L.q8_0_gemv.argtypes = [PW, P, P, I64, I64, I64, P, SZ, P]
+        L.q8_0_gemv_noalloc.argtypes = [PW, P, P, I64, I64, I64, P]
         L.q8_0_gemv_fused.argtypes = [PW, P, P, I64, I64, ctypes.POINTER(q8_0_fusion), P, SZ, P]
         L.q8_0_gemv_argmax.argtypes = [PW, P, P, I64, I64, I64, P, P, SZ, P]
         L.q8_0_quantize_act.argtypes = [P, I64, I64, P, P, P]
@@ -469,6 +470,19 @@ def q8_0_gemv(W: PackedQ8, x: torch.Tensor, y: torch.Tensor | None = None, works
     wsp, wsb = _ws(workspace, q8_0_workspace_bytes(Q8_OP_GEMV, W.M, W.K, N), x.device)
     _check("q8_0_gemv", lib().q8_0_gemv(ctypes.byref(W.desc), x.data_ptr(), y.data_ptr(), W.M,
                                         W.K, N, wsp, wsb, _stream(stream)))
+    return y
+
+
+def q8_0_gemv_noalloc(W: PackedQ8, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """q8_0_gemv with no workspace and no allocation (the library's own
+    per-device scratch array); y must be given."""
+    N = _ncols(x, W.K)
+    _room(y, N * W.M, "y")
+    _need(x, torch.float32, "x")
+    _need(y, torch.float32, "y")
+    _check("q8_0_gemv_noalloc", lib().q8_0_gemv_noalloc(ctypes.byref(W.desc), x.data_ptr(),
+                                                        y.data_ptr(), W.M, W.K, N,
+                                                        _stream(stream)))
     return y
 
 

@@ -7,6 +7,8 @@
 // kernels bound-check them instead of reading through them.
 #include <string.h>
 
+#include <mutex>
+
 #include "q8_internal.h"
 
 using namespace q8;
@@ -267,6 +269,82 @@ static int gemv_common(const q8_0_weights* W, const float* x, float* y, int64_t 
 int q8_0_gemv(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
               void* workspace, size_t workspace_bytes, void* stream) {
   return gemv_common(W, x, y, M, K, N, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+// ---- q8_0_gemv without allocation ---------------------------------------------
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): the split-K partials and tickets live in a file-scope device array
+// instead of a caller workspace.  Each device holds its own copy until the
+// process ends; its address is looked up once per device, with that device
+// current, and only that address is handed to kernels.
+}  // extern "C"
+
+namespace {
+constexpr size_t kScratchBytes = (size_t)8 << 20;  // 8 MiB per device
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` per device (nullptr: not looked up)
+
+// The current device's copy of `scratch` (set up on the first call per device).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return Q8_ELAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return Q8_ELAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return Q8_ELAUNCH;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return Q8_OK;
+}
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+}  // namespace
+
+extern "C" {
+
+int q8_0_gemv_noalloc(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,
+                      int64_t N, void* stream) {
+  int rc = check_weights_shape(W, M, K, false);
+  if (rc) return rc;
+  if (N < 1 || N > Q8_MAX_N) return Q8_EINVAL;
+  if (!x || !y) return Q8_ENULL;
+  ProbDesc pd;
+  if ((rc = build_gemv(W, x, y, M, K, N, nullptr, &pd))) return rc;
+  if (M == 0) return Q8_OK;
+  Plan plan;
+  if ((rc = plan_problems(&pd, 1, (int)N, &plan))) return rc;
+  if (plan.ws_bytes > kScratchBytes) return Q8_EWORKSPACE;
+  if ((rc = check_weights_ptrs(W)) || (rc = check_dev_aligned(x, 4)) ||
+      (rc = check_dev_aligned(y, 4)))
+    return rc;
+  void* ws = nullptr;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan.ws_bytes > 0) {
+    if ((rc = scratch_address(&ws))) return rc;
+    // the array keeps the last call's contents: clear the ticket counters,
+    // which must start at zero, with a kernel on the same stream (no memset
+    // node, so the call can be captured)
+    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, s, static_cast<uint32_t*>(ws),
+                       (int)(kCounterBytes / 4));
+    if (hipGetLastError() != hipSuccess) return Q8_ELAUNCH;
+  }
+  return launch_problems(&pd, 1, (int)N, ws, kScratchBytes, s);
 }
 
 int q8_0_gemv_argmax(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,

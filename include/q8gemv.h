@@ -137,6 +137,21 @@ int q8_0_repack_layout(const void* aos, int64_t M, int64_t K, int32_t layout, vo
 int q8_0_gemv(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- GEMV without allocation -------------------------------------------------
+ * For callers that cannot allocate or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same
+ * product as q8_0_gemv (same kernels and plan, so bitwise the same y), with
+ * the split-K partials and tickets in a library-owned device array of 8 MiB
+ * per device (held until the process ends) instead of a workspace; it calls
+ * no allocator.  Every call on one device shares that array: calls that
+ * overlap on a device (different streams without ordering) race and must not
+ * be issued; stream-ordered calls are fine (each clears the array's ticket
+ * counters first, with a small kernel on the same stream).  Errors as
+ * q8_0_gemv, and Q8_EWORKSPACE if the plan for (M, K, N) needs more than the
+ * array holds (q8_0_workspace_bytes(Q8_OP_GEMV, ...) > 8 MiB). */
+int q8_0_gemv_noalloc(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,
+                      int64_t N, void* stream);
+
 /* ---- GEMV with fused decode-chain glue (N = 1) ----------------------------
  * The non-matmul steps between the projections of one Qwen2-style decoder
  * layer ("augur" README, "Features": RMSNorm before attention, before the MLP
