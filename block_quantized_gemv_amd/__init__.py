@@ -40,7 +40,8 @@ EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv",
            "q8_0_strerror", "q8_0_version", "q8_0_chain_workspace_bytes", "q8_0_chain_prepare",
            "q8_0_chain_run", "q8_0_chain_read", "q8_0_chain_status", "q4k_packed_size",
            "q4k_repack", "q4k_gemv", "q5k_packed_size", "q5k_repack", "q5k_gemv",
-           "q6k_packed_size", "q6k_repack", "q6k_gemv", "q8_0_gemv_noalloc")
+           "q6k_packed_size", "q6k_repack", "q6k_gemv", "q8_0_gemv_noalloc",
+           "q8_stream_read")
 
 
 class Q8Error(RuntimeError):
@@ -108,6 +109,7 @@ def lib() -> ctypes.CDLL:
         L.q8_0_repack_layout.argtypes = [P, I64, I64, I32, P, P, P]
         L.q8_0_gemv.argtypes = [PW, P, P, I64, I64, I64, P, SZ, P]
         L.q8_0_gemv_noalloc.argtypes = [PW, P, P, I64, I64, I64, P]
+        L.q8_stream_read.argtypes = [P, I64, P, I32, P]
         L.q8_0_gemv_fused.argtypes = [PW, P, P, I64, I64, ctypes.POINTER(q8_0_fusion), P, SZ, P]
         L.q8_0_gemv_argmax.argtypes = [PW, P, P, I64, I64, I64, P, P, SZ, P]
         L.q8_0_quantize_act.argtypes = [P, I64, I64, P, P, P]
@@ -484,6 +486,17 @@ def q8_0_gemv_noalloc(W: PackedQ8, x: torch.Tensor, y: torch.Tensor, stream=None
                                                         y.data_ptr(), W.M, W.K, N,
                                                         _stream(stream)))
     return y
+
+
+def q8_stream_read(buf: torch.Tensor, out: torch.Tensor, grid: int = 0, stream=None) -> None:
+    """The streaming read-reduce reference kernel over all of buf's bytes
+    (see q8_stream_read in include/q8gemv.h); out: device int32 [1]."""
+    if not buf.is_cuda or not out.is_cuda:
+        raise ValueError("buf and out must be device tensors")
+    _room(out, 1, "out")
+    _check("q8_stream_read", lib().q8_stream_read(buf.data_ptr(),
+                                                  buf.numel() * buf.element_size(),
+                                                  out.data_ptr(), grid, _stream(stream)))
 
 
 def make_fusion(prologue: int = Q8_PRO_NONE, epilogue: int = 0, eps: float = 0.0,

@@ -175,6 +175,10 @@ int launch_quantize_act(const float* x, int64_t K, int64_t N, int8_t* qx, uint16
 int launch_repack(const void* aos, int64_t M, int64_t K, int32_t layout, void* qs, void* d,
                   hipStream_t stream);
 
+// streaming read-reduce (calib.hip): the achievable-read-bandwidth reference
+int launch_read_reduce(const void* buf, int64_t bytes, uint32_t* out, int grid,
+                       hipStream_t stream);
+
 // persistent decode chain (chain.hip); arguments validated by the C entry points
 size_t chain_ws_bytes(const q8_0_chain_desc* c);
 int chain_prepare(const q8_0_chain_desc* c, void* ws, size_t ws_bytes, q8_0_chain_plan* plan,

@@ -552,6 +552,16 @@ int q8_0_chain_read(const q8_0_chain_plan* plan, const void* workspace, int32_t 
  * Errors: Q8_ENULL, Q8_EHOSTPTR, Q8_ELAUNCH. */
 int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
 
+/* ---- measurement utility ------------------------------------------------------
+ * The on-box reference for achievable HBM read bandwidth: reads the first
+ * `bytes` (rounded down to 16) of device buffer buf (16-byte aligned) with
+ * 16-byte non-temporal loads, the GEMV's weight-streaming instruction, in a
+ * grid-stride loop over `grid` workgroups of 512 threads (0: 2048), and XORs
+ * everything into *out (device uint32, caller-cleared) so no read can be
+ * dropped.  Bandwidth = bytes / kernel time.  Not part of the GEMV path.
+ * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_ELAUNCH. */
+int q8_stream_read(const void* buf, int64_t bytes, uint32_t* out, int32_t grid, void* stream);
+
 /* ---- workspace sizes --------------------------------------------------------
  * op Q8_OP_GEMV: (M, K, N) of q8_0_gemv.
  * op Q8_OP_GEMV_FUSED: (M, K, epilogue flags in N) of q8_0_gemv_fused.
