@@ -335,21 +335,25 @@ def measure_rows(log, only=()):
 
     # ---- the read reference: 16-byte non-temporal loads, 2 GiB and cold 145 MB
     if want("q8_stream_read"):
-        out = torch.zeros(1, dtype=torch.int32, device=dev)
+        out = torch.zeros(8192, dtype=torch.int32, device=dev)
         big = torch.empty(1 << 31, dtype=torch.uint8, device=dev).fill_(1)
         st = torch.cuda.current_stream()
         for grid in (2048, 4096):
             _, secs = time_launches(lambda: q.q8_stream_read(big, out, grid), 10, 2, st)
-            rec("hbm", f"q8_stream_read 2 GiB (grid {grid} x 512)", "M1", secs, big.numel(),
+            rec("hbm", f"q8_stream_read 2 GiB (grid {grid} x 256)", "M1", secs, big.numel(),
                 copies=1)
         del big
         lmb = 151936 * 896 * 17 // 16
         n = copies_for(lmb)
         bufs = torch.empty(n * lmb, dtype=torch.uint8, device=dev).fill_(1)
         views = [bufs[i * lmb:(i + 1) * lmb] for i in range(n)]
-        secs = graph_rounds(lambda i, s: q.q8_stream_read(views[i % n], out, 0, stream=s), n)
+        secs = graph_rounds(lambda i, s: q.q8_stream_read(views[i % n], out, 4096, stream=s), n)
         rec("hbm", "q8_stream_read 145 MB (lm_head bytes), rotating cold copies", "M1", secs,
             lmb, copies=n)
+        secs = graph_rounds(lambda i, s: q.q8_stream_read(views[i % n][:16], out, 1, stream=s),
+                            n)
+        rec("hbm", "q8_stream_read 16 B, one workgroup: the dependent-launch floor", "M1", secs,
+            0)
         del bufs, views
         torch.cuda.empty_cache()
 

@@ -488,12 +488,14 @@ def q8_0_gemv_noalloc(W: PackedQ8, x: torch.Tensor, y: torch.Tensor, stream=None
     return y
 
 
-def q8_stream_read(buf: torch.Tensor, out: torch.Tensor, grid: int = 0, stream=None) -> None:
-    """The streaming read-reduce reference kernel over all of buf's bytes
-    (see q8_stream_read in include/q8gemv.h); out: device int32 [1]."""
+def q8_stream_read(buf: torch.Tensor, out: torch.Tensor, grid: int = 4096, stream=None) -> None:
+    """The streaming read reference kernel over all of buf's bytes (see
+    q8_stream_read in include/q8gemv.h); out: device int32 [>= grid], one XOR
+    word per workgroup."""
     if not buf.is_cuda or not out.is_cuda:
         raise ValueError("buf and out must be device tensors")
-    _room(out, 1, "out")
+    _room(out, grid, "out")
+    _need(out, torch.int32, "out")
     _check("q8_stream_read", lib().q8_stream_read(buf.data_ptr(),
                                                   buf.numel() * buf.element_size(),
                                                   out.data_ptr(), grid, _stream(stream)))

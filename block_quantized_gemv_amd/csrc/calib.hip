@@ -1,39 +1,48 @@
 // calib.hip -- the on-box reference for "achievable HBM read bandwidth": a
-// plain streaming read-reduce, against which the GEMV rows are judged.  It
-// reads `bytes` with 16-byte non-temporal loads (global_load_dwordx4, the
-// same instruction the GEMV streams its weights with), 8 in flight per lane,
-// grid-stride, and folds them into one word so the reads cannot be dropped.
+// plain streaming read, against which the GEMV rows are judged.  Each
+// workgroup of 256 threads reads one contiguous chunk of the buffer with
+// 16-byte non-temporal loads (global_load_dwordx4, the instruction the GEMV
+// streams its weights with), 4 in flight per lane; a contiguous chunk per
+// workgroup measured 7.0 TB/s on 2 GiB where a grid-stride sweep of the whole
+// buffer reached 6.0 TB/s (a workgroup's requests stay within few DRAM pages).
+// The workgroup's XOR of every word it read goes to out[blockIdx.x] with a
+// plain store, so no read can be dropped and the host can check that every
+// word was read exactly once; no atomics, which would serialise the end of
+// the kernel on one address.
 #include "q8_internal.h"
 
 namespace q8 {
 namespace {
 
-constexpr int kReadUnroll = 8;
+constexpr int kReadThreads = 256;
+constexpr int kReadUnroll = 4;
 
-__global__ __launch_bounds__(512) void read_reduce_kernel(const u32x4* __restrict__ p, int64_t n16,
-                                                          uint32_t* out) {
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+__global__ __launch_bounds__(kReadThreads) void read_reduce_kernel(const u32x4* __restrict__ p,
+                                                                   int64_t n16, int64_t chunk,
+                                                                   uint32_t* out) {
+  const int64_t b = (int64_t)blockIdx.x * chunk;
+  const int64_t e = b + chunk < n16 ? b + chunk : n16;
   uint32_t acc = 0;
-  int64_t i = tid;
-  for (; i + (kReadUnroll - 1) * stride < n16; i += kReadUnroll * stride) {
+  int64_t i = b + threadIdx.x;
+  for (; i + (kReadUnroll - 1) * kReadThreads < e; i += kReadUnroll * kReadThreads) {
     u32x4 v[kReadUnroll];
 #pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+    for (int u = 0; u < kReadUnroll; ++u)
+      v[u] = __builtin_nontemporal_load(p + i + u * kReadThreads);
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < e; i += kReadThreads) {
     const u32x4 v = __builtin_nontemporal_load(p + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
-  // one word per workgroup survives: the XOR of everything it read
-  __shared__ uint32_t s;
-  if (threadIdx.x == 0) s = 0;
+  // XOR over the wave, then over the workgroup's 4 waves
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc ^= __shfl_xor(acc, m, 64);
+  __shared__ uint32_t s[kReadThreads / 64];
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = acc;
   __syncthreads();
-  atomicXor(&s, acc);
-  __syncthreads();
-  if (threadIdx.x == 0) atomicXor(out, s);
+  if (threadIdx.x == 0) out[blockIdx.x] = s[0] ^ s[1] ^ s[2] ^ s[3];
 }
 
 }  // namespace
@@ -41,9 +50,11 @@ __global__ __launch_bounds__(512) void read_reduce_kernel(const u32x4* __restric
 int launch_read_reduce(const void* buf, int64_t bytes, uint32_t* out, int grid,
                        hipStream_t stream) {
   const int64_t n16 = bytes / 16;
-  if (n16 <= 0) return Q8_OK;
-  hipLaunchKernelGGL(read_reduce_kernel, dim3(grid), dim3(512), 0, stream,
-                     static_cast<const u32x4*>(buf), n16, out);
+  // chunk: a whole number of the workgroup's 256-load sweeps
+  const int64_t per = cdiv(n16, (int64_t)grid);
+  const int64_t chunk = cdiv(per, (int64_t)kReadThreads) * kReadThreads;
+  hipLaunchKernelGGL(read_reduce_kernel, dim3(grid), dim3(kReadThreads), 0, stream,
+                     static_cast<const u32x4*>(buf), n16, chunk, out);
   return hipGetLastError() == hipSuccess ? Q8_OK : Q8_ELAUNCH;
 }
 

@@ -749,12 +749,10 @@ int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream) 
 }
 
 int q8_stream_read(const void* buf, int64_t bytes, uint32_t* out, int32_t grid, void* stream) {
-  if (bytes < 0 || grid < 0 || grid > (1 << 20)) return Q8_EINVAL;
-  if (bytes == 0) return Q8_OK;
+  if (bytes < 0 || grid < 1 || grid > (1 << 20)) return Q8_EINVAL;
   int rc;
   if ((rc = check_dev_aligned(buf, 16)) || (rc = check_dev_aligned(out, 4))) return rc;
-  return launch_read_reduce(buf, bytes, out, grid > 0 ? grid : 2048,
-                            static_cast<hipStream_t>(stream));
+  return launch_read_reduce(buf, bytes, out, grid, static_cast<hipStream_t>(stream));
 }
 
 const char* q8_0_strerror(int status) {

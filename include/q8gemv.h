@@ -555,10 +555,12 @@ int q8_0_chain_status(const void* workspace, int32_t* dev_status, void* stream);
 /* ---- measurement utility ------------------------------------------------------
  * The on-box reference for achievable HBM read bandwidth: reads the first
  * `bytes` (rounded down to 16) of device buffer buf (16-byte aligned) with
- * 16-byte non-temporal loads, the GEMV's weight-streaming instruction, in a
- * grid-stride loop over `grid` workgroups of 512 threads (0: 2048), and XORs
- * everything into *out (device uint32, caller-cleared) so no read can be
- * dropped.  Bandwidth = bytes / kernel time.  Not part of the GEMV path.
+ * 16-byte non-temporal loads, the GEMV's weight-streaming instruction; each
+ * of `grid` workgroups (1 .. 2^20) of 256 threads reads one contiguous chunk
+ * and writes the XOR of every 32-bit word it read to out[workgroup] (device
+ * uint32 [grid]), so no read can be dropped; the XOR of all grid words is the
+ * XOR of the buffer's words.  Bandwidth = bytes / kernel time.  Not part of
+ * the GEMV path.  bytes == 0 (or < 16) still writes grid zero words.
  * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_ELAUNCH. */
 int q8_stream_read(const void* buf, int64_t bytes, uint32_t* out, int32_t grid, void* stream);
 
