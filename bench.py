@@ -507,8 +507,18 @@ def measure_rows(log, only=()):
             graph_rounds(scatter, nt), bs, copies=NSH)
         rec("a8", "C5 combine: 4 slots down 2048x1408 + shared 2048x5632, weighted", "M1",
             graph_rounds(combine, nt), bc, copies=NSH)
-        rec("a5-a8", "C5 MoE FFN token: router + scatter + combine", "M1",
+        rec("a5-a8", "C5 MoE FFN token: router + scatter + combine (3 launches)", "M1",
             graph_rounds(lambda t, s: (route(t, s), scatter(t, s), combine(t, s)), nt), bs + bc,
+            copies=NSH)
+        # the router fused into the scatter launch; the combine reads the ids
+        # and weights that launch publishes
+        route_scatter = lambda t, s: q.q8_0_moe_route_gemv(
+            gu, logits[t % T], S, x[t % T], h[t % T], mode_s, shared=sgu[t % NSH],
+            expert_ids=ids[t % T], slot_weights=w[t % T], workspace=ws1, stream=s)
+        rec("a5+a6", "C5 router fused into the scatter launch", "M1",
+            graph_rounds(route_scatter, nt), bs, copies=NSH)
+        rec("a5-a8", "C5 MoE FFN token: fused router + scatter, combine (2 launches)", "M1",
+            graph_rounds(lambda t, s: (route_scatter(t, s), combine(t, s)), nt), bs + bc,
             copies=NSH)
         del gu, dn, sgu, sdn
         torch.cuda.empty_cache()

@@ -41,7 +41,7 @@ EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv",
            "q8_0_chain_run", "q8_0_chain_read", "q8_0_chain_status", "q4k_packed_size",
            "q4k_repack", "q4k_gemv", "q5k_packed_size", "q5k_repack", "q5k_gemv",
            "q6k_packed_size", "q6k_repack", "q6k_gemv", "q8_0_gemv_noalloc",
-           "q8_stream_read")
+           "q8_stream_read", "q8_0_moe_route_gemv")
 
 
 class Q8Error(RuntimeError):
@@ -128,6 +128,8 @@ def lib() -> ctypes.CDLL:
         L.q8_0_argmax.argtypes = [P, I64, P, P, SZ, P]
         L.q8_0_route_topk.argtypes = [P, I32, I32, P, P, P]
         L.q8_0_moe_gemv.argtypes = [PW, P, P, P, P, I64, I64, I32, I32, PW, P, P, P, SZ, P]
+        L.q8_0_moe_route_gemv.argtypes = [PW, P, I32, P, P, P, P, I64, I64, I32, I32, PW, P, P,
+                                          SZ, P]
         L.q8_0_workspace_bytes.argtypes = [I32, I64, I64, I64, I64, I64, I32]
         L.q8_0_workspace_bytes.restype = SZ
         L.q8_0_gemv_plan.argtypes = [I64, I64, I64, I32, ctypes.POINTER(I32)]
@@ -686,6 +688,48 @@ def q8_0_moe_gemv(W_experts: PackedQ8, expert_ids: torch.Tensor, slot_weights, x
         dev_status.data_ptr() if dev_status is not None else None, wsp, wsb, _stream(stream))
     _check("q8_0_moe_gemv", rc)
     return y
+
+
+def q8_0_moe_route_gemv(W_experts: PackedQ8, logits: torch.Tensor, k: int, x: torch.Tensor,
+                        y: torch.Tensor, mode: int = Q8_MOE_SCATTER,
+                        shared: PackedQ8 | None = None, expert_ids: torch.Tensor | None = None,
+                        slot_weights: torch.Tensor | None = None,
+                        dev_status: torch.Tensor | None = None, workspace=None, stream=None):
+    """The router and the scatter (gate_up) launch of every slot in one launch;
+    see q8_0_moe_route_gemv in include/q8gemv.h.  Returns (y, expert_ids,
+    slot_weights), the last two written by the launch for the combine."""
+    if mode & ~Q8_MOE_SWIGLU != Q8_MOE_SCATTER:
+        raise ValueError("the fused router serves the scatter mode only")
+    half = 2 if mode & Q8_MOE_SWIGLU else 1
+    if x.numel() != W_experts.K or (shared is not None and shared.K != W_experts.K):
+        raise ValueError(f"scatter reads one x of K = {W_experts.K} entries (x has {x.numel()})")
+    _room(y, k * W_experts.M // half + (shared.M // half if shared is not None else 0), "y")
+    if expert_ids is not None:
+        _room(expert_ids, k, "expert_ids")
+    if slot_weights is not None:
+        _room(slot_weights, k, "slot_weights")
+    if dev_status is not None:
+        _room(dev_status, 1, "dev_status")
+    _need(logits, torch.float32, "logits")
+    _need(x, torch.float32, "x")
+    _need(y, torch.float32, "y")
+    if expert_ids is None:
+        expert_ids = torch.empty(k, dtype=torch.int32, device=x.device)
+    if slot_weights is None:
+        slot_weights = torch.empty(k, dtype=torch.float32, device=x.device)
+    _need(expert_ids, torch.int32, "expert_ids")
+    _need(slot_weights, torch.float32, "slot_weights")
+    M2 = shared.M if shared is not None else 0
+    K2 = shared.K if shared is not None else 0
+    wsp, wsb = _ws(workspace, q8_0_workspace_bytes(Q8_OP_MOE_SCATTER, W_experts.M, W_experts.K,
+                                                   k, M2, K2, mode), x.device)
+    rc = lib().q8_0_moe_route_gemv(
+        ctypes.byref(W_experts.desc), logits.data_ptr(), logits.numel(), expert_ids.data_ptr(),
+        slot_weights.data_ptr(), x.data_ptr(), y.data_ptr(), W_experts.M, W_experts.K, k, mode,
+        ctypes.byref(shared.desc) if shared is not None else None,
+        dev_status.data_ptr() if dev_status is not None else None, wsp, wsb, _stream(stream))
+    _check("q8_0_moe_route_gemv", rc)
+    return y, expert_ids, slot_weights
 
 
 # ---------------------------------------------------------------------------

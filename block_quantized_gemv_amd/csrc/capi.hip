@@ -585,6 +585,40 @@ int q8_0_moe_gemv(const q8_0_weights* W_experts, const int32_t* expert_ids,
   return launch_problems(pd, np, 1, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
+int q8_0_moe_route_gemv(const q8_0_weights* W_experts, const float* router_logits, int32_t E,
+                        int32_t* expert_ids, float* slot_weights, const float* x, float* y,
+                        int64_t M, int64_t K, int32_t n_slots, int32_t mode,
+                        const q8_0_weights* shared, int32_t* dev_status, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if ((mode & ~Q8_MOE_SWIGLU) != Q8_MOE_SCATTER) return Q8_EINVAL;
+  int rc = check_weights_shape(W_experts, M, K, true);
+  if (rc) return rc;
+  if (shared && (rc = check_weights_shape(shared, shared->M, K, false))) return rc;
+  if (!router_logits || !expert_ids || !slot_weights || !x || !y) return Q8_ENULL;
+  if (E < 1 || E > 1024 || E > W_experts->n_mats || n_slots < 1 || n_slots > E ||
+      n_slots > Q8_MAX_SLOTS)
+    return Q8_EINVAL;
+  ProbDesc pd[kMaxProb];
+  int np = 0;
+  // expert_ids marks the routed segments; the kernel writes it, never reads it
+  if ((rc = build_moe(W_experts, expert_ids, nullptr, x, y, M, K, n_slots, mode, shared, nullptr,
+                      dev_status, pd, &np)))
+    return rc;
+  if ((rc = check_dev_aligned(router_logits, 4)) || (rc = check_dev_aligned(expert_ids, 4)) ||
+      (rc = check_dev_aligned(slot_weights, 4)))
+    return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M == 0) return launch_route(router_logits, E, n_slots, expert_ids, slot_weights, st);
+  if ((rc = check_weights_ptrs(W_experts)) || (rc = check_dev_aligned(x, 4)) ||
+      (rc = check_dev_aligned(y, 4)))
+    return rc;
+  if (shared && (rc = check_weights_ptrs(shared))) return rc;
+  if (dev_status && (rc = check_dev_aligned(dev_status, 4))) return rc;
+  if (workspace && (rc = check_dev(workspace))) return rc;
+  const RouteParams rp = {router_logits, E, n_slots, expert_ids, slot_weights};
+  return launch_problems(pd, np, 1, workspace, workspace_bytes, st, &rp);
+}
+
 size_t q8_0_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int64_t M2, int64_t K2,
                             int32_t flags) {
   Plan plan;

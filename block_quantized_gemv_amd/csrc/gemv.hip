@@ -927,6 +927,15 @@ __global__ __launch_bounds__(64 * max_waves_for(N, MODE >= 3)) void gemv_kernel(
     }
   }
 
+  // fused router: workgroup 0 also publishes every slot's id and weight for
+  // the launch that combines the slots
+  if (!ONE && p.route.logits && g == 0 && wave == 0) {
+    float sel_v[Q8_MAX_SLOTS];
+    int sel_i[Q8_MAX_SLOTS];
+    route_topk_wave(p.route.logits, p.route.E, p.route.k, lane, sel_v, sel_i);
+    if (lane == 0) route_store(sel_v, sel_i, p.route.k, p.route.ids_out, p.route.w_out);
+  }
+
   float acc[N];
 #pragma unroll
   for (int n = 0; n < N; ++n) acc[n] = 0.f;
@@ -944,7 +953,11 @@ __global__ __launch_bounds__(64 * max_waves_for(N, MODE >= 3)) void gemv_kernel(
     int e = 0;
     bool ok = true;
     if (s.eid) {
-      e = __builtin_amdgcn_readfirstlane(s.eid[s.slot]);
+      // the slot's expert: picked here from the router logits when the router
+      // is fused into this launch, else read from the id array
+      e = __builtin_amdgcn_readfirstlane(
+          p.route.logits ? route_pick_wave(p.route.logits, p.route.E, s.slot, lane)
+                         : s.eid[s.slot]);
       ok = e >= 0 && e < s.n_mats;
     }
     if (ok) {
@@ -1405,7 +1418,7 @@ static hipError_t launch_n(const GemvParams& gp, int wgs, hipStream_t stream) {
 }
 
 int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws_bytes,
-                    hipStream_t stream) {
+                    hipStream_t stream, const RouteParams* route) {
   Plan plan;
   int rc = plan_problems(probs, nprob, N, &plan);
   if (rc) return rc;
@@ -1481,6 +1494,7 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
   }
   gp.total_wg = wg;
   gp.W = plan.W;
+  if (route) gp.route = *route;  // (memset above: no router otherwise)
   if (wg <= 0) return Q8_OK;
   hipError_t e;
   switch (N) {

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -101,12 +102,23 @@ struct Prob {
   int32_t* dev_status;
 };
 
+// Router fused into a routed-expert launch: every wave with a routed segment
+// picks its slot's expert from the logits itself, and workgroup 0 also writes
+// the ids and renormalised weights of all k slots for the next launch.
+struct RouteParams {
+  const float* logits;   // [E], or nullptr: ids are read from Seg::eid
+  int32_t E, k;
+  int32_t* ids_out;      // [k]
+  float* w_out;          // [k]
+};
+
 struct GemvParams {
   Seg seg[kMaxSeg];
   Prob prob[kMaxProb];
   int32_t nprob;
   int32_t total_wg;
   int32_t W;             // waves per workgroup
+  RouteParams route;
 };
 
 // Host-side launcher shared by the C entry points (gemv.hip).
@@ -156,7 +168,7 @@ struct Plan {
 
 int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan);
 int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws_bytes,
-                    hipStream_t stream);
+                    hipStream_t stream, const RouteParams* route = nullptr);
 
 // argmax / router / repack launchers (select.hip, repack.hip)
 size_t argmax_ws_bytes(int64_t n);
@@ -209,6 +221,104 @@ __device__ __forceinline__ T ld_dev(const T* p) {
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ unsigned ticket_add(uint32_t* t) {
   return __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- top-k routing, one wave ------------------------------------------------
+// The k largest of E <= 1024 router logits in descending order, ties to the
+// lower index (lane l holds logits l, l + 64, ...); every lane ends with the
+// same picks.  Exact comparisons, so every caller selects identically.
+__device__ __forceinline__ void route_better(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+__device__ __forceinline__ void route_topk_wave(const float* logits, int E, int k, int lane,
+                                                float* sel_v, int* sel_i) {
+  float lv[16];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    lv[i] = -INFINITY;
+    if (64 * i < E) {  // uniform: the loads of one row of 64 are issued together
+      const int e = lane + 64 * i;
+      const float t = logits[e < E ? e : E - 1];
+      lv[i] = e < E ? t : -INFINITY;
+    }
+  }
+  // (unrolled over the slot bound so the picks stay in registers)
+#pragma unroll
+  for (int s = 0; s < Q8_MAX_SLOTS; ++s) {
+    sel_v[s] = -INFINITY;
+    sel_i[s] = 0x7fffffff;
+    if (s < k) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && !(taken >> i & 1u)) route_better(bv, bi, lv[i], e);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1)
+        route_better(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
+      sel_v[s] = bv;
+      sel_i[s] = bi;
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    }
+  }
+}
+// Expert of slot s alone (the (s+1)-th largest logit), same selection.
+__device__ __forceinline__ int route_pick_wave(const float* logits, int E, int s_target,
+                                               int lane) {
+  float lv[16];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    lv[i] = -INFINITY;
+    if (64 * i < E) {
+      const int e = lane + 64 * i;
+      const float t = logits[e < E ? e : E - 1];
+      lv[i] = e < E ? t : -INFINITY;
+    }
+  }
+  int pick = 0x7fffffff;
+  for (int s = 0; s <= s_target; ++s) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !(taken >> i & 1u)) route_better(bv, bi, lv[i], e);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+      route_better(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
+    pick = bi;
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+  }
+  return pick;
+}
+// Renormalised softmax weight of pick s: exp(l_s - l_0) / sum_t exp(l_t - l_0),
+// the sum in pick order.
+__device__ __forceinline__ float route_denominator(const float* sel_v, int k) {
+  float den = 0.f;
+#pragma unroll
+  for (int t = 0; t < Q8_MAX_SLOTS; ++t)
+    if (t < k) den += expf(sel_v[t] - sel_v[0]);
+  return den;
+}
+// Writes ids[s] and the renormalised weight w[s] of every pick s < k.
+__device__ __forceinline__ void route_store(const float* sel_v, const int* sel_i, int k,
+                                            int32_t* ids, float* w) {
+  const float den = route_denominator(sel_v, k);
+#pragma unroll
+  for (int s = 0; s < Q8_MAX_SLOTS; ++s) {
+    if (s < k) {
+      ids[s] = sel_i[s];
+      w[s] = expf(sel_v[s] - sel_v[0]) / den;
+    }
+  }
 }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

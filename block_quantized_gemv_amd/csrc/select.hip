@@ -130,37 +130,10 @@ int launch_argmax(const float* v, int64_t n, int32_t* out, void* ws, size_t ws_b
 // One wave; lane l holds logits l, l+64, ... (E <= 1024).
 __global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ logits, int E, int k,
                                                    int32_t* ids, float* w) {
-  const int lane = threadIdx.x;
-  float lv[16];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = lane + 64 * i;
-    lv[i] = e < E ? logits[e] : -INFINITY;
-  }
   float sel_v[Q8_MAX_SLOTS];
   int sel_i[Q8_MAX_SLOTS];
-  for (int s = 0; s < k; ++s) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !(taken >> i & 1u)) better(bv, bi, lv[i], e);
-    }
-    wave_best(bv, bi);
-    sel_v[s] = bv;
-    sel_i[s] = bi;
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-  }
-  if (lane == 0) {
-    float den = 0.f;
-    for (int s = 0; s < k; ++s) den += expf(sel_v[s] - sel_v[0]);
-    for (int s = 0; s < k; ++s) {
-      ids[s] = sel_i[s];
-      w[s] = expf(sel_v[s] - sel_v[0]) / den;
-    }
-  }
+  route_topk_wave(logits, E, k, threadIdx.x, sel_v, sel_i);
+  if (threadIdx.x == 0) route_store(sel_v, sel_i, k, ids, w);
 }
 
 int launch_route(const float* logits, int32_t E, int32_t k, int32_t* ids, float* w,

@@ -422,6 +422,27 @@ int q8_0_moe_gemv(const q8_0_weights* W_experts, const int32_t* expert_ids,
                   const float* shared_gate, int32_t* dev_status, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* ---- MoE router fused into the gate_up launch ----------------------------------
+ * The router of q8_0_route_topk and the Q8_MOE_SCATTER launch of
+ * q8_0_moe_gemv in one launch (#144 PR: the router may share the routed-
+ * expert launch, fewer launches per layer): every wave that computes a routed
+ * slot picks its own expert from router_logits (device fp32 [E]), with the
+ * same selection rule, so no kernel boundary separates routing from the
+ * experts' weights.  The launch also writes expert_ids (device int32
+ * [n_slots]) and slot_weights (device fp32 [n_slots]) exactly as
+ * q8_0_route_topk would, for the Q8_MOE_COMBINE call that follows.
+ * mode: Q8_MOE_SCATTER, optionally | Q8_MOE_SWIGLU; x, y, M, K, shared,
+ * dev_status and the workspace as in q8_0_moe_gemv (workspace size: op
+ * Q8_OP_MOE_SCATTER).  1 <= n_slots <= min(E, Q8_MAX_SLOTS), E <= 1024 and
+ * E <= W_experts->n_mats.  With M == 0 only the ids and weights are written.
+ * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_EWORKSPACE,
+ * Q8_ELAUNCH. */
+int q8_0_moe_route_gemv(const q8_0_weights* W_experts, const float* router_logits, int32_t E,
+                        int32_t* expert_ids, float* slot_weights, const float* x, float* y,
+                        int64_t M, int64_t K, int32_t n_slots, int32_t mode,
+                        const q8_0_weights* shared, int32_t* dev_status, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* ---- persistent decode chain --------------------------------------------------
  * One launch runs a whole decode step of a Qwen2-style decoder at position 0,
  * the per-layer steps of the fused GEMVs above in the decoder block order of

@@ -187,3 +187,75 @@ def test_moe_repeatable():
         h = moe.scatter(ids, xd, True)
         assert torch.equal(h, h0)
         assert torch.equal(moe.combine(ids, w, h, lamd), y0)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_moe_router_fused_into_scatter(layout, swiglu):
+    """q8_0_moe_route_gemv: the router fused into the gate_up launch picks the
+    oracle's experts (bit-exact, planted ties included), publishes the same
+    ids and weights as q8_0_route_topk, and its products equal the unfused
+    route + scatter pair bitwise (same kernel, same plan)."""
+    moe = MoE(cfg=52, E=60, H=256, I=128, Ish=192, layout=layout)
+    mode = q.Q8_MOE_SCATTER | (q.Q8_MOE_SWIGLU if swiglu else 0)
+    Mo = moe.I if swiglu else 2 * moe.I
+    Msh = moe.Ish if swiglu else 2 * moe.Ish
+    for t in range(12):
+        x, lg, _ = moe.inputs(t)
+        if t % 3 == 0:  # ties at the top and across the k-th place
+            lg[np.random.default_rng(t).integers(0, moe.E, 6)] = lg.max()
+        xd, lgd = to_dev(x), to_dev(lg)
+        y_f = torch.full((moe.S * Mo + Msh,), np.nan, dtype=torch.float32, device=DEV)
+        _, ids_f, w_f = q.q8_0_moe_route_gemv(moe.p_gu, lgd, moe.S, xd, y_f, mode,
+                                              shared=moe.p_sgu)
+        ids, w = q.q8_0_route_topk(lgd, moe.S)
+        y = moe.scatter(ids, xd, swiglu)
+        ids_r, w_r = oracle.route_topk(lg, moe.S)
+        assert np.array_equal(host(ids_f), ids_r), t
+        assert np.array_equal(host(ids_f), host(ids)), t
+        assert np.array_equal(host(w_f), host(w)), t
+        assert np.all(np.abs(host(w_f).astype(np.float64) - w_r) <= 1e-6), t
+        assert np.array_equal(host(y_f), host(y)), t
+
+
+def test_moe_router_fused_qwen15_token():
+    """The fused router at the Qwen1.5-MoE shapes (60 experts, top-4, shared
+    expert), followed by the combine on its published ids and weights, equals
+    the three-launch token bitwise."""
+    c = W.C5
+    moe = MoE(cfg=c["cfg"], E=c["n_experts"], H=c["hidden"], I=c["inter"], Ish=c["shared_inter"],
+              S=c["top_k"])
+    for t in range(3):
+        x, lg, lam = moe.inputs(t)
+        xd, lgd = to_dev(x), to_dev(lg)
+        lamd = torch.tensor([lam], dtype=torch.float32, device=DEV)
+        h_f = torch.full((moe.S * moe.I + moe.Ish,), np.nan, dtype=torch.float32, device=DEV)
+        _, ids_f, w_f = q.q8_0_moe_route_gemv(moe.p_gu, lgd, moe.S, xd, h_f,
+                                              q.Q8_MOE_SCATTER | q.Q8_MOE_SWIGLU,
+                                              shared=moe.p_sgu)
+        y_f = moe.combine(ids_f, w_f, h_f, lamd)
+        ids, w = q.q8_0_route_topk(lgd, moe.S)
+        h = moe.scatter(ids, xd, swiglu=True)
+        y = moe.combine(ids, w, h, lamd)
+        assert np.array_equal(host(h_f), host(h)), t
+        assert np.array_equal(host(y_f), host(y)), t
+
+
+def test_moe_router_fused_invalid_arguments():
+    moe = MoE(cfg=53, E=8, H=256, I=128, Ish=192)
+    lib = q.lib()
+    lg = to_dev(np.zeros(8, dtype=np.float32))
+    x = to_dev(np.zeros(256, dtype=np.float32))
+    y = torch.zeros(4 * 256 + 384, dtype=torch.float32, device=DEV)
+    ids = torch.zeros(8, dtype=torch.int32, device=DEV)
+    w = torch.zeros(8, dtype=torch.float32, device=DEV)
+    import ctypes
+    call = lambda E, k, mode: lib.q8_0_moe_route_gemv(
+        ctypes.byref(moe.p_gu.desc), lg.data_ptr(), E, ids.data_ptr(), w.data_ptr(), x.data_ptr(),
+        y.data_ptr(), 256, 256, k, mode, None, None, None, 0, None)
+    assert call(8, 9, q.Q8_MOE_SCATTER) == q.Q8_EINVAL      # k > E
+    assert call(9, 4, q.Q8_MOE_SCATTER) == q.Q8_EINVAL      # E > experts stored
+    assert call(8, 0, q.Q8_MOE_SCATTER) == q.Q8_EINVAL
+    assert call(8, 4, q.Q8_MOE_COMBINE) == q.Q8_EINVAL      # scatter only
+    with pytest.raises(ValueError):
+        q.q8_0_moe_route_gemv(moe.p_gu, lg, 4, x, y, q.Q8_MOE_COMBINE)

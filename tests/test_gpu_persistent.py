@@ -35,7 +35,7 @@ def outputs(pc: q.PersistentChain, cfg: ChainConfig):
     return logits, tok, h_out
 
 
-def check_stagewise(aos, lm, pc, h0, cfg: ChainConfig, logits, tok, h_out, lm_rows=3000):
+def check_stagewise(aos, lm, pc, h0, cfg: ChainConfig, logits, tok, h_out, lm_rows=None):
     n_layers = len(aos)
     H, I = cfg.hidden, cfg.intermediate
     voff = (cfg.n_heads + cfg.n_kv_heads) * cfg.head_dim
@@ -70,8 +70,10 @@ def check_stagewise(aos, lm, pc, h0, cfg: ChainConfig, logits, tok, h_out, lm_ro
     lg = host(logits)
     pick = int(host(tok)[0])
     assert pick == int(np.argmax(lg)), "next_token is the lowest index of the largest logit"
-    rows = np.unique(np.concatenate([np.random.default_rng(0).integers(0, cfg.vocab, lm_rows),
-                                     [0, cfg.vocab - 1, pick]]))
+    # every logit unless a sample size is given
+    rows = (np.arange(cfg.vocab) if lm_rows is None else
+            np.unique(np.concatenate([np.random.default_rng(0).integers(0, cfg.vocab, lm_rows),
+                                      [0, cfg.vocab - 1, pick]])))
     yr, S = oracle.gemv(lm.aos()[rows], oracle.rmsnorm(hin, cfg.eps))
     assert np.all(np.abs(lg[rows].astype(np.float64) - yr) <= normed_bound(S, yr)), "lm_head"
 
