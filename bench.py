@@ -31,7 +31,7 @@ Prints one JSON line:
                BLAS-backed numpy matvec, on a bounded sample
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--path persistent|graph]
-                       [--only SUBSTR[,SUBSTR...]] [--no-rows] [--no-cpu-baseline]
+                       [--only SUBSTR[,SUBSTR...]] [--no-rows] [--no-cpu-baseline] [--stages RUNS]
 """
 from __future__ import annotations
 
@@ -74,6 +74,10 @@ def parse():
     ap.add_argument("--only", default="",
                     help="comma-separated substrings: run only the rows whose description "
                          "contains one of them (no decode step, no CPU baseline); for profiling")
+    ap.add_argument("--stages", type=int, default=0, metavar="RUNS",
+                    help="only time the persistent step with stage timestamps "
+                         "(q8_0_chain_run_stamped) over RUNS steps and print the per-stage "
+                         "breakdown of a layer")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -653,6 +657,69 @@ def context_rows(cfg, layers, lm_p, h0, steps, stream, log):
     return rows
 
 
+STAGE_POINTS = ("A start", "value/query/key task stored", "B start", "wo task stored",
+                "C start", "last gate-up task stored (first wave)",
+                "first gate-up task stored (last wave)", "D start", "down partial stored",
+                "8 partials received", "h2 rows stored", "next h staged")
+
+
+def stage_breakdown(cfg, layers, lm_p, h0, runs, log):
+    """The persistent step with stage timestamps: for every stamped point of a
+    layer, the median over workgroups of its time after that layer's stage-A
+    barrier, averaged over the middle layers and over `runs` steps; plus the
+    LM head's share and the stamped step time (HIP events)."""
+    import torch
+    import block_quantized_gemv_amd as q
+    pc = q.PersistentChain(layers, lm_p, cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
+                           cfg.intermediate, cfg.eps)
+    dev = h0.device
+    G, Wd = pc.plan.grid, q.Q8_CHAIN_STAMP_WORDS
+    LP, KP = q.Q8_CHAIN_STAMP_LAYERS, q.Q8_CHAIN_STAMP_POINTS
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
+    tok = torch.empty(1, dtype=torch.int32, device=dev)
+    stamps = torch.zeros(G * Wd, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    plain, _ = time_launches(lambda: pc.run(h0, logits, tok, stream=stream), 50, 10, stream)
+    stamped, _ = time_launches(lambda: pc.run(h0, logits, tok, stream=stream, stamps=stamps), 50,
+                               10, stream)
+    L = min(len(layers), LP)
+    mids = range(1, max(2, L - 1))
+    acc = np.zeros((runs, KP))
+    lm = np.zeros((runs, 3))
+    for r in range(runs):
+        stamps.zero_()
+        pc.run(h0, logits, tok, stream=stream, stamps=stamps)
+        torch.cuda.synchronize()
+        t = stamps.cpu().numpy().reshape(G, Wd).astype(np.float64) * 0.01  # us
+        lay = t[:, :LP * KP].reshape(G, LP, KP)
+        for k in range(KP):
+            vals = []
+            for l in mids:
+                base = lay[:, l, 0]
+                have = lay[:, l, k] > 0
+                vals.append(np.median(lay[have, l, k] - base[have]) if have.any() else np.nan)
+            acc[r, k] = np.nanmean(vals)
+        kern = t[:, LP * KP:]
+        lm[r] = [np.median(kern[:, 1] - kern[:, 0]), np.median(kern[:, 3] - kern[:, 1]),
+                 np.median(kern[:, 1] - lay[:, L - 1, 0])]
+    if int(tok.cpu()[0]) < 0 or pc.status() != 0:
+        raise RuntimeError("stamped step reported an invalid token")
+    med = np.median(acc, axis=0)
+    period = np.median([np.median(lay[:, l + 1, 0] - lay[:, l, 0]) for l in mids])
+    out = {"step_us": round(plain * 1e6, 2), "stamped_step_us": round(stamped * 1e6, 2),
+           "layer_period_us": round(float(period), 3),
+           "points_us_after_A": {STAGE_POINTS[k]: round(float(med[k]), 3) for k in range(KP)},
+           "layers_us": round(float(np.median(lm[:, 0])), 2),
+           "lm_head_us": round(float(np.median(lm[:, 1])), 2),
+           "last_layer_to_lm_us": round(float(np.median(lm[:, 2])), 2),
+           "layers_averaged": f"{mids.start}..{mids.stop - 1}", "runs": runs}
+    log(f"stamped step {out['stamped_step_us']} us (plain {out['step_us']} us); "
+        f"layer period {out['layer_period_us']} us")
+    for name, v in out["points_us_after_A"].items():
+        log(f"  {v:7.2f} us  {name}")
+    return out
+
+
 def main():
     args = parse()
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
@@ -677,6 +744,10 @@ def main():
         print(json.dumps({"rows": rows}), flush=True)
         return
     cfg, layers, lm_p, h0, step_bytes, sample_aos = build_weights(args.layers, log)
+    if args.stages:
+        print(json.dumps({"stages": stage_breakdown(cfg, layers, lm_p, h0, args.stages, log)}),
+              flush=True)
+        return
     stream = torch.cuda.current_stream()
     timer = time_persistent if args.path == "persistent" else time_graph
     sec, rounds, launches, kernel, tok = timer(cfg, layers, lm_p, h0, args.steps, args.warmup,

@@ -33,6 +33,8 @@ Q8_OP_Q5K_GEMV = 9
 Q8_LAYOUT_ROWS, Q8_LAYOUT_GATE_UP_PAIRS = 0, 1
 Q8_CHAIN_COHERENT = 1
 Q8_CHAIN_QKV, Q8_CHAIN_H_ATTN, Q8_CHAIN_SWIGLU, Q8_CHAIN_H_OUT = 0, 1, 2, 3
+Q8_CHAIN_STAMP_LAYERS, Q8_CHAIN_STAMP_POINTS, Q8_CHAIN_STAMP_KERNEL = 32, 12, 4
+Q8_CHAIN_STAMP_WORDS = Q8_CHAIN_STAMP_LAYERS * Q8_CHAIN_STAMP_POINTS + Q8_CHAIN_STAMP_KERNEL
 
 EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv", "q8_0_gemv_fused",
            "q8_0_gemv_argmax", "q8_0_quantize_act", "q8_0_gemv_q8act", "q8_0_argmax",
@@ -41,7 +43,7 @@ EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv",
            "q8_0_chain_run", "q8_0_chain_read", "q8_0_chain_status", "q4k_packed_size",
            "q4k_repack", "q4k_gemv", "q5k_packed_size", "q5k_repack", "q5k_gemv",
            "q6k_packed_size", "q6k_repack", "q6k_gemv", "q8_0_gemv_noalloc",
-           "q8_stream_read", "q8_0_moe_route_gemv")
+           "q8_stream_read", "q8_0_moe_route_gemv", "q8_0_chain_run_stamped")
 
 
 class Q8Error(RuntimeError):
@@ -141,6 +143,7 @@ def lib() -> ctypes.CDLL:
         L.q8_0_chain_workspace_bytes.restype = SZ
         L.q8_0_chain_prepare.argtypes = [PD, P, SZ, PP, P]
         L.q8_0_chain_run.argtypes = [PP, P, P, P, P, P, P]
+        L.q8_0_chain_run_stamped.argtypes = [PP, P, P, P, P, P, P, P]
         L.q8_0_chain_read.argtypes = [PP, P, I32, I32, P, P]
         L.q8_0_chain_status.argtypes = [P, P, P]
         _lib = L
@@ -770,10 +773,15 @@ class PersistentChain:
 
     def run(self, h_in: torch.Tensor, logits: torch.Tensor | None = None,
             next_token: torch.Tensor | None = None, h_out: torch.Tensor | None = None,
-            stream=None, check: bool = False) -> None:
+            stream=None, check: bool = False, stamps: torch.Tensor | None = None) -> None:
         """One decode step.  With check=True the call waits for the step and
         raises ChainStepError if it was marked invalid (next_token == -1: a
-        wait for another workgroup's data expired)."""
+        wait for another workgroup's data expired).  With stamps (device
+        int64 [grid * Q8_CHAIN_STAMP_WORDS]) the step also records its stage
+        timestamps (q8_0_chain_run_stamped)."""
+        if stamps is not None:
+            _need(stamps, torch.int64, "stamps")
+            _room(stamps, self.plan.grid * Q8_CHAIN_STAMP_WORDS, "stamps")
         _need(h_in, torch.float32, "h_in")
         if h_in.numel() != self.hidden:
             raise ValueError(f"h_in has {h_in.numel()} entries, expected {self.hidden}")
@@ -792,9 +800,17 @@ class PersistentChain:
             if t is not None:
                 _need(t, dt, name)
         ptr = lambda t: t.data_ptr() if t is not None else None
-        _check("q8_0_chain_run",
-               lib().q8_0_chain_run(ctypes.byref(self.plan), self.ws.data_ptr(), h_in.data_ptr(),
-                                    ptr(h_out), ptr(logits), ptr(next_token), _stream(stream)))
+        if stamps is None:
+            _check("q8_0_chain_run",
+                   lib().q8_0_chain_run(ctypes.byref(self.plan), self.ws.data_ptr(),
+                                        h_in.data_ptr(), ptr(h_out), ptr(logits),
+                                        ptr(next_token), _stream(stream)))
+        else:
+            _check("q8_0_chain_run_stamped",
+                   lib().q8_0_chain_run_stamped(ctypes.byref(self.plan), self.ws.data_ptr(),
+                                                h_in.data_ptr(), ptr(h_out), ptr(logits),
+                                                ptr(next_token), stamps.data_ptr(),
+                                                _stream(stream)))
         if check:
             s = stream if stream is not None else torch.cuda.current_stream()
             s.synchronize()

@@ -761,7 +761,25 @@ int q8_0_chain_run(const q8_0_chain_plan* plan, void* workspace, const float* h_
     if ((rc = check_dev_aligned(logits, 4))) return rc;
     if ((rc = check_dev_aligned(next_token, 4))) return rc;
   }
-  return q8::chain_run(plan, workspace, h_in, h_out, logits, next_token, (hipStream_t)stream);
+  return q8::chain_run(plan, workspace, h_in, h_out, logits, next_token, nullptr,
+                       (hipStream_t)stream);
+}
+
+int q8_0_chain_run_stamped(const q8_0_chain_plan* plan, void* workspace, const float* h_in,
+                           float* h_out, float* logits, int32_t* next_token, int64_t* stamps,
+                           void* stream) {
+  if (!plan || !stamps) return Q8_ENULL;
+  if (!plan_ok(plan)) return Q8_EINVAL;
+  int rc = check_dev_aligned(workspace, 256);
+  if (rc) return rc;
+  if ((rc = check_dev_aligned(h_in, 4)) || (rc = check_dev_aligned(stamps, 8))) return rc;
+  if (h_out && (rc = check_dev_aligned(h_out, 4))) return rc;
+  if (plan->vocab > 0) {
+    if ((rc = check_dev_aligned(logits, 4))) return rc;
+    if ((rc = check_dev_aligned(next_token, 4))) return rc;
+  }
+  return q8::chain_run(plan, workspace, h_in, h_out, logits, next_token, stamps,
+                       (hipStream_t)stream);
 }
 
 int q8_0_chain_read(const q8_0_chain_plan* plan, const void* workspace, int32_t layer,

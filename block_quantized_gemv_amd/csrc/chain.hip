@@ -93,6 +93,13 @@ constexpr int kHdrBytes = 256;
 constexpr uint32_t kDefaultSpin = 1u << 16;
 constexpr int kAuxDev = 16;        // cache policy sc1: device scope
 constexpr int kMaxTw = 12;         // wo/down tasks of one workgroup (<= kXW)
+// Optional stage timestamps (q8_0_chain_run_stamped): per workgroup,
+// Q8_CHAIN_STAMP_POINTS points of each of the first Q8_CHAIN_STAMP_LAYERS
+// layers, then Q8_CHAIN_STAMP_KERNEL points of the whole step.
+constexpr int kStampL = Q8_CHAIN_STAMP_LAYERS;
+constexpr int kStampP = Q8_CHAIN_STAMP_POINTS;
+constexpr int kStampK = Q8_CHAIN_STAMP_KERNEL;
+constexpr int kStampWords = kStampL * kStampP + kStampK;
 
 enum { ST_QKV = 0, ST_WO = 1, ST_GU = 2, ST_DN = 3 };
 
@@ -122,6 +129,7 @@ struct ChainArgs {
   int64_t am_off;         // argmax partials: [kMaxGrid] (fp32 value, int32 index)
   int64_t ws_bytes;
   ChainMat lm;
+  int64_t* stamps;        // [G][kStampWords] s_memrealtime ticks, or nullptr
 };
 
 struct Hdr {  // first 256 bytes of the workspace
@@ -415,12 +423,16 @@ __device__ __forceinline__ void span(int n, int parts, int i, int& lo, int& hi) 
   hi = (int)((int64_t)n * (i + 1) / parts);
 }
 
+// kStamp: the q8_0_chain_run_stamped instance; the plain instance has no
+// stamp code at all (its presence alone cost 2 % of the step).
+template <bool kStamp>
 __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   extern __shared__ __attribute__((aligned(16))) float lds[];
   __shared__ float s_ss[2][kPW];  // poll waves' sums of squares: [0] h (stage A), [1] h1 (stage C)
   __shared__ float s_cv[kCW];
   __shared__ int s_ci[kCW];
   __shared__ int s_last;
+  __shared__ long long s_st[kStamp ? kStampWords : 1];
 
   uint8_t* const ws = P.ws;
   Hdr* hdr = reinterpret_cast<Hdr*>(ws);
@@ -435,6 +447,17 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   const bool coherent = (P.flags & Q8_CHAIN_COHERENT) != 0;
   uint32_t* const status = &hdr->err;
   bool failed = false;
+  // stage timestamps: uniform branch, nothing when stamps == nullptr
+  constexpr bool stamping = kStamp;
+  auto stamp = [&](int slot) { s_st[slot] = (long long)__builtin_amdgcn_s_memrealtime(); };
+  auto stamp_l = [&](int l, int k) {
+    if (l < kStampL) stamp(l * kStampP + k);
+  };
+  if (stamping) {
+    for (int i = threadIdx.x; i < kStampWords; i += kCT) s_st[i] = 0;
+    __syncthreads();
+    if (threadIdx.x == 0) stamp(kStampL * kStampP + 0);
+  }
 
   uint32_t step = ld_dev(&hdr->step) + 1u;
   if (step == 0u) step = 1u;
@@ -518,6 +541,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   for (int l = 0; l < L; ++l) {
     // ================= stage A: value rows (and query/key rows) ===============
     __syncthreads();
+    if (stamping && threadIdx.x == 0) stamp_l(l, 0);
     if (!poller) {
       if (hasD && l > 0) loadD(l);  // slot 0 of the bottom waves is free since D(l - 1)
       if (hasA) {
@@ -534,6 +558,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
             st_tag<0>(rs, lrec(P.o_qkv, l) + (int64_t)row * 8, y, step);
           }
         }
+        if (stamping && lane == 0 && ta == 0) stamp_l(l, 1);
       }
     } else {
       // the value vector of this XCD -> the position-0 attention output: query
@@ -551,6 +576,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
     }
     // ================= stage B: h1 = h + Wo attn (all of h1 on every XCD) =====
     __syncthreads();
+    if (stamping && threadIdx.x == 0) stamp_l(l, 2);
     if (!poller) {
       if (hasA && l + 1 < L) loadA(l + 1);
       if (hasB) {
@@ -561,6 +587,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
           h1s[4 * cw + lane] = h1;
           st_tag_local(rs, lrec(P.o_h1, l) + ((int64_t)x * P.gh + row) * 8, h1, step, coherent);
         }
+        if (stamping && lane == 0 && cw == 0) stamp_l(l, 3);
       }
     } else {
       float ss = 0.f;
@@ -578,6 +605,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
     }
     // ================= stage C: this XCD's slice of s = swiglu(gate, up) ======
     __syncthreads();
+    if (stamping && threadIdx.x == 0) stamp_l(l, 4);
     if (!poller) {
       if (hasC) {
         const float c = rms_scale(s_ss[1], H, P.eps);
@@ -589,6 +617,8 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
           st_tag_local(rs, lrec(P.o_s, l) + (int64_t)o * 8, y / (1.0f + expf(-y)) * up, step,
                        coherent);
         }
+        if (stamping && lane == 0 && ta == 0) stamp_l(l, 5);
+        if (stamping && lane == 0 && ta == tc - 1) stamp_l(l, 6);
       }
       if (hasB && l + 1 < L) loadB(l + 1);
     } else {
@@ -603,6 +633,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
     }
     // ================= stage D: this XCD's split-K partial of down ============
     __syncthreads();
+    if (stamping && threadIdx.x == 0) stamp_l(l, 7);
     if (!poller) {
       if (hasD) {
         const float y = task_dot(s0, cslice, xb1, lane);
@@ -610,6 +641,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
           const int row = 4 * (w0 + cw) + lane;
           st_tag<kAuxDev>(rs, lrec(P.o_p, l) + ((int64_t)x * P.gh + row) * 8, y, step);
         }
+        if (stamping && lane == 0 && cw == 0) stamp_l(l, 8);
       }
       if (hasC && l + 1 < L) loadC(l + 1);
     } else {
@@ -637,6 +669,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
             poll_rec<3>(rs, nsl, 64, step, lane, P.spin, failed, status, addr, put);
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's partials are in LDS
+        if (stamping && lane == 0) stamp_l(l, 9);
         if (lane < nr) {
           float h2 = h1s[lane];
 #pragma unroll
@@ -645,6 +678,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
           st_tag_local(rs, lrec(P.o_h2, l) + ((int64_t)x * P.gh + row) * 8, h2, step, coherent);
           if (x == 0 && l == L - 1 && P.h_out) P.h_out[row] = h2;
         }
+        if (stamping && lane == 0) stamp_l(l, 10);
       }
       float ss = 0.f;
       poll_stage_rec(
@@ -660,6 +694,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
           });
       ss = wave_sum_dpp(ss);
       if (lane == 0) s_ss[0][wave] = ss;
+      if (stamping && wave == 0 && lane == 0) stamp_l(l, 11);
     }
   }
 
@@ -669,6 +704,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   int bi = 0x7fffffff;
   if (V > 0) {
     __syncthreads();  // the final h is staged in xb0
+    if (stamping && threadIdx.x == 0) stamp(kStampL * kStampP + 1);
     const float c = rms_scale(s_ss[0], H, P.eps);
     const int T = (V + 63) >> 6;
     for (int tile = wave * G + b; tile < T; tile += kCW * G) {
@@ -696,6 +732,7 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
         }
       st_dev(reinterpret_cast<float*>(ws + P.am_off) + 2 * b, bv);
       st_dev(reinterpret_cast<int32_t*>(ws + P.am_off) + 2 * b + 1, bi);
+      if (stamping) stamp(kStampL * kStampP + 2);
     }
   }
 
@@ -705,6 +742,12 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   // last arriver's device-scope loads see every partial.
   wait_stores();
   __syncthreads();
+  if (stamping) {
+    if (threadIdx.x == 0) stamp(kStampL * kStampP + 3);
+    __syncthreads();
+    for (int i = threadIdx.x; i < kStampWords; i += kCT)
+      P.stamps[(int64_t)b * kStampWords + i] = s_st[i];
+  }
   if (threadIdx.x == 0) s_last = ticket_add(&hdr->ticket) == (unsigned)(G - 1);
   __syncthreads();
   if (!s_last || wave != 0) return;
@@ -853,7 +896,8 @@ int chain_prepare(const q8_0_chain_desc* c, void* ws, size_t ws_bytes, q8_0_chai
   int lds = lo.lds_bytes;
   if (maxlds >= 96 * 1024 && lds < 84 * 1024) lds = 84 * 1024;
   if (lds > maxlds) return Q8_EINVAL;
-  const void* kernels[2] = {(const void*)chain_kernel, (const void*)chain_place_kernel};
+  const void* kernels[3] = {(const void*)chain_kernel<false>, (const void*)chain_kernel<true>,
+                            (const void*)chain_place_kernel};
   for (const void* k : kernels) {
     if (lds > 64 * 1024 &&
         hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
@@ -862,7 +906,7 @@ int chain_prepare(const q8_0_chain_desc* c, void* ws, size_t ws_bytes, q8_0_chai
     }
   }
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel, kCT, lds) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel<true>, kCT, lds) !=
           hipSuccess ||
       per_cu < 1) {
     (void)hipGetLastError();
@@ -940,7 +984,7 @@ int chain_prepare(const q8_0_chain_desc* c, void* ws, size_t ws_bytes, q8_0_chai
 }
 
 int chain_run(const q8_0_chain_plan* plan, void* ws, const float* h_in, float* h_out,
-              float* logits, int32_t* next_token, hipStream_t stream) {
+              float* logits, int32_t* next_token, int64_t* stamps, hipStream_t stream) {
   if (plan->groups != kNX || plan->grid % kNX) return Q8_EINVAL;
   ChainArgs a;
   memset(&a, 0, sizeof(a));
@@ -977,7 +1021,12 @@ int chain_run(const q8_0_chain_plan* plan, void* ws, const float* h_in, float* h
   a.ws_bytes = plan->ws_bytes;
   a.lm.qs = static_cast<const uint8_t*>(plan->lm_qs);
   a.lm.d = static_cast<const uint8_t*>(plan->lm_d);
-  hipLaunchKernelGGL(chain_kernel, dim3(plan->grid), dim3(kCT), plan->lds_bytes, stream, a);
+  a.stamps = stamps;
+  if (stamps)
+    hipLaunchKernelGGL(chain_kernel<true>, dim3(plan->grid), dim3(kCT), plan->lds_bytes, stream, a);
+  else
+    hipLaunchKernelGGL(chain_kernel<false>, dim3(plan->grid), dim3(kCT), plan->lds_bytes, stream,
+                       a);
   if (hipGetLastError() != hipSuccess) return Q8_ELAUNCH;
   return Q8_OK;
 }

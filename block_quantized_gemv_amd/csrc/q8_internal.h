@@ -196,7 +196,7 @@ size_t chain_ws_bytes(const q8_0_chain_desc* c);
 int chain_prepare(const q8_0_chain_desc* c, void* ws, size_t ws_bytes, q8_0_chain_plan* plan,
                   hipStream_t stream);
 int chain_run(const q8_0_chain_plan* plan, void* ws, const float* h_in, float* h_out,
-              float* logits, int32_t* next_token, hipStream_t stream);
+              float* logits, int32_t* next_token, int64_t* stamps, hipStream_t stream);
 int chain_read(const q8_0_chain_plan* plan, const void* ws, int32_t layer, int32_t which,
                float* dst, hipStream_t stream);
 int chain_status(const void* ws, int32_t* out, hipStream_t stream);

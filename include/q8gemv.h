@@ -555,6 +555,29 @@ int q8_0_chain_prepare(const q8_0_chain_desc* desc, void* workspace, size_t work
 int q8_0_chain_run(const q8_0_chain_plan* plan, void* workspace, const float* h_in, float* h_out,
                    float* logits, int32_t* next_token, void* stream);
 
+/* q8_0_chain_run that also records stage timestamps, for profiling.
+ * stamps: device int64 [plan->grid][Q8_CHAIN_STAMP_WORDS], written at the end
+ * of the step: for workgroup b, word b * Q8_CHAIN_STAMP_WORDS + l *
+ * Q8_CHAIN_STAMP_POINTS + k is the 100 MHz s_memrealtime counter at point k
+ * of layer l (first Q8_CHAIN_STAMP_LAYERS layers; 0 where a workgroup has no
+ * such point):
+ *   0 stage A starts, 1 a value/query/key task stored, 2 stage B starts,
+ *   3 a wo task stored, 4 stage C starts, 5 / 6 the first / last gate-up task
+ *   of the workgroup stored, 7 stage D starts, 8 a down partial stored,
+ *   9 the 8 partials of the workgroup's rows received, 10 its h2 rows stored,
+ *   11 the next h staged;
+ * then Q8_CHAIN_STAMP_KERNEL words: 0 step start, 1 LM head start, 2 LM
+ * partial stored, 3 step end.  Results equal those of q8_0_chain_run; the
+ * stamps cost a few percent of the step.
+ * Errors: as q8_0_chain_run. */
+#define Q8_CHAIN_STAMP_LAYERS 32
+#define Q8_CHAIN_STAMP_POINTS 12
+#define Q8_CHAIN_STAMP_KERNEL 4
+#define Q8_CHAIN_STAMP_WORDS (Q8_CHAIN_STAMP_LAYERS * Q8_CHAIN_STAMP_POINTS + Q8_CHAIN_STAMP_KERNEL)
+int q8_0_chain_run_stamped(const q8_0_chain_plan* plan, void* workspace, const float* h_in,
+                           float* h_out, float* logits, int32_t* next_token, int64_t* stamps,
+                           void* stream);
+
 /* Copies one activation vector of layer `layer` from the last run to dst
  * (device fp32): Q8_CHAIN_QKV ([q; k; v], (n_heads + 2 n_kv_heads) head_dim),
  * Q8_CHAIN_H_ATTN (h after the attention residual, hidden), Q8_CHAIN_SWIGLU

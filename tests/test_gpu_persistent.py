@@ -245,3 +245,36 @@ def test_persistent_coherent_mode_bitwise_equal():
     assert torch.equal(logits, ref[0]) and torch.equal(tok, ref[1])
     assert torch.equal(h_out, ref[2]) and torch.equal(pc.read(2, q.Q8_CHAIN_SWIGLU), ref[3])
     check_stagewise(aos, lm, pc, h0, cfg, logits, tok, h_out)
+
+
+def test_persistent_stamped_run_equals_plain_and_orders_its_stamps():
+    """q8_0_chain_run_stamped: the same outputs bit for bit as q8_0_chain_run,
+    and per workgroup the stage-start stamps of every recorded layer are
+    nonzero and in stage order (A < B < C < D < next A)."""
+    cfg = ChainConfig(vocab=4096)
+    n_layers = 3
+    aos, lm, pc, h0 = build(cfg, n_layers, 72)
+    logits, tok, h_out = outputs(pc, cfg)
+    x = to_dev(h0)
+    pc.run(x, logits, tok, h_out)
+    torch.cuda.synchronize()
+    ref = (logits.clone(), tok.clone(), h_out.clone())
+    G, Wd = pc.plan.grid, q.Q8_CHAIN_STAMP_WORDS
+    stamps = torch.zeros(G * Wd, dtype=torch.int64, device=DEV)
+    logits.fill_(0)
+    pc.run(x, logits, tok, h_out, stamps=stamps)
+    torch.cuda.synchronize()
+    assert torch.equal(logits, ref[0]) and torch.equal(tok, ref[1]) and torch.equal(h_out, ref[2])
+    t = host(stamps).reshape(G, Wd)
+    P = q.Q8_CHAIN_STAMP_POINTS
+    lay = t[:, :q.Q8_CHAIN_STAMP_LAYERS * P].reshape(G, q.Q8_CHAIN_STAMP_LAYERS, P)
+    for l in range(n_layers):
+        starts = lay[:, l, [0, 2, 4, 7]]
+        assert np.all(starts > 0), l
+        assert np.all(np.diff(starts, axis=1) > 0), l
+        if l + 1 < n_layers:
+            assert np.all(lay[:, l + 1, 0] > lay[:, l, 7]), l
+    assert np.all(lay[:, n_layers:, :] == 0)  # nothing recorded past the last layer
+    kern = t[:, q.Q8_CHAIN_STAMP_LAYERS * P:]
+    assert np.all(kern[:, 0] > 0) and np.all(kern[:, 3] >= kern[:, 1]) and np.all(kern[:, 1] > 0)
+    assert pc.status() == 0
