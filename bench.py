@@ -660,7 +660,9 @@ def context_rows(cfg, layers, lm_p, h0, steps, stream, log):
 STAGE_POINTS = ("A start", "value/query/key task stored", "B start", "wo task stored",
                 "C start", "last gate-up task stored (first wave)",
                 "first gate-up task stored (last wave)", "D start", "down partial stored",
-                "8 partials received", "h2 rows stored", "next h staged")
+                "8 partials received", "h2 rows stored", "next h staged",
+                "value/query/key weights in registers", "gate-up weights in registers",
+                "value/query/key dot product done", "gate-up dot product done")
 
 
 def stage_breakdown(cfg, layers, lm_p, h0, runs, log):

@@ -33,7 +33,7 @@ Q8_OP_Q5K_GEMV = 9
 Q8_LAYOUT_ROWS, Q8_LAYOUT_GATE_UP_PAIRS = 0, 1
 Q8_CHAIN_COHERENT = 1
 Q8_CHAIN_QKV, Q8_CHAIN_H_ATTN, Q8_CHAIN_SWIGLU, Q8_CHAIN_H_OUT = 0, 1, 2, 3
-Q8_CHAIN_STAMP_LAYERS, Q8_CHAIN_STAMP_POINTS, Q8_CHAIN_STAMP_KERNEL = 32, 12, 4
+Q8_CHAIN_STAMP_LAYERS, Q8_CHAIN_STAMP_POINTS, Q8_CHAIN_STAMP_KERNEL = 32, 16, 4
 Q8_CHAIN_STAMP_WORDS = Q8_CHAIN_STAMP_LAYERS * Q8_CHAIN_STAMP_POINTS + Q8_CHAIN_STAMP_KERNEL
 
 EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv", "q8_0_gemv_fused",

@@ -545,8 +545,16 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
     if (!poller) {
       if (hasD && l > 0) loadD(l);  // slot 0 of the bottom waves is free since D(l - 1)
       if (hasA) {
+        if (stamping && ta == 0) {
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the task's weights are in
+          if (lane == 0) stamp_l(l, 12);
+        }
         const float c = rms_scale(s_ss[0], H, P.eps);
         const float y = task_dot(s0, KA >> 4, xb0, lane) * c;
+        if (stamping && ta == 0) {
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          if (lane == 0 && y == y + 0.0f) stamp_l(l, 14);
+        }
         if (lane < 4) {
           if (ta < tv) {
             const int row = 4 * (v0 + ta) + lane;  // value row
@@ -608,8 +616,16 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
     if (stamping && threadIdx.x == 0) stamp_l(l, 4);
     if (!poller) {
       if (hasC) {
+        if (stamping && ta == 0) {
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+          if (lane == 0) stamp_l(l, 13);
+        }
         const float c = rms_scale(s_ss[1], H, P.eps);
         const float y = task_dot(s2, KC >> 4, xb0, lane) * c;
+        if (stamping && ta == 0) {
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          if (lane == 0 && y == y + 0.0f) stamp_l(l, 15);
+        }
         // lanes 0, 1: gate rows; 2, 3: the matching up rows (quad_perm [2,3,2,3])
         const float up = dpp_f<0xEE>(y);
         if (lane < 2) {

@@ -565,13 +565,15 @@ int q8_0_chain_run(const q8_0_chain_plan* plan, void* workspace, const float* h_
  *   3 a wo task stored, 4 stage C starts, 5 / 6 the first / last gate-up task
  *   of the workgroup stored, 7 stage D starts, 8 a down partial stored,
  *   9 the 8 partials of the workgroup's rows received, 10 its h2 rows stored,
- *   11 the next h staged;
+ *   11 the next h staged, 12 / 13 the first value/query/key and gate-up
+ *   tasks' weights in registers (the stamped instance waits for them there),
+ *   14 / 15 the same tasks' dot products done;
  * then Q8_CHAIN_STAMP_KERNEL words: 0 step start, 1 LM head start, 2 LM
  * partial stored, 3 step end.  Results equal those of q8_0_chain_run; the
  * stamps cost a few percent of the step.
  * Errors: as q8_0_chain_run. */
 #define Q8_CHAIN_STAMP_LAYERS 32
-#define Q8_CHAIN_STAMP_POINTS 12
+#define Q8_CHAIN_STAMP_POINTS 16
 #define Q8_CHAIN_STAMP_KERNEL 4
 #define Q8_CHAIN_STAMP_WORDS (Q8_CHAIN_STAMP_LAYERS * Q8_CHAIN_STAMP_POINTS + Q8_CHAIN_STAMP_KERNEL)
 int q8_0_chain_run_stamped(const q8_0_chain_plan* plan, void* workspace, const float* h_in,
