@@ -233,6 +233,43 @@ __device__ __forceinline__ void route_better(float& v, int& i, float ov, int oi)
     i = oi;
   }
 }
+// The best (largest value, then lowest index) of the wave's 64 pairs, in
+// every lane: DPP row rotations within each 16-lane row, then the row-pair
+// and half swaps (v_permlane16/32_swap, VALU moves; the nop covers the
+// VALU-write to permlane-read hazard).  A total order on the pairs, so the
+// result does not depend on the reduction order.  About 30 VALU operations
+// against 12 LDS-routed shuffles (ds_bpermute) for a butterfly.
+template <int CTRL>
+__device__ __forceinline__ int route_dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ void route_best_wave(float& v, int& i) {
+#define Q8_ROUTE_ROR(C)                                                                   \
+  route_better(v, i, __builtin_bit_cast(float, route_dpp<C>(__builtin_bit_cast(int, v))), \
+               route_dpp<C>(i))
+  Q8_ROUTE_ROR(0x121);  // row_ror:1
+  Q8_ROUTE_ROR(0x122);  // row_ror:2
+  Q8_ROUTE_ROR(0x124);  // row_ror:4
+  Q8_ROUTE_ROR(0x128);  // row_ror:8
+#undef Q8_ROUTE_ROR
+  float va = v, vb = v;
+  int ia = i, ib = i;
+  __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(va), "+v"(vb));
+  __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(ia), "+v"(ib));
+  v = va;
+  i = ia;
+  route_better(v, i, vb, ib);
+  va = v;
+  vb = v;
+  ia = i;
+  ib = i;
+  __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(va), "+v"(vb));
+  __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(ia), "+v"(ib));
+  v = va;
+  i = ia;
+  route_better(v, i, vb, ib);
+}
+
 __device__ __forceinline__ void route_topk_wave(const float* logits, int E, int k, int lane,
                                                 float* sel_v, int* sel_i) {
   float lv[16];
@@ -256,12 +293,11 @@ __device__ __forceinline__ void route_topk_wave(const float* logits, int E, int 
       int bi = 0x7fffffff;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        if (64 * i >= E) break;  // uniform: rows of 64 logits that exist
         const int e = lane + 64 * i;
         if (e < E && !(taken >> i & 1u)) route_better(bv, bi, lv[i], e);
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1)
-        route_better(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
+      route_best_wave(bv, bi);
       sel_v[s] = bv;
       sel_i[s] = bi;
       if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
@@ -288,12 +324,11 @@ __device__ __forceinline__ int route_pick_wave(const float* logits, int E, int s
     int bi = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
+      if (64 * i >= E) break;  // uniform: rows of 64 logits that exist
       const int e = lane + 64 * i;
       if (e < E && !(taken >> i & 1u)) route_better(bv, bi, lv[i], e);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-      route_better(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
+    route_best_wave(bv, bi);
     pick = bi;
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
   }
