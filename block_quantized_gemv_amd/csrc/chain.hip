@@ -155,17 +155,7 @@ __device__ __forceinline__ float q_at(uint32_t w, int k) {
 __device__ __forceinline__ float f16_to_f32(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oi = __shfl_xor(i, o, 64);
-    if (ov > v || (ov == v && oi < i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) { wave_best_pair(v, i); }
 
 // Weight pointers come from a table in memory, so the compiler cannot prove
 // they are global; flat loads would also count against lgkmcnt and make every

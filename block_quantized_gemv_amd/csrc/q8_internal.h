@@ -223,11 +223,10 @@ __device__ __forceinline__ unsigned ticket_add(uint32_t* t) {
   return __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---- top-k routing, one wave ------------------------------------------------
-// The k largest of E <= 1024 router logits in descending order, ties to the
-// lower index (lane l holds logits l, l + 64, ...); every lane ends with the
-// same picks.  Exact comparisons, so every caller selects identically.
-__device__ __forceinline__ void route_better(float& v, int& i, float ov, int oi) {
+// ---- (value, index) selection, one wave ---------------------------------------
+// pair_better keeps the larger value, then the lower index: a total order on
+// finite values, so any reduction order selects the same pair.
+__device__ __forceinline__ void pair_better(float& v, int& i, float ov, int oi) {
   if (ov > v || (ov == v && oi < i)) {
     v = ov;
     i = oi;
@@ -240,25 +239,25 @@ __device__ __forceinline__ void route_better(float& v, int& i, float ov, int oi)
 // result does not depend on the reduction order.  About 30 VALU operations
 // against 12 LDS-routed shuffles (ds_bpermute) for a butterfly.
 template <int CTRL>
-__device__ __forceinline__ int route_dpp(int v) {
+__device__ __forceinline__ int pair_dpp(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
 }
-__device__ __forceinline__ void route_best_wave(float& v, int& i) {
-#define Q8_ROUTE_ROR(C)                                                                   \
-  route_better(v, i, __builtin_bit_cast(float, route_dpp<C>(__builtin_bit_cast(int, v))), \
-               route_dpp<C>(i))
-  Q8_ROUTE_ROR(0x121);  // row_ror:1
-  Q8_ROUTE_ROR(0x122);  // row_ror:2
-  Q8_ROUTE_ROR(0x124);  // row_ror:4
-  Q8_ROUTE_ROR(0x128);  // row_ror:8
-#undef Q8_ROUTE_ROR
+__device__ __forceinline__ void wave_best_pair(float& v, int& i) {
+#define Q8_PAIR_ROR(C)                                                                   \
+  pair_better(v, i, __builtin_bit_cast(float, pair_dpp<C>(__builtin_bit_cast(int, v))), \
+               pair_dpp<C>(i))
+  Q8_PAIR_ROR(0x121);  // row_ror:1
+  Q8_PAIR_ROR(0x122);  // row_ror:2
+  Q8_PAIR_ROR(0x124);  // row_ror:4
+  Q8_PAIR_ROR(0x128);  // row_ror:8
+#undef Q8_PAIR_ROR
   float va = v, vb = v;
   int ia = i, ib = i;
   __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(va), "+v"(vb));
   __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(ia), "+v"(ib));
   v = va;
   i = ia;
-  route_better(v, i, vb, ib);
+  pair_better(v, i, vb, ib);
   va = v;
   vb = v;
   ia = i;
@@ -267,9 +266,13 @@ __device__ __forceinline__ void route_best_wave(float& v, int& i) {
   __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(ia), "+v"(ib));
   v = va;
   i = ia;
-  route_better(v, i, vb, ib);
+  pair_better(v, i, vb, ib);
 }
 
+// ---- top-k routing, one wave ------------------------------------------------
+// The k largest of E <= 1024 router logits in descending order, ties to the
+// lower index (lane l holds logits l, l + 64, ...); every lane ends with the
+// same picks.  Exact comparisons, so every caller selects identically.
 __device__ __forceinline__ void route_topk_wave(const float* logits, int E, int k, int lane,
                                                 float* sel_v, int* sel_i) {
   float lv[16];
@@ -295,9 +298,9 @@ __device__ __forceinline__ void route_topk_wave(const float* logits, int E, int 
       for (int i = 0; i < 16; ++i) {
         if (64 * i >= E) break;  // uniform: rows of 64 logits that exist
         const int e = lane + 64 * i;
-        if (e < E && !(taken >> i & 1u)) route_better(bv, bi, lv[i], e);
+        if (e < E && !(taken >> i & 1u)) pair_better(bv, bi, lv[i], e);
       }
-      route_best_wave(bv, bi);
+      wave_best_pair(bv, bi);
       sel_v[s] = bv;
       sel_i[s] = bi;
       if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
@@ -326,9 +329,9 @@ __device__ __forceinline__ int route_pick_wave(const float* logits, int E, int s
     for (int i = 0; i < 16; ++i) {
       if (64 * i >= E) break;  // uniform: rows of 64 logits that exist
       const int e = lane + 64 * i;
-      if (e < E && !(taken >> i & 1u)) route_better(bv, bi, lv[i], e);
+      if (e < E && !(taken >> i & 1u)) pair_better(bv, bi, lv[i], e);
     }
-    route_best_wave(bv, bi);
+    wave_best_pair(bv, bi);
     pick = bi;
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
   }

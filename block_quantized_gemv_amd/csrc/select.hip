@@ -26,10 +26,7 @@ __device__ __forceinline__ void better(float& v, int& i, float ov, int oi) {
   }
 }
 
-__device__ __forceinline__ void wave_best(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) better(v, i, __shfl_xor(v, o, 64), __shfl_xor(i, o, 64));
-}
+__device__ __forceinline__ void wave_best(float& v, int& i) { wave_best_pair(v, i); }
 
 constexpr int kArgThreads = 256;
 constexpr int kArgPerThread = 8;
