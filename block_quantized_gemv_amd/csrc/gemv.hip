@@ -1026,10 +1026,34 @@ __global__ __launch_bounds__(64 * max_waves_for(N, MODE >= 3)) void gemv_kernel(
     if (threadIdx.x == 0) s_last = ticket_add(&pr.tile_tickets[ot]) == (unsigned)(pr.P - 1);
     __syncthreads();
     if (!s_last) return;
-    if (wave != 0) return;
-    if (lane == 0) st_dev(&pr.tile_tickets[ot], 0u);  // ready for the next call
-    fold_units<N>(p, pr, us, [&](int uu, int n) { return ld_dev(gp + (uu * N + n) * 64 + lane); },
-                  val);
+    if (threadIdx.x == 0) st_dev(&pr.tile_tickets[ot], 0u);  // ready for the next call
+    if (pr.fold_lds) {
+      // every wave of the last workgroup fetches a share of the tile's
+      // partials, 8 loads a lane in flight together (indexes past the end
+      // clamp to the last word and are not kept), into LDS; wave 0 then
+      // folds them in the same order as from memory
+      const int tot = pr.U * N * 64;
+      const int nt = (int)blockDim.x;
+      for (int b = (int)threadIdx.x; b < tot; b += 8 * nt) {
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = b + j * nt;
+          t[j] = ld_dev(gp + (i < tot ? i : tot - 1));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (b + j * nt < tot) lds_part[b + j * nt] = t[j];
+      }
+      __syncthreads();
+      if (wave != 0) return;
+      fold_units<N>(p, pr, us, [&](int uu, int n) { return lds_part[(uu * N + n) * 64 + lane]; },
+                    val);
+    } else {
+      if (wave != 0) return;
+      fold_units<N>(p, pr, us,
+                    [&](int uu, int n) { return ld_dev(gp + (uu * N + n) * 64 + lane); }, val);
+    }
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -1393,7 +1417,12 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
 
 template <int N>
 static hipError_t launch_n(const GemvParams& gp, int wgs, hipStream_t stream) {
-  const size_t lds = (size_t)gp.W * N * 64 * sizeof(float);
+  size_t lds = (size_t)gp.W * N * 64 * sizeof(float);
+  for (int i = 0; i < gp.nprob; ++i)
+    if (gp.prob[i].fold_lds) {
+      const size_t f = (size_t)gp.prob[i].U * N * 64 * sizeof(float);
+      if (f > lds) lds = f;
+    }
   if (gp.seg[0].qx)  // the integer-activation path: one plain problem
     hipLaunchKernelGGL((gemv_kernel<N, true, 1>), dim3(wgs), dim3(64 * gp.W), lds, stream, gp);
   else if (gp.seg[0].fmt != FMT_Q8_0) {  // K-quants: one plain problem, N <= 4
@@ -1441,6 +1470,15 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
     pr.Tout = (int32_t)Tout;
     pr.U = plan.U[i];
     pr.P = plan.P[i];
+    // In a launch of at most one workgroup per compute unit the last tile's
+    // fold is the launch's tail: split tiles whose partials fit a
+    // workgroup's LDS share at the kernel's occupancy (16 waves a compute
+    // unit: 160 KB / 16 = 10 KB a wave, 8 KB kept) stage them there first
+    // (MoE combine, 4 routed down 2048x1408 + shared 2048x5632 at N = 1:
+    // 13.4 -> 12.4 us).  In larger launches other workgroups hide the fold,
+    // and the staging measured slightly slower (C4 gate_up N = 8: +0.5 us).
+    pr.fold_lds = pr.P > 1 && plan.total_wg <= num_cus() &&
+                  (int64_t)pr.U * N <= 32 * (int64_t)plan.W && pr.U * N <= 128;
     pr.wg0 = wg;
     pr.flags = pd.flags;
     pr.eps = pd.eps;

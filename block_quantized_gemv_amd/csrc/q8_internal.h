@@ -86,6 +86,7 @@ struct Prob {
   int32_t Tout;          // output tiles
   int32_t U;             // units per output tile (R * sum of segment units)
   int32_t P;             // workgroups per output tile
+  int32_t fold_lds;      // P > 1: the last workgroup stages the tile's partials in LDS
   int32_t wg0;           // first workgroup of this problem
   int32_t flags;         // F_*
   float eps;
