@@ -203,6 +203,123 @@ __device__ __forceinline__ void dot_range(const uint8_t* qs_tile, const uint8_t*
   }
 }
 
+// ---- row groups: several columns, activations not replicated ---------------
+// With N >= kRowGroupN columns the replicated activations above cost 16 N
+// VGPRs per block in flight (64 N per quad), which caps the waves a SIMD
+// holds and with them the hiding of each wave's load latency.  Here the 16-
+// lane row r of a wave takes block r of each quad instead, for the 64 rows of
+// the tile in four row groups: lane 16r + j computes rows 16q + j (q = 0..3)
+// of block 4g + r.  A lane row then needs the activations of its own block
+// only (one XBlock a quad instead of four), the weights are loaded as the
+// same 16-byte pieces of the same packed tile (four 256-byte runs per load
+// instead of one 1 KiB run), and each lane keeps four partial sums per
+// column.  Each row group's weights of the next quad are loaded right after
+// that row group's products, into the registers they just freed, so one quad
+// of weights is in flight with one quad's registers.  Loads are never
+// conditional (past the range they re-read the last quad, which the L2 still
+// holds), so the compiler's wait counts stay exact.  At the end of the range
+// the four lane rows' sums of each row group are added across rows with two
+// lane-half swaps (permlane32, then permlane16) in a fixed order,
+// ((r0 + r2) + (r1 + r3)), which leaves row 16q + j's total in lane 16q + j:
+// the layout dot_range produces.
+constexpr int kRowGroupN = 4;
+
+// Where lane row r finds block 4g + r of a quad (clamped into [b0, b1)).
+struct RgPos {
+  uint32_t qoff;   // byte offset of the lane's first 16 weights (row group 0)
+  uint32_t doff;   // byte offset of the dword holding the lane's block scale
+  uint32_t sh;     // 0 or 16: the half of that dword
+  uint32_t blk;    // block whose activations the lane row reads
+  bool ok;         // the block lies in [b0, b1) (else it adds nothing)
+};
+
+__device__ __forceinline__ RgPos rg_pos(int g, int r, int j, int b0, int b1) {
+  RgPos P;
+  const int blk = 4 * g + r;
+  P.ok = blk >= b0 && blk < b1;
+  const int bc = blk < b0 ? b0 : (blk < b1 ? blk : b1 - 1);
+  P.blk = (uint32_t)bc;
+  P.qoff = (uint32_t)((2 * bc * 64 + j) * 16);
+  P.doff = (uint32_t)((128 * (bc >> 2) + 2 * j + ((bc >> 1) & 1)) * 4);
+  P.sh = (uint32_t)(bc & 1) * 16;
+  return P;
+}
+
+// The 32 weights and the scale dword of row group q at P.
+__device__ __forceinline__ void rg_wload(u32x4 (&w)[2], uint32_t& sc, const uint8_t* qs_tile,
+                                         const uint8_t* d_tile, const RgPos& P, int q) {
+  w[0] = __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4*>(qs_tile + P.qoff + 256 * q));
+  w[1] = __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4*>(qs_tile + P.qoff + 1024 + 256 * q));
+  sc = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(d_tile + P.doff + 128 * q));
+}
+
+// a[n] += d * sum_k w[k] x[n][k] for row group q of the lane row's block.
+template <int N>
+__device__ __forceinline__ void rg_fma(const u32x4 (&wq)[2], uint32_t sc, const XBlock<N>& X,
+                                       const RgPos& P, float (&a)[N]) {
+  const uint32_t w[8] = {wq[0].x, wq[0].y, wq[0].z, wq[0].w, wq[1].x, wq[1].y, wq[1].z, wq[1].w};
+  float p[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) p[n] = 0.f;
+  xv_steps<N>(w, X, p, std::make_integer_sequence<int, 32>{});
+  const float d = P.ok ? f16_to_f32(sc >> P.sh) : 0.f;
+#pragma unroll
+  for (int n = 0; n < N; ++n) a[n] = fmaf(d, p[n], a[n]);
+}
+
+template <int N>
+__device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8_t* d_tile, int b0,
+                                             int b1, int lane, const float* x, int64_t xs, int gg,
+                                             int ghd, int64_t goff, float (&acc)[N]) {
+  const int r = lane >> 4, j = lane & 15;
+  float a4[4][N];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int n = 0; n < N; ++n) a4[q][n] = 0.f;
+  const int g0 = b0 >> 2;
+  const int nq = b1 > b0 ? ((b1 + 3) >> 2) - g0 : 0;
+  if (nq > 0) {
+    const int gl = g0 + nq - 1;
+    u32x4 W[4][2];
+    uint32_t SC[4];
+    XBlock<N> XA, XB;
+    RgPos PA = rg_pos(g0, r, j, b0, b1), PB;
+    load_xblock<N>(x_block(x, PA.blk, gg, ghd, goff), xs, j, XA);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rg_wload(W[q], SC[q], qs_tile, d_tile, PA, q);
+    for (int it = 0; it < nq; it += 2) {
+      const int ga = g0 + it + 1, gb = g0 + it + 2;
+      PB = rg_pos(ga < gl ? ga : gl, r, j, b0, b1);
+      load_xblock<N>(x_block(x, PB.blk, gg, ghd, goff), xs, j, XB);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rg_fma<N>(W[q], SC[q], XA, PA, a4[q]);
+        rg_wload(W[q], SC[q], qs_tile, d_tile, PB, q);
+      }
+      const bool second = it + 1 < nq;
+      PA = rg_pos(gb < gl ? gb : gl, r, j, b0, b1);
+      load_xblock<N>(x_block(x, PA.blk, gg, ghd, goff), xs, j, XA);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (second) rg_fma<N>(W[q], SC[q], XB, PB, a4[q]);
+        rg_wload(W[q], SC[q], qs_tile, d_tile, PA, q);
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    float s0 = a4[0][n], s2 = a4[2][n], s1 = a4[1][n], s3 = a4[3][n];
+    __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(s0), "+v"(s2));
+    __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(s1), "+v"(s3));
+    float u = s0 + s2, v = s1 + s3;
+    __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(u), "+v"(v));
+    acc[n] += u + v;
+  }
+}
+
 // ---- Q4_K and Q5_K weights ---------------------------------------------------
 // A quad is half of a 256-weight block: 4 sub-blocks of 32.  Sub-block j of
 // a row is 16 bytes whose byte i holds weights i (low nibble) and i + 16 (high
@@ -999,8 +1116,14 @@ __global__ __launch_bounds__(64 * max_waves_for(N, MODE >= 3)) void gemv_kernel(
                            s.d + (int64_t)t * s.G * 1024, b0, b1, lane, s.x, s.x_stride, acc);
       }
       else
-        dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
-                     s.gqa_off, acc);
+      {
+        if constexpr (N >= kRowGroupN)
+          dot_range_rg<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
+                          s.gqa_off, acc);
+        else
+          dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
+                       s.gqa_off, acc);
+      }
     } else if (lane == 0 && pr.dev_status) {
       atomicOr(pr.dev_status, 1);
     }
