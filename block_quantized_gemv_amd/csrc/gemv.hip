@@ -225,24 +225,46 @@ __device__ __forceinline__ void dot_range(const uint8_t* qs_tile, const uint8_t*
 constexpr int kRowGroupN = 4;
 
 // Where lane row r finds block 4g + r of a quad (clamped into [b0, b1)).
+// Offsets are 32-bit and from bases every lane shares, so the loads take the
+// scalar-base, vector-offset form with no 64-bit address arithmetic.
 struct RgPos {
   uint32_t qoff;   // byte offset of the lane's first 16 weights (row group 0)
   uint32_t doff;   // byte offset of the dword holding the lane's block scale
+  uint32_t xoff;   // byte offset of activation j of the lane row's block
   uint32_t sh;     // 0 or 16: the half of that dword
-  uint32_t blk;    // block whose activations the lane row reads
   bool ok;         // the block lies in [b0, b1) (else it adds nothing)
 };
 
-__device__ __forceinline__ RgPos rg_pos(int g, int r, int j, int b0, int b1) {
+template <bool GQA>
+__device__ __forceinline__ RgPos rg_pos(int g, int r, int j, int b0, int b1, int gg, int ghd,
+                                        int64_t goff) {
   RgPos P;
   const int blk = 4 * g + r;
   P.ok = blk >= b0 && blk < b1;
   const int bc = blk < b0 ? b0 : (blk < b1 ? blk : b1 - 1);
-  P.blk = (uint32_t)bc;
   P.qoff = (uint32_t)((2 * bc * 64 + j) * 16);
   P.doff = (uint32_t)((128 * (bc >> 2) + 2 * j + ((bc >> 1) & 1)) * 4);
   P.sh = (uint32_t)(bc & 1) * 16;
+  if constexpr (GQA) {
+    const int k = bc * 32;
+    const int head = k / ghd;
+    P.xoff = (uint32_t)((goff + (int64_t)(head / gg) * ghd + (k - head * ghd) + j) * 4);
+  } else {
+    P.xoff = (uint32_t)((bc * 32 + j) * 4);
+  }
   return P;
+}
+
+// Activations of the lane row's block: x[n][k0 + j] and x[n][k0 + 16 + j].
+template <int N>
+__device__ __forceinline__ void rg_xload(const float* x, int64_t xs, uint32_t xoff,
+                                         XBlock<N>& X) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const char* xn = reinterpret_cast<const char*>(x + n * xs);
+    X.a[n] = *reinterpret_cast<const float*>(xn + xoff);
+    X.b[n] = *reinterpret_cast<const float*>(xn + xoff + 64);
+  }
 }
 
 // The 32 weights and the scale dword of row group q at P.
@@ -269,7 +291,7 @@ __device__ __forceinline__ void rg_fma(const u32x4 (&wq)[2], uint32_t sc, const 
   for (int n = 0; n < N; ++n) a[n] = fmaf(d, p[n], a[n]);
 }
 
-template <int N>
+template <int N, bool GQA>
 __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8_t* d_tile, int b0,
                                              int b1, int lane, const float* x, int64_t xs, int gg,
                                              int ghd, int64_t goff, float (&acc)[N]) {
@@ -282,30 +304,52 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
   const int g0 = b0 >> 2;
   const int nq = b1 > b0 ? ((b1 + 3) >> 2) - g0 : 0;
   if (nq > 0) {
-    const int gl = g0 + nq - 1;
     u32x4 W[4][2];
     uint32_t SC[4];
     XBlock<N> XA, XB;
-    RgPos PA = rg_pos(g0, r, j, b0, b1), PB;
-    load_xblock<N>(x_block(x, PA.blk, gg, ghd, goff), xs, j, XA);
+    RgPos PA = rg_pos<GQA>(g0, r, j, b0, b1, gg, ghd, goff), PB;
+    rg_xload<N>(x, xs, PA.xoff, XA);
 #pragma unroll
     for (int q = 0; q < 4; ++q) rg_wload(W[q], SC[q], qs_tile, d_tile, PA, q);
-    for (int it = 0; it < nq; it += 2) {
-      const int ga = g0 + it + 1, gb = g0 + it + 2;
-      PB = rg_pos(ga < gl ? ga : gl, r, j, b0, b1);
-      load_xblock<N>(x_block(x, PB.blk, gg, ghd, goff), xs, j, XB);
+    // An odd quad count starts with one quad alone; then two quads a trip in
+    // two named buffers (no loop-carried copies).  The loads of the last
+    // trip are for quads past the range: those have no block in [b0, b1),
+    // so they re-read the last block and are never used.  No product is
+    // conditional (a conditional one lets the compiler sink its weights'
+    // load down to it), and the scheduling barriers keep each load where it
+    // is issued (within one basic block the scheduler would otherwise move
+    // the loads down to their uses to save registers).
+    int it = 0;
+    if (nq & 1) {
+      const RgPos P1 = rg_pos<GQA>(g0 + 1, r, j, b0, b1, gg, ghd, goff);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        rg_fma<N>(W[q], SC[q], XA, PA, a4[q]);
+        rg_wload(W[q], SC[q], qs_tile, d_tile, P1, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      PA = P1;
+      rg_xload<N>(x, xs, PA.xoff, XA);
+      it = 1;
+    }
+    for (; it < nq; it += 2) {
+      PB = rg_pos<GQA>(g0 + it + 1, r, j, b0, b1, gg, ghd, goff);
+      rg_xload<N>(x, xs, PB.xoff, XB);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         rg_fma<N>(W[q], SC[q], XA, PA, a4[q]);
         rg_wload(W[q], SC[q], qs_tile, d_tile, PB, q);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const bool second = it + 1 < nq;
-      PA = rg_pos(gb < gl ? gb : gl, r, j, b0, b1);
-      load_xblock<N>(x_block(x, PA.blk, gg, ghd, goff), xs, j, XA);
+      PA = rg_pos<GQA>(g0 + it + 2, r, j, b0, b1, gg, ghd, goff);
+      rg_xload<N>(x, xs, PA.xoff, XA);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (second) rg_fma<N>(W[q], SC[q], XB, PB, a4[q]);
+        rg_fma<N>(W[q], SC[q], XB, PB, a4[q]);
         rg_wload(W[q], SC[q], qs_tile, d_tile, PA, q);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -1117,9 +1161,13 @@ __global__ __launch_bounds__(64 * max_waves_for(N, MODE >= 3)) void gemv_kernel(
       }
       else
       {
-        if constexpr (N >= kRowGroupN)
-          dot_range_rg<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
-                          s.gqa_off, acc);
+        if constexpr (N >= kRowGroupN) {
+          if (s.gqa_group > 0)
+            dot_range_rg<N, true>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group,
+                                  s.gqa_hd, s.gqa_off, acc);
+          else
+            dot_range_rg<N, false>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, 0, 1, 0, acc);
+        }
         else
           dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
                        s.gqa_off, acc);
