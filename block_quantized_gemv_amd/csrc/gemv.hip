@@ -235,9 +235,7 @@ struct RgPos {
   bool ok;         // the block lies in [b0, b1) (else it adds nothing)
 };
 
-template <bool GQA>
-__device__ __forceinline__ RgPos rg_pos(int g, int r, int j, int b0, int b1, int gg, int ghd,
-                                        int64_t goff) {
+__device__ __forceinline__ RgPos rg_pos(int g, int r, int j, int b0, int b1) {
   RgPos P;
   const int blk = 4 * g + r;
   P.ok = blk >= b0 && blk < b1;
@@ -245,13 +243,7 @@ __device__ __forceinline__ RgPos rg_pos(int g, int r, int j, int b0, int b1, int
   P.qoff = (uint32_t)((2 * bc * 64 + j) * 16);
   P.doff = (uint32_t)((128 * (bc >> 2) + 2 * j + ((bc >> 1) & 1)) * 4);
   P.sh = (uint32_t)(bc & 1) * 16;
-  if constexpr (GQA) {
-    const int k = bc * 32;
-    const int head = k / ghd;
-    P.xoff = (uint32_t)((goff + (int64_t)(head / gg) * ghd + (k - head * ghd) + j) * 4);
-  } else {
-    P.xoff = (uint32_t)((bc * 32 + j) * 4);
-  }
+  P.xoff = (uint32_t)((bc * 32 + j) * 4);
   return P;
 }
 
@@ -291,10 +283,10 @@ __device__ __forceinline__ void rg_fma(const u32x4 (&wq)[2], uint32_t sc, const 
   for (int n = 0; n < N; ++n) a[n] = fmaf(d, p[n], a[n]);
 }
 
-template <int N, bool GQA>
+template <int N>
 __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8_t* d_tile, int b0,
-                                             int b1, int lane, const float* x, int64_t xs, int gg,
-                                             int ghd, int64_t goff, float (&acc)[N]) {
+                                             int b1, int lane, const float* x, int64_t xs,
+                                             float (&acc)[N]) {
   const int r = lane >> 4, j = lane & 15;
   float a4[4][N];
 #pragma unroll
@@ -307,7 +299,7 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
     u32x4 W[4][2];
     uint32_t SC[4];
     XBlock<N> XA, XB;
-    RgPos PA = rg_pos<GQA>(g0, r, j, b0, b1, gg, ghd, goff), PB;
+    RgPos PA = rg_pos(g0, r, j, b0, b1), PB;
     rg_xload<N>(x, xs, PA.xoff, XA);
 #pragma unroll
     for (int q = 0; q < 4; ++q) rg_wload(W[q], SC[q], qs_tile, d_tile, PA, q);
@@ -321,7 +313,7 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
     // the loads down to their uses to save registers).
     int it = 0;
     if (nq & 1) {
-      const RgPos P1 = rg_pos<GQA>(g0 + 1, r, j, b0, b1, gg, ghd, goff);
+      const RgPos P1 = rg_pos(g0 + 1, r, j, b0, b1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         rg_fma<N>(W[q], SC[q], XA, PA, a4[q]);
@@ -333,7 +325,7 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
       it = 1;
     }
     for (; it < nq; it += 2) {
-      PB = rg_pos<GQA>(g0 + it + 1, r, j, b0, b1, gg, ghd, goff);
+      PB = rg_pos(g0 + it + 1, r, j, b0, b1);
       rg_xload<N>(x, xs, PB.xoff, XB);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -342,7 +334,7 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
         rg_wload(W[q], SC[q], qs_tile, d_tile, PB, q);
         __builtin_amdgcn_sched_barrier(0);
       }
-      PA = rg_pos<GQA>(g0 + it + 2, r, j, b0, b1, gg, ghd, goff);
+      PA = rg_pos(g0 + it + 2, r, j, b0, b1);
       rg_xload<N>(x, xs, PA.xoff, XA);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1161,12 +1153,14 @@ __global__ __launch_bounds__(64 * max_waves_for(N, MODE >= 3)) void gemv_kernel(
       }
       else
       {
+        // (the GQA prologue is a single-column operation: it keeps the
+        // replicated path)
         if constexpr (N >= kRowGroupN) {
           if (s.gqa_group > 0)
-            dot_range_rg<N, true>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group,
-                                  s.gqa_hd, s.gqa_off, acc);
+            dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
+                         s.gqa_off, acc);
           else
-            dot_range_rg<N, false>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, 0, 1, 0, acc);
+            dot_range_rg<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, acc);
         }
         else
           dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,

@@ -28,7 +28,7 @@ SHAPES = [(1, 32), (7, 64), (64, 896), (65, 96), (130, 160), (200, 224), (896, 8
 
 
 @pytest.mark.parametrize("M,K", SHAPES)
-@pytest.mark.parametrize("N", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_gemv_matches_oracle(M, K, N):
     g = W.rng(20, M * 7 + N, K)
     m = W.draw_matrix(g, M, K)
