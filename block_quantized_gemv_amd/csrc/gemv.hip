@@ -283,10 +283,27 @@ __device__ __forceinline__ void rg_fma(const u32x4 (&wq)[2], uint32_t sc, const 
   for (int n = 0; n < N; ++n) a[n] = fmaf(d, p[n], a[n]);
 }
 
+// Issue priority falls with progress through the unit (quads done of nq,
+// four levels).  A SIMD issues from its oldest wave first, so without this
+// the waves sharing it finish one after another and the last runs alone,
+// unable to hide its loads; with it a wave that is ahead yields to the ones
+// behind, and they finish together.
+__device__ __forceinline__ void rg_progress_prio(int done, int nq) {
+  const int level = (4 * done) / nq;
+  if (level == 0)
+    __builtin_amdgcn_s_setprio(3);
+  else if (level == 1)
+    __builtin_amdgcn_s_setprio(2);
+  else if (level == 2)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 template <int N>
 __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8_t* d_tile, int b0,
                                              int b1, int lane, const float* x, int64_t xs,
-                                             float (&acc)[N]) {
+                                             bool prio, float (&acc)[N]) {
   const int r = lane >> 4, j = lane & 15;
   float a4[4][N];
 #pragma unroll
@@ -313,6 +330,7 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
     // the loads down to their uses to save registers).
     int it = 0;
     if (nq & 1) {
+      if (prio) rg_progress_prio(0, nq);
       const RgPos P1 = rg_pos(g0 + 1, r, j, b0, b1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -325,6 +343,7 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
       it = 1;
     }
     for (; it < nq; it += 2) {
+      if (prio) rg_progress_prio(it, nq);
       PB = rg_pos(g0 + it + 1, r, j, b0, b1);
       rg_xload<N>(x, xs, PB.xoff, XB);
       __builtin_amdgcn_sched_barrier(0);
@@ -334,6 +353,7 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
         rg_wload(W[q], SC[q], qs_tile, d_tile, PB, q);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (prio) rg_progress_prio(it + 1, nq);
       PA = rg_pos(g0 + it + 2, r, j, b0, b1);
       rg_xload<N>(x, xs, PA.xoff, XA);
       __builtin_amdgcn_sched_barrier(0);
@@ -345,6 +365,7 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
       }
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     float s0 = a4[0][n], s2 = a4[2][n], s1 = a4[1][n], s3 = a4[3][n];
@@ -1153,15 +1174,11 @@ __global__ __launch_bounds__(64 * max_waves_for(N, MODE >= 3)) void gemv_kernel(
       }
       else
       {
-        // (the GQA prologue is a single-column operation: it keeps the
-        // replicated path)
-        if constexpr (N >= kRowGroupN) {
-          if (s.gqa_group > 0)
-            dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
-                         s.gqa_off, acc);
-          else
-            dot_range_rg<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, acc);
-        }
+        // (the GQA prologue exists for one column only, which the launcher
+        // enforces; the row-group instances carry no replicated path, whose
+        // registers would set the whole kernel's occupancy)
+        if constexpr (N >= kRowGroupN)
+          dot_range_rg<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, p.prio != 0, acc);
         else
           dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
                        s.gqa_off, acc);
@@ -1613,6 +1630,11 @@ static hipError_t launch_n(const GemvParams& gp, int wgs, hipStream_t stream) {
 
 int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws_bytes,
                     hipStream_t stream, const RouteParams* route) {
+  // the GQA prologue is a one-column operation; the kernels with several
+  // columns do not implement it
+  for (int i = 0; i < nprob; ++i)
+    for (int s = 0; s < probs[i].nseg; ++s)
+      if (probs[i].seg[s].gqa_group > 0 && N > 1) return Q8_EINVAL;
   Plan plan;
   int rc = plan_problems(probs, nprob, N, &plan);
   if (rc) return rc;
@@ -1697,6 +1719,11 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
   }
   gp.total_wg = wg;
   gp.W = plan.W;
+  // Progress priorities pay when all of a launch's waves are resident from
+  // the start (the row-group instances hold at least 3 waves per SIMD); in
+  // launches of several rounds, oldest-first issue frees slots sooner
+  // (lm_head at N = 8: 62.5 us without, 64.9 with).
+  gp.prio = (int64_t)wg * plan.W <= 3 * 4 * (int64_t)num_cus();
   if (route) gp.route = *route;  // (memset above: no router otherwise)
   if (wg <= 0) return Q8_OK;
   hipError_t e;

@@ -119,6 +119,7 @@ struct GemvParams {
   int32_t nprob;
   int32_t total_wg;
   int32_t W;             // waves per workgroup
+  int32_t prio;          // every wave resident at once: issue priority by progress
   RouteParams route;
 };
 
