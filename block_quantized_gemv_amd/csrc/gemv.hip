@@ -1662,9 +1662,13 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
     // workgroup's LDS share at the kernel's occupancy (16 waves a compute
     // unit: 160 KB / 16 = 10 KB a wave, 8 KB kept) stage them there first
     // (MoE combine, 4 routed down 2048x1408 + shared 2048x5632 at N = 1:
-    // 13.4 -> 12.4 us).  In larger launches other workgroups hide the fold,
-    // and the staging measured slightly slower (C4 gate_up N = 8: +0.5 us).
-    pr.fold_lds = pr.P > 1 && plan.total_wg <= num_cus() &&
+    // 13.4 -> 12.4 us).  So do row-group launches whose waves are all
+    // resident at once (C4 gate_up N = 8: 41.5 -> 39.2 us).  In launches of
+    // several rounds other workgroups hide the fold, and the staging measured
+    // slightly slower.
+    pr.fold_lds = pr.P > 1 &&
+                  (plan.total_wg <= num_cus() ||
+                   (N >= kRowGroupN && (int64_t)plan.total_wg * plan.W <= 3 * 4 * (int64_t)num_cus())) &&
                   (int64_t)pr.U * N <= 32 * (int64_t)plan.W && pr.U * N <= 128;
     pr.wg0 = wg;
     pr.flags = pd.flags;
