@@ -343,6 +343,8 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
       it = 1;
     }
     for (; it < nq; it += 2) {
+      // (once a trip: a second call mid-trip split the loop's block and cost
+      // 20-27 more VGPRs)
       if (prio) rg_progress_prio(it, nq);
       PB = rg_pos(g0 + it + 1, r, j, b0, b1);
       rg_xload<N>(x, xs, PB.xoff, XB);
@@ -353,7 +355,6 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
         rg_wload(W[q], SC[q], qs_tile, d_tile, PB, q);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (prio) rg_progress_prio(it + 1, nq);
       PA = rg_pos(g0 + it + 2, r, j, b0, b1);
       rg_xload<N>(x, xs, PA.xoff, XA);
       __builtin_amdgcn_sched_barrier(0);
@@ -1177,9 +1178,19 @@ __global__ __launch_bounds__(64 * max_waves_for(N, MODE >= 3)) void gemv_kernel(
         // (the GQA prologue exists for one column only, which the launcher
         // enforces; the row-group instances carry no replicated path, whose
         // registers would set the whole kernel's occupancy)
+        // N >= 4: row groups always.  N = 2, 3: row groups when every wave is
+        // resident (C4 down 4096x12288 N = 2: 16.7 -> 15.2 us), the
+        // replicated loop in launches of several rounds with short units
+        // (lm_head N = 2: 31.5 us replicated, 33.9 with row groups).
         if constexpr (N >= kRowGroupN)
           dot_range_rg<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, p.prio != 0, acc);
-        else
+        else if constexpr (N >= 2) {
+          if (p.prio)
+            dot_range_rg<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, true, acc);
+          else
+            dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
+                         s.gqa_off, acc);
+        } else
           dot_range<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, s.gqa_group, s.gqa_hd,
                        s.gqa_off, acc);
       }
@@ -1668,7 +1679,7 @@ int launch_problems(const ProbDesc* probs, int nprob, int N, void* ws, size_t ws
     // slightly slower.
     pr.fold_lds = pr.P > 1 &&
                   (plan.total_wg <= num_cus() ||
-                   (N >= kRowGroupN && (int64_t)plan.total_wg * plan.W <= 3 * 4 * (int64_t)num_cus())) &&
+                   (N >= 2 && (int64_t)plan.total_wg * plan.W <= 3 * 4 * (int64_t)num_cus())) &&
                   (int64_t)pr.U * N <= 32 * (int64_t)plan.W && pr.U * N <= 128;
     pr.wg0 = wg;
     pr.flags = pd.flags;
