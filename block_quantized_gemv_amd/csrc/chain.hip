@@ -52,12 +52,17 @@
 // whole dot products after a reduction over the 16 lanes of each row.  A
 // weight wave owns at most one task per stage, in one of three register
 // slots, and reloads a slot with the next layer's weights once the slot is
-// free, so every load has most of a layer to arrive.  In a stage where a wave
-// both computes and reloads, the reload is issued after the dot product: the
-// compiler cannot count loads issued under branches, so a dot product that
-// follows a reload waits for that fresh burst too (vmcnt 0), which cost about
-// a microsecond per stage; issued afterwards, the burst overlaps the hand-off
-// instead (measured: 406 -> 349 us per 24-layer step).
+// free, so every load has most of a layer to arrive.  A compute unit's vector
+// memory requests drain in order, so a burst delays every hand-off load or
+// store issued behind it until the burst has streamed in (about 24 GB/s per
+// compute unit while all of them load).  A burst therefore either follows the
+// dot product of its stage (the down and gate/up reloads: the compiler cannot
+// count loads issued under branches, so a dot product behind a reload would
+// wait for the whole burst, vmcnt 0) or, for the wo reload, goes out before
+// the gate/up dot products with an explicit wait for the wave's older loads
+// first, so that it drains during the layer's longest compute window.
+// Measured per 24-layer step: reloads before their stage's dot product
+// 406 us, after it 349 us, with the wo burst moved into stage C 340 us.
 //
 // Every wait is bounded.  An expired wait sets bit 1 of the step's error
 // word; the step then writes next_token = -1, the bit is added to the sticky
@@ -605,6 +610,13 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
     __syncthreads();
     if (stamping && threadIdx.x == 0) stamp_l(l, 4);
     if (!poller) {
+      // The next layer's wo burst goes out before this stage's dot products,
+      // so that it drains while they run (the longest compute window of the
+      // layer) instead of in front of the next hand-off.  Waiting for this
+      // wave's older loads first (long complete) lets the compiler see that
+      // the gate/up weights need no wait behind the new burst.
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      if (hasB && l + 1 < L) loadB(l + 1);
       if (hasC) {
         if (stamping && ta == 0) {
           __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -626,7 +638,6 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
         if (stamping && lane == 0 && ta == 0) stamp_l(l, 5);
         if (stamping && lane == 0 && ta == tc - 1) stamp_l(l, 6);
       }
-      if (hasB && l + 1 < L) loadB(l + 1);
     } else {
       const int base = 16 * cs0;
       poll_stage_rec(
