@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +37,8 @@ Q8_CHAIN_QKV, Q8_CHAIN_H_ATTN, Q8_CHAIN_SWIGLU, Q8_CHAIN_H_OUT = 0, 1, 2, 3
 Q8_CHAIN_STAMP_LAYERS, Q8_CHAIN_STAMP_POINTS, Q8_CHAIN_STAMP_KERNEL = 32, 16, 4
 Q8_CHAIN_STAMP_WORDS = Q8_CHAIN_STAMP_LAYERS * Q8_CHAIN_STAMP_POINTS + Q8_CHAIN_STAMP_KERNEL
 
-EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_gemv", "q8_0_gemv_fused",
+EXPORTS = ("q8_0_packed_size", "q8_0_repack", "q8_0_repack_layout", "q8_0_repack_host",
+           "q8_0_repack_staging_bytes", "q8_0_gemv", "q8_0_gemv_fused",
            "q8_0_gemv_argmax", "q8_0_quantize_act", "q8_0_gemv_q8act", "q8_0_argmax",
            "q8_0_route_topk", "q8_0_moe_gemv", "q8_0_workspace_bytes", "q8_0_gemv_plan",
            "q8_0_strerror", "q8_0_version", "q8_0_chain_workspace_bytes", "q8_0_chain_prepare",
@@ -109,6 +111,9 @@ def lib() -> ctypes.CDLL:
         L.q8_0_packed_size.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
         L.q8_0_repack.argtypes = [P, I64, I64, P, P, P]
         L.q8_0_repack_layout.argtypes = [P, I64, I64, I32, P, P, P]
+        L.q8_0_repack_host.argtypes = [P, I64, I64, I32, P, P, P, SZ, P]
+        L.q8_0_repack_staging_bytes.argtypes = [I64, I64]
+        L.q8_0_repack_staging_bytes.restype = SZ
         L.q8_0_gemv.argtypes = [PW, P, P, I64, I64, I64, P, SZ, P]
         L.q8_0_gemv_noalloc.argtypes = [PW, P, P, I64, I64, I64, P]
         L.q8_stream_read.argtypes = [P, I64, P, I32, P]
@@ -448,6 +453,39 @@ def q8_0_repack(aos: torch.Tensor, M: int, K: int, qs: torch.Tensor, d: torch.Te
         rc = lib().q8_0_repack_layout(aos.data_ptr(), M, K, layout, qs.data_ptr(), d.data_ptr(),
                                       _stream(stream))
         _check("q8_0_repack_layout", rc)
+
+
+def q8_0_repack_staging_bytes(M: int, K: int) -> int:
+    """Smallest device staging buffer q8_0_repack_host accepts (one 64-row
+    tile of 34-byte blocks)."""
+    return int(lib().q8_0_repack_staging_bytes(M, K))
+
+
+def q8_0_repack_host(aos, M: int, K: int, qs: torch.Tensor, d: torch.Tensor,
+                     staging: torch.Tensor, stream=None, layout: int = Q8_LAYOUT_ROWS) -> None:
+    """Repack GGUF Q8_0 blocks held in host memory (a contiguous uint8 numpy
+    array or CPU tensor of M*(K/32)*34 bytes) through the device buffer
+    `staging`, band by band.  Synchronises the stream before returning, so the
+    host array may be freed afterwards."""
+    if isinstance(aos, torch.Tensor):
+        if aos.is_cuda or aos.dtype != torch.uint8 or not aos.is_contiguous():
+            raise ValueError("aos must be a contiguous uint8 host array")
+        ptr, n = aos.data_ptr(), aos.numel()
+    else:
+        if aos.dtype != np.uint8 or not aos.flags["C_CONTIGUOUS"]:
+            raise ValueError("aos must be a contiguous uint8 host array")
+        ptr, n = aos.ctypes.data, aos.size
+    if n != M * (K // 32) * 34:
+        raise ValueError(f"aos has {n} bytes, expected {M * (K // 32) * 34}")
+    qb, db = q8_0_packed_size(M, K)
+    _room(qs, qb, "qs")
+    _room(d, db, "d")
+    _need(staging, torch.uint8, "staging")
+    st = stream if stream is not None else torch.cuda.current_stream()
+    rc = lib().q8_0_repack_host(ptr, M, K, layout, qs.data_ptr(), d.data_ptr(),
+                                staging.data_ptr(), staging.numel(), _stream(st))
+    _check("q8_0_repack_host", rc)
+    st.synchronize()
 
 
 # ---------------------------------------------------------------------------

@@ -243,6 +243,70 @@ int q8_0_repack_layout(const void* aos, int64_t M, int64_t K, int32_t layout, vo
   return launch_repack(aos, M, K, layout, qs, d, static_cast<hipStream_t>(stream));
 }
 
+// Rows of the GGUF matrix that one band of whole 64-row tiles moves through
+// the staging buffer, or 0 when not even one tile fits.
+static int64_t host_band_tiles(int64_t M, int64_t K, size_t staging_bytes) {
+  const int64_t tile_bytes = (int64_t)kTile * (K / 32) * 34;
+  const int64_t T = (M + kTile - 1) / kTile;
+  const int64_t n = (int64_t)(staging_bytes / (size_t)tile_bytes);
+  return n < T ? n : T;
+}
+
+size_t q8_0_repack_staging_bytes(int64_t M, int64_t K) {
+  if (!shape_ok(M, K) || M == 0) return 0;
+  return (size_t)kTile * (size_t)(K / 32) * 34;
+}
+
+int q8_0_repack_host(const void* aos_host, int64_t M, int64_t K, int32_t layout, void* qs,
+                     void* d, void* staging, size_t staging_bytes, void* stream) {
+  if (!shape_ok(M, K)) return Q8_EINVAL;
+  if (layout != Q8_LAYOUT_ROWS && layout != Q8_LAYOUT_GATE_UP_PAIRS) return Q8_EINVAL;
+  if (layout == Q8_LAYOUT_GATE_UP_PAIRS && M % kTile) return Q8_EINVAL;
+  if (!aos_host || !qs || !d || !staging) return Q8_ENULL;
+  if (M == 0) return Q8_OK;
+  int rc;
+  if ((rc = check_dev_aligned(qs, 16)) || (rc = check_dev_aligned(d, 8)) ||
+      (rc = check_dev_aligned(staging, 16)))
+    return rc;
+  const int64_t band = host_band_tiles(M, K, staging_bytes);
+  if (band < 1) return Q8_EWORKSPACE;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t row_bytes = (K / 32) * 34;
+  const int64_t T = (M + kTile - 1) / kTile, G = (K / 32 + 3) / 4;
+  const uint8_t* src = static_cast<const uint8_t*>(aos_host);
+  uint8_t* stg = static_cast<uint8_t*>(staging);
+  for (int64_t t0 = 0; t0 < T; t0 += band) {
+    const int64_t nt = T - t0 < band ? T - t0 : band;
+    int64_t rows;
+    // stream order keeps each copy behind the previous band's repack kernels
+    if (layout == Q8_LAYOUT_GATE_UP_PAIRS) {
+      // gate rows 32 t0 .., then the matching up rows M/2 + 32 t0 ..: a
+      // gate/up matrix of 64 nt rows whose tiles are tiles t0 .. of the whole
+      const int64_t h = 32 * nt, g0 = 32 * t0, u0 = M / 2 + 32 * t0;
+      if (hipMemcpyAsync(stg, src + g0 * row_bytes, (size_t)(h * row_bytes),
+                         hipMemcpyHostToDevice, st) != hipSuccess ||
+          hipMemcpyAsync(stg + h * row_bytes, src + u0 * row_bytes, (size_t)(h * row_bytes),
+                         hipMemcpyHostToDevice, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return Q8_ELAUNCH;
+      }
+      rows = 2 * h;
+    } else {
+      const int64_t r0 = kTile * t0;
+      rows = M - r0 < kTile * nt ? M - r0 : kTile * nt;
+      if (hipMemcpyAsync(stg, src + r0 * row_bytes, (size_t)(rows * row_bytes),
+                         hipMemcpyHostToDevice, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return Q8_ELAUNCH;
+      }
+    }
+    if ((rc = launch_repack(stg, rows, K, layout, static_cast<uint8_t*>(qs) + t0 * kTile * K,
+                            static_cast<uint8_t*>(d) + t0 * G * kTile * 8, st)))
+      return rc;
+  }
+  return Q8_OK;
+}
+
 static int gemv_common(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K,
                        int64_t N, const q8_0_fusion* f, int32_t* col_argmax, void* ws,
                        size_t wsb, void* stream) {

@@ -117,6 +117,29 @@ int q8_0_packed_size(int64_t M, int64_t K, size_t* qs_bytes, size_t* d_bytes);
  * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_ELAUNCH. */
 int q8_0_repack(const void* aos, int64_t M, int64_t K, void* qs, void* d, void* stream);
 
+/* The repack from host memory: aos_host holds the M * K/32 blocks of 34
+ * bytes (row-major, as read from a GGUF file; pageable or pinned host
+ * memory, or device memory).  They move to the device through `staging`, a
+ * caller-owned device buffer of staging_bytes (16-byte aligned), in bands of
+ * whole 64-row tiles: each band is one stream-ordered copy (two for the
+ * gate/up pairs layout: its gate rows, then the matching up rows) followed
+ * by the repack of those tiles, so staging is reused band after band and
+ * the library allocates nothing.  A larger staging buffer means fewer
+ * bands; q8_0_repack_staging_bytes(M, K) gives the smallest (one tile of
+ * rows).  layout, qs and d as q8_0_repack_layout; the packed bytes are the
+ * same as q8_0_repack_layout's on a device copy of aos_host.  The call
+ * returns once the last copy is queued (pageable host memory may make the
+ * copies synchronous); aos_host must stay valid until the stream has run
+ * them.  Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR (qs, d or
+ * staging not device memory), Q8_EWORKSPACE (staging_bytes below one tile
+ * of rows), Q8_ELAUNCH. */
+int q8_0_repack_host(const void* aos_host, int64_t M, int64_t K, int32_t layout, void* qs,
+                     void* d, void* staging, size_t staging_bytes, void* stream);
+
+/* Smallest staging buffer q8_0_repack_host accepts for an M x K matrix:
+ * 64 rows of 34-byte blocks (0 for an invalid shape or M == 0). */
+size_t q8_0_repack_staging_bytes(int64_t M, int64_t K);
+
 /* The same with a row order: layout Q8_LAYOUT_ROWS (as q8_0_repack) or
  * Q8_LAYOUT_GATE_UP_PAIRS (M % 64 == 0).  Set the descriptor's `layout` to
  * the same value.  Errors as q8_0_repack. */

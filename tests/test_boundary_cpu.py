@@ -46,6 +46,24 @@ def test_packed_size():
         assert e.value.code == q.Q8_EINVAL
 
 
+def test_repack_host_staging_and_host_checks():
+    """q8_0_repack_host: staging size is one 64-row tile of 34-byte blocks;
+    shape, layout and null arguments are rejected before any copy."""
+    L = q.lib()
+    assert q.q8_0_repack_staging_bytes(896, 896) == 64 * 28 * 34
+    assert q.q8_0_repack_staging_bytes(1, 32) == 64 * 34
+    assert q.q8_0_repack_staging_bytes(0, 32) == 0
+    assert q.q8_0_repack_staging_bytes(4, 33) == 0
+    dummy = ctypes.c_void_p(16)
+    big = 1 << 30
+    for M, K, layout in [(4, 33, 0), (-1, 32, 0), (96, 64, 1), (64, 64, 2)]:
+        assert L.q8_0_repack_host(dummy, M, K, layout, dummy, dummy, dummy, big,
+                                  None) == q.Q8_EINVAL, (M, K, layout)
+    assert L.q8_0_repack_host(None, 64, 64, 0, dummy, dummy, dummy, big, None) == q.Q8_ENULL
+    assert L.q8_0_repack_host(dummy, 64, 64, 0, dummy, dummy, None, big, None) == q.Q8_ENULL
+    assert L.q8_0_repack_host(dummy, 0, 64, 0, dummy, dummy, dummy, 0, None) == q.Q8_OK
+
+
 def _desc(M, K, n=1):
     return q.q8_0_weights(None, None, M, K, n, 0, 0)
 

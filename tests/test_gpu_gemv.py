@@ -184,6 +184,40 @@ def test_repack_gate_up_pairs_layout_bit_exact(M, K):
     assert np.array_equal(host(p.d), ed)
 
 
+@pytest.mark.parametrize("M,K,layout", [(1, 32, 0), (65, 96, 0), (200, 896, 0), (333, 1408, 0),
+                                         (128, 96, 1), (9728, 896, 1), (2816, 2048, 1)])
+@pytest.mark.parametrize("tiles", [1, 2.5, 1000])
+def test_repack_from_host_memory_bit_exact(M, K, layout, tiles):
+    """q8_0_repack_host moves the blocks from a numpy array through a staging
+    buffer of one tile, two and a half tiles (ragged last band) or the whole
+    matrix; the packed bytes equal the layout written out from the header."""
+    m = W.draw_matrix(W.rng(12, M, K), M, K)
+    aos = np.ascontiguousarray(m.aos().reshape(-1))
+    smin = q.q8_0_repack_staging_bytes(M, K)
+    assert smin == 64 * (K // 32) * 34
+    staging = torch.empty(int(smin * tiles), dtype=torch.uint8, device=DEV)
+    qb, db = q.q8_0_packed_size(M, K)
+    qs = torch.full((qb,), 0xA5, dtype=torch.uint8, device=DEV)
+    d = torch.full((db,), 0xA5, dtype=torch.uint8, device=DEV)
+    q.q8_0_repack_host(aos, M, K, qs, d, staging, layout=layout)
+    eq, ed = expected_packed(m.qs, m.d, layout)
+    assert np.array_equal(host(qs), eq)
+    assert np.array_equal(host(d), ed)
+
+
+def test_repack_from_host_rejects_small_staging():
+    M, K = 100, 64
+    m = W.draw_matrix(W.rng(13, M, K), M, K)
+    aos = np.ascontiguousarray(m.aos().reshape(-1))
+    qb, db = q.q8_0_packed_size(M, K)
+    qs = torch.empty(qb, dtype=torch.uint8, device=DEV)
+    d = torch.empty(db, dtype=torch.uint8, device=DEV)
+    staging = torch.empty(q.q8_0_repack_staging_bytes(M, K) - 1, dtype=torch.uint8, device=DEV)
+    with pytest.raises(q.Q8Error) as e:
+        q.q8_0_repack_host(aos, M, K, qs, d, staging)
+    assert e.value.code == q.Q8_EWORKSPACE
+
+
 @pytest.mark.parametrize("M,K,N", [(128, 96, 1), (9728, 896, 1), (640, 2048, 3)])
 def test_gemv_on_pairs_layout_writes_row_order(M, K, N):
     g = W.rng(27, M, K)
