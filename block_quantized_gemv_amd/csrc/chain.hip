@@ -747,8 +747,9 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
           bv = s_cv[w];
           bi = s_ci[w];
         }
-      st_dev(reinterpret_cast<float*>(ws + P.am_off) + 2 * b, bv);
-      st_dev(reinterpret_cast<int32_t*>(ws + P.am_off) + 2 * b + 1, bi);
+      // one 8-byte word: the value's bits, then the index
+      st_dev(reinterpret_cast<uint64_t*>(ws + P.am_off) + b,
+             (uint64_t)__float_as_uint(bv) | (uint64_t)(uint32_t)bi << 32);
       if (stamping) stamp(kStampL * kStampP + 2);
     }
   }
@@ -769,25 +770,37 @@ __global__ __launch_bounds__(kCT) void chain_kernel(const ChainArgs P) {
   __syncthreads();
   if (!s_last || wave != 0) return;
   __asm__ volatile("" ::: "memory");
+  // the status word and every partial are loaded before any is compared, so
+  // this fold costs one round trip (G <= kMaxGrid = 16 * 64 partials)
+  const uint32_t st = ld_dev(status);
   if (V > 0) {
+    const uint64_t* am = reinterpret_cast<const uint64_t*>(ws + P.am_off);
+    uint64_t pw[kMaxGrid / 64];
+#pragma unroll
+    for (int k = 0; k < kMaxGrid / 64; ++k) {
+      const int g = lane + 64 * k;
+      pw[k] = 64 * k < G ? ld_dev(am + (g < G ? g : G - 1)) : 0;
+    }
     float v = -INFINITY;
     int i = 0x7fffffff;
-    for (int g = lane; g < G; g += 64) {
-      const float tv2 = ld_dev(reinterpret_cast<const float*>(ws + P.am_off) + 2 * g);
-      const int ti = ld_dev(reinterpret_cast<const int32_t*>(ws + P.am_off) + 2 * g + 1);
-      if (tv2 > v || (tv2 == v && ti < i)) {
-        v = tv2;
-        i = ti;
+#pragma unroll
+    for (int k = 0; k < kMaxGrid / 64; ++k) {
+      const int g = lane + 64 * k;
+      if (64 * k < G && g < G) {
+        const float tv2 = __uint_as_float((uint32_t)pw[k]);
+        const int ti = (int)(pw[k] >> 32);
+        if (tv2 > v || (tv2 == v && ti < i)) {
+          v = tv2;
+          i = ti;
+        }
       }
     }
     wave_argmax(v, i);
     // an expired wait anywhere in this step makes its outputs invalid: say so
     // in the token itself
-    const uint32_t st = ld_dev(status);
     if (lane == 0) *P.next_token = st ? -1 : i;
   }
   if (lane == 0) {
-    const uint32_t st = ld_dev(status);
     if (st) atomicOr(&hdr->status, st);
     st_dev(status, 0u);
     st_dev(&hdr->ticket, 0u);
