@@ -3,8 +3,8 @@
 // workgroup of 256 threads reads one contiguous chunk of the buffer with
 // 16-byte non-temporal loads (global_load_dwordx4, the instruction the GEMV
 // streams its weights with), 4 in flight per lane; a contiguous chunk per
-// workgroup measured 7.0 TB/s on 2 GiB where a grid-stride sweep of the whole
-// buffer reached 6.0 TB/s (a workgroup's requests stay within few DRAM pages).
+// workgroup keeps a workgroup's requests within few DRAM pages (bench.py's
+// read-reference rows: 6.4-6.8 TB/s over 2 GiB).
 // The workgroup's XOR of every word it read goes to out[blockIdx.x] with a
 // plain store, so no read can be dropped and the host can check that every
 // word was read exactly once; no atomics, which would serialise the end of
