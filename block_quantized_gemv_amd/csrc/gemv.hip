@@ -378,6 +378,176 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
   }
 }
 
+// ---- matrix cores: several columns as a skinny product ---------------------
+// With N >= kRowGroupN columns the lane dot product above issues N FMAs per
+// weight and is bound by VALU issue, not by HBM.  Here each block is one
+// v_mfma_f32_16x16x32_bf16 per 16 rows, with the weights as the B operand:
+// an int8 quant is exact in bf16.  The fp32 activations are cut into three
+// bf16 parts, x = h + m + l with h = x truncated to bf16 and m, l the next
+// eight significant bits each, so every product is exact and only the fp32
+// accumulation order differs from the FMA loop.  The 16 A rows are [h of
+// columns 0..7 | m of columns 0..7] in a first product and [0 | l] in a second
+// chained onto it; column n's block sum is D[n] + D[n + 8].
+//
+// Operand layout of the 16x16x32 product (lane l, e = 0..7): A row l % 16 and
+// B column l % 16 take k = 8 (l / 16) + e; D slot t of lane l is row
+// 4 (l / 16) + t, column l % 16.  So lane (j = l % 16, g = l / 16) loads
+// bytes 8 (g & 1) .. + 7 of half g >> 1 of row 16 q + j's block (two 256-byte
+// runs per row group), and 8 activations of column l & 7 from k = 8 g.  D
+// slot t of lane l then holds, for row 16 q + j, column 4 (g & 1) + t: the h
+// part for g < 2, the m + l parts for g >= 2.  One quad of weights and
+// activations is in flight with one quad's registers: each block's weights
+// and activations of the next quad are loaded right after its products.  At
+// the end, a permlane32 swap adds the two parts and a permlane16 swap moves
+// row 16 q + j's columns 0..3 and 4..7 into lane 16 q + j: the layout
+// dot_range produces.
+//
+// Each block's products run without scheduling barriers, so the compiler
+// overlaps one block's conversions with the previous block's products.  C4
+// gate_up 24576x4096 / down 4096x12288, same box, lane loop -> this: N = 8
+// 38.0 -> 29.9 / 26.5 -> 22.4 us; N = 6 32.2 -> 28.5 / 23.0 -> 20.9; N = 5
+// 31.1 -> 28.0 / 20.7 -> 21.6; N = 4 28.5 -> 27.7 / 18.3 -> 20.5 (kept on
+// the lane loop: its registers leave 5 waves a SIMD against 4).  With the
+// barriers that keep each load where it is issued (as the lane loop needs)
+// N = 8 took 32.6 / 24.1 us.
+constexpr int kMfmaN = 5;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+
+// High halves of (lo, hi) as two packed bf16 (lo in bits 0..15).
+__device__ __forceinline__ uint32_t bf16_hi_pair(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// The 8 quants of a u32x2 as bf16 (exact).
+__device__ __forceinline__ bf16x8 mf_weights(u32x2 w) {
+  u32x4 r;
+  r.x = bf16_hi_pair(q_at(w.x, 0), q_at(w.x, 1));
+  r.y = bf16_hi_pair(q_at(w.x, 2), q_at(w.x, 3));
+  r.z = bf16_hi_pair(q_at(w.y, 0), q_at(w.y, 1));
+  r.w = bf16_hi_pair(q_at(w.y, 2), q_at(w.y, 3));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// A operands of one block from the lane's 8 activations: a1 = h (lanes of the
+// first half row) or m (second half), a2 = 0 or l.  m1 = 0 / 0xffff0000 and
+// m2 = 0 / ~0 select the half; m2 also zeroes columns >= N.
+__device__ __forceinline__ void mf_split(const f32x4 (&xv)[2], uint32_t m1, uint32_t m1z,
+                                         uint32_t m2, bf16x8& a1, bf16x8& a2) {
+  float t[8], r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = xv[e >> 2][e & 3];
+    t[e] = v - __uint_as_float(__float_as_uint(v) & m1);          // x, or x - h
+    r[e] = t[e] - __uint_as_float(__float_as_uint(t[e]) & 0xffff0000u);  // below its bf16
+  }
+  u32x4 p1, p2;
+  p1.x = bf16_hi_pair(t[0], t[1]) & m1z;
+  p1.y = bf16_hi_pair(t[2], t[3]) & m1z;
+  p1.z = bf16_hi_pair(t[4], t[5]) & m1z;
+  p1.w = bf16_hi_pair(t[6], t[7]) & m1z;
+  p2.x = bf16_hi_pair(r[0], r[1]) & m2;
+  p2.y = bf16_hi_pair(r[2], r[3]) & m2;
+  p2.z = bf16_hi_pair(r[4], r[5]) & m2;
+  p2.w = bf16_hi_pair(r[6], r[7]) & m2;
+  a1 = __builtin_bit_cast(bf16x8, p1);
+  a2 = __builtin_bit_cast(bf16x8, p2);
+}
+
+template <int N>
+__device__ __forceinline__ void dot_range_mf(const uint8_t* qs_tile, const uint8_t* d_tile, int b0,
+                                             int b1, int lane, const float* x, int64_t xs,
+                                             bool prio, float (&acc)[N]) {
+  static_assert(N >= 1 && N <= 8, "one product holds 8 columns");
+  const int j = lane & 15, g = lane >> 4, c = lane & 7;
+  const bool second = (lane >> 3) & 1;
+  const uint32_t m1 = second ? 0xffff0000u : 0u;
+  const uint32_t m1z = c < N ? ~0u : 0u;
+  const uint32_t m2 = second ? m1z : 0u;
+  const float* xl = x + (int64_t)(c < N ? c : N - 1) * xs + 8 * g;
+  const uint32_t wofs = (uint32_t)((g >> 1) * 1024 + j * 16 + (g & 1) * 8);
+  const uint32_t dofs = (uint32_t)(j * 8);
+  f32x4 a4[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) a4[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int g0 = b0 >> 2;
+  const int nq = b1 > b0 ? ((b1 + 3) >> 2) - g0 : 0;
+  if (nq > 0) {
+    const int gl = (b1 - 1) >> 2;
+    // block clamped into [b0, b1): loads past the range re-read the last
+    // block (never used), so no load is conditional
+    auto bcl = [&](int b) { return b < b0 ? b0 : (b < b1 ? b : b1 - 1); };
+    auto wload = [&](int b, int q) {
+      return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
+          qs_tile + (uint32_t)bcl(b) * 2048u + wofs + 256u * q));
+    };
+    auto xload = [&](int b, f32x4 (&v)[2]) {
+      const float* p = xl + 32 * bcl(b);
+      v[0] = *reinterpret_cast<const f32x4u*>(p);
+      v[1] = *reinterpret_cast<const f32x4u*>(p + 4);
+    };
+    auto dload = [&](int G, int q) {
+      return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
+          d_tile + (uint32_t)(G < gl ? G : gl) * 512u + dofs + 128u * q));
+    };
+    u32x2 W[4][4];  // [block of the quad][row group]
+    f32x4 X[4][2];  // [block of the quad]
+    u32x2 D[4], DN[4];
+#pragma unroll
+    for (int bq = 0; bq < 4; ++bq) {
+      xload(4 * g0 + bq, X[bq]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) W[bq][q] = wload(4 * g0 + bq, q);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) DN[q] = dload(g0, q);
+    for (int it = 0; it < nq; ++it) {
+      const int G = g0 + it;
+      if (prio) rg_progress_prio(it, nq);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        D[q] = DN[q];
+        DN[q] = dload(G + 1, q);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int bq = 0; bq < 4; ++bq) {
+        const int b = 4 * G + bq;
+        const bool ok = b >= b0 && b < b1;
+        bf16x8 a1, a2;
+        mf_split(X[bq], m1, m1z, m2, a1, a2);
+        xload(b + 4, X[bq]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bf16x8 wb = mf_weights(W[bq][q]);
+          W[bq][q] = wload(b + 4, q);
+          f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, wb, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                            0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, wb, s, 0, 0, 0);
+          const float dq = ok ? f16_to_f32(quad_bits(D[q], bq)) : 0.f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) a4[q][t] = fmaf(dq, s[t], a4[q][t]);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float s0 = a4[0][t], s2 = a4[2][t], s1 = a4[1][t], s3 = a4[3][t];
+    __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(s0), "+v"(s2));
+    __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(s1), "+v"(s3));
+    // u: row groups 0 (lanes 0..31) and 2, v: 1 and 3; lanes 16..31 of each
+    // 32 hold columns 4..7
+    float u = s0 + s2, v = s1 + s3;
+    __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(u), "+v"(v));
+    if (t < N) acc[t] += u;
+    if (4 + t < N) acc[4 + t] += v;
+  }
+}
+
 // ---- Q4_K and Q5_K weights ---------------------------------------------------
 // A quad is half of a 256-weight block: 4 sub-blocks of 32.  Sub-block j of
 // a row is 16 bytes whose byte i holds weights i (low nibble) and i + 16 (high
@@ -1178,11 +1348,14 @@ __global__ __launch_bounds__(64 * max_waves_for(N, MODE >= 3)) void gemv_kernel(
         // (the GQA prologue exists for one column only, which the launcher
         // enforces; the row-group instances carry no replicated path, whose
         // registers would set the whole kernel's occupancy)
-        // N >= 4: row groups always.  N = 2, 3: row groups when every wave is
+        // N >= kMfmaN: matrix-core products.  N = 4: row groups always.
+        // N = 2, 3: row groups when every wave is
         // resident (C4 down 4096x12288 N = 2: 16.7 -> 15.2 us), the
         // replicated loop in launches of several rounds with short units
         // (lm_head N = 2: 31.5 us replicated, 33.9 with row groups).
-        if constexpr (N >= kRowGroupN)
+        if constexpr (N >= kMfmaN)
+          dot_range_mf<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, p.prio != 0, acc);
+        else if constexpr (N >= kRowGroupN)
           dot_range_rg<N>(qs_tile, d_tile, b0, b1, lane, s.x, s.x_stride, p.prio != 0, acc);
         else if constexpr (N >= 2) {
           if (p.prio)
@@ -1381,6 +1554,10 @@ int env_int(const char* name, int dflt) {
 //  Q8G_MIN_UNITS     fewest units per 64-row tile when K allows
 //  Q8G_MAX_WAVES     most waves per workgroup (units of one tile beyond it
 //                    spill into more workgroups and a ticketed fold)
+//  Q8G_WIDE_UNITS    units per tile of a plan with one to two tiles per
+//                    compute unit at N >= 2 (default 8)
+//  Q8G_WIDE_WAVES    most waves per workgroup in plans with a tile or more
+//                    per compute unit (default 4)
 int target_waves() {
   static const int v = env_int("Q8G_TARGET_WAVES", 2048);
   return v;
@@ -1391,6 +1568,14 @@ int min_quads() {
 }
 int min_units() {
   static const int v = env_int("Q8G_MIN_UNITS", 4);
+  return v;
+}
+int wide_units() {
+  static const int v = env_int("Q8G_WIDE_UNITS", 8);
+  return v;
+}
+int wide_waves() {
+  static const int v = env_int("Q8G_WIDE_WAVES", 4);
   return v;
 }
 // Compute units of the current device (256 on an MI355X; that value when no
@@ -1507,11 +1692,11 @@ int plan_problems(const ProbDesc* probs, int nprob, int N, Plan* plan) {
   const bool few = !wide && f0 == FMT_Q8_0 && N <= 4 && nprob == 1 && probs[0].R == 1 &&
                    !probs[0].seg[0].qx && total_tout < num_cus() && k_total >= 4096;
   const int64_t want_u =
-      wide ? (wide_split ? 8 : 4)
+      wide ? (wide_split ? wide_units() : 4)
            : cdiv((kq || few) ? target_waves() / 2 : target_waves(), total_tout);
   const int wfmt = max_waves_for(N, f0 == FMT_Q6K || f0 == FMT_Q5K);
   int wmax = max_waves() < wfmt ? max_waves() : wfmt;
-  if ((wide || kq || few) && wmax > 4) wmax = 4;
+  if ((wide || kq || few) && wmax > wide_waves()) wmax = wide_waves();
   // units per tile
   int sbase = 0;
   int64_t U[kMaxProb];

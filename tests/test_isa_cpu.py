@@ -11,8 +11,11 @@ cross-compiles, nothing runs).
   dot result read by another VALU instruction needs three wait states,
   which the compiler does not see through the asm.  The scan holds every
   dot (compiler-made ones too) to that.
-* The path is bandwidth-bound at N <= 8 and uses no matrix cores: no MFMA
-  instruction may appear in any kernel.
+* Matrix cores appear in one place only: the GEMV at five or more columns
+  runs each block as v_mfma_f32_16x16x32_bf16 products (bf16 parts of the
+  activations, exact int8 weights).  No other MFMA instruction may appear in
+  gemv.hip, and none at all in the other units (the decode chain, the
+  argmax, the repack).
 """
 import os
 import re
@@ -162,5 +165,9 @@ def test_kernel_assembly(unit, tmp_path):
     assert badd == [], f"{unit}: {len(badd)} dot result hazards, first: {badd[:3]}"
     if unit == "gemv.hip":
         assert nd > 0, "the integer-activation GEMV should use v_dot4c"
-    mfma = [t for k, t in insts if k == "I" and t.split()[0].startswith("v_mfma")]
-    assert mfma == [], f"{unit}: matrix-core instructions found: {mfma[:3]}"
+    mfma = [t.split()[0] for k, t in insts if k == "I" and t.split()[0].startswith("v_mfma")]
+    if unit == "gemv.hip":
+        assert mfma, "the GEMV at N >= 5 should use matrix-core products"
+        assert set(mfma) == {"v_mfma_f32_16x16x32_bf16"}, sorted(set(mfma))
+    else:
+        assert mfma == [], f"{unit}: matrix-core instructions found: {mfma[:3]}"
