@@ -103,6 +103,51 @@ def test_edge_scales_and_quants_within_tolerance():
     assert np.all(y[:, 200:210] == 0)
 
 
+@pytest.mark.parametrize("N", [5, 8])
+def test_matrix_core_split_edge_values(N):
+    """N >= 5 runs each block as bf16 matrix-core products, with every fp32
+    activation cut into three bf16 parts whose sum is exact.  Activations
+    with all 24 significand bits, values just above each bf16 cut, huge and
+    tiny magnitudes and signed zeros, with edge scales.  Then one-hot
+    columns holding full-significand values against power-of-two scales: the
+    block sum q * x is then one product, so the result must be exact."""
+    M, K = 200, 1408
+    g = W.rng(25, N)
+    m = W.draw_matrix(g, M, K)
+    d = m.d.view(np.uint16).copy()
+    d[:32, ::3] = 0x0001       # smallest subnormal
+    d[32:64, :] = 0x7BFF       # 65504
+    d[64:96, :] |= 0x8000      # negative scales
+    qs = m.qs.copy()
+    qs[96:128, ::5] = -128
+    m = W.Q8Matrix(qs, d.view(np.float16))
+    x = W.draw_x(g, N, K)
+    bits = x.view(np.uint32)
+    bits[0, ::2] |= 0x007FFFFF                        # all significand bits set
+    bits[1 % N, ::3] = (bits[1 % N, ::3] & 0xFFFF0000) | 0x00008001  # just above the cuts
+    x[2 % N, ::7] *= np.float32(1e25)   # d = 65504 rows stay far below fp32 overflow
+    x[3 % N, ::11] *= np.float32(1e-30)
+    x[4 % N, ::13] = np.float32(-0.0)
+    y = host(q.q8_0_gemv(pack(m), to_dev(x)))
+    yr, S = oracle.gemv(m.aos(), x)
+    q8tol.check(y, yr, S, f"matrix-core edge values N={N}")
+
+    dpow = np.full((M, K // 32), np.float16(0.5))
+    dpow[::2] = np.float16(-4.0)
+    mp = W.Q8Matrix(m.qs, dpow)
+    xo = np.zeros((N, K), dtype=np.float32)
+    ks = [0, 31, 32, 100, 700, 1000, K - 33, K - 1][:N]
+    vals = (np.array([1.0 + 2.0 ** -23, -3.14159274, 1.0e-20, 7.0e20, 0.1, -1.9999999, 1234.5678,
+                      2.0 ** -100], dtype=np.float32))[:N]
+    for i, k in enumerate(ks):
+        xo[i, k] = vals[i]
+    y = host(q.q8_0_gemv(pack(mp), to_dev(xo)))
+    for i, k in enumerate(ks):
+        want = np.float32(dpow[:, k // 32].astype(np.float32)
+                          * (m.qs[:, k].astype(np.float32) * np.float32(vals[i])))
+        assert np.array_equal(y[i], want.astype(np.float32)), (N, i, k)
+
+
 @pytest.mark.parametrize("M,K,N", [(896, 4864, 1), (896, 896, 1), (4096, 12288, 2),
                                    (9728, 896, 1), (1152, 896, 8)])
 def test_repeated_calls_bitwise_identical(M, K, N):
