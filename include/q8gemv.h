@@ -18,7 +18,10 @@
  * a block is 34 bytes: d (little-endian) then the 32 quants.
  *
  * Arithmetic: quants and scales are converted exactly to fp32, products and
- * sums are fp32 FMAs, activations stay fp32 (no requantisation).  Results
+ * sums are fp32 FMAs, activations stay fp32 (no requantisation).  The GEMV
+ * at N >= 5 columns runs each block as bf16 matrix-core products on an exact
+ * three-part bf16 split of each activation.  Its products are exact too, and
+ * only the fp32 summation order differs.  Results
  * agree with the exact value within 2e-5 * sum_k |w_k x_k| + 1e-6 per output.
  * For a fixed (M, K, N) and device the summation order is fixed: repeated
  * calls give bitwise identical results.
@@ -155,6 +158,12 @@ int q8_0_repack_layout(const void* aos, int64_t M, int64_t K, int32_t layout, vo
  * The N = 1 case is the decode projection; N in {2,4,8} is a small verify
  * chunk ("skuznetsov/cogni-ml" README, "Qwen 3.5 Native Metal":
  * target-verifier chunks), weights read once for all N columns.
+ * Arithmetic: every product q * x is exact and sums run in fp32, in an order
+ * fixed by (M, K, N), so repeated calls give bitwise the same y.  N <= 4 uses
+ * fp32 FMAs on the converted quants.  N >= 5 uses bf16 matrix-core products,
+ * with each activation split into three bf16 parts whose sum is x (for
+ * |x| above about 2^-110).  So a
+ * column's last bits may differ between an N <= 4 and an N >= 5 call.
  * Errors: Q8_EINVAL, Q8_ENULL, Q8_EALIGN, Q8_EHOSTPTR, Q8_EWORKSPACE,
  * Q8_ELAUNCH. */
 int q8_0_gemv(const q8_0_weights* W, const float* x, float* y, int64_t M, int64_t K, int64_t N,
