@@ -396,8 +396,9 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
 // runs per row group), and 8 activations of column l & 7 from k = 8 g.  D
 // slot t of lane l then holds, for row 16 q + j, column 4 (g & 1) + t: the h
 // part for g < 2, the m + l parts for g >= 2.  One quad of weights and
-// activations is in flight with one quad's registers: each block's weights
-// and activations of the next quad are loaded right after its products.  At
+// activations is in flight with one quad's registers: the source reloads each
+// block's registers with the next quad after its products, and the compiler
+// moves those loads to the end of the quad, then waits block by block.  At
 // the end, a permlane32 swap adds the two parts and a permlane16 swap moves
 // row 16 q + j's columns 0..3 and 4..7 into lane 16 q + j: the layout
 // dot_range produces.
@@ -409,7 +410,8 @@ __device__ __forceinline__ void dot_range_rg(const uint8_t* qs_tile, const uint8
 // 31.1 -> 28.0 / 20.7 -> 21.6; N = 4 28.5 -> 27.7 / 18.3 -> 20.5 (kept on
 // the lane loop: its registers leave 5 waves a SIMD against 4).  With the
 // barriers that keep each load where it is issued (as the lane loop needs)
-// N = 8 took 32.6 / 24.1 us.
+// N = 8 took 32.6 / 24.1 us: the loop then waited for the whole next quad at
+// its top.  Two quad buffers (244 VGPRs, 2 waves a SIMD) took 35-45 us.
 constexpr int kMfmaN = 5;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
